@@ -1,0 +1,189 @@
+/*
+ * moe.h -- C ABI of the routing-aware fused Mixture-of-Experts layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (GC-MoE, arXiv 2611.04222, section 2.1, Eq. 1, routed-expert term):
+ *     y_t = sum_{j in TopK(t)} g_{t,j} * W2^(j) * SwiGLU(W1^(j) x_t),
+ * with SwiGLU(v) = silu(W1 v) * (W3 v): W1 is the gate and W3 the up projection
+ * (GC-MoE stacks them as one 2I x H matrix), W2 the down projection.  It runs as
+ * five stream-ordered calls:
+ *
+ *   moe_route_topk     top-k of the router logits, softmax weights, and the
+ *                      per-local-expert token histogram n_e (RaMP, arXiv
+ *                      2604.26039, sections 2.1 and 2.3; the counting half of
+ *                      the selection kernel of section 3.2).
+ *   moe_select_config  the on-GPU cost model: for every compiled tile
+ *                      configuration c, t_c = th0 + th1 W_c + th2 T_c + th3 A
+ *                      (RaMP section 3.1, Eq. 3) over the row-tiles T_c and waves
+ *                      W_c of section 2.2, Eq. 1, then c* = argmin_c t_c (section
+ *                      2.4, Eq. 2), written to device memory.
+ *   moe_align_sort     the routed slots grouped by expert and padded into the
+ *                      chosen configuration's tiles (RaMP section 3.2).
+ *   moe_grouped_ffn    the polymorphic grouped expert kernel: every compiled
+ *                      configuration lives in one kernel that reads c* from device
+ *                      memory (RaMP section 3.3); gate/up with fused SwiGLU, then
+ *                      the down projection.
+ *   moe_combine        y_t = sum_j g_{t,j} y_{t,j}, accumulated in fp32 in j order
+ *                      (GC-MoE section 4, the combine role).
+ *
+ * Conventions for every call
+ *   - All array arguments are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises, and never reads device memory from
+ *     the host, so every call can be captured in a HIP graph (the captured-forward
+ *     constraint of RaMP section 2.4).  `stream` is a hipStream_t (NULL = the
+ *     default stream); work is enqueued on it and the call returns.
+ *   - Host-side validation runs first; on any error nothing is enqueued and the
+ *     status says why.  A failed launch returns MOE_ERR_HIP.
+ *   - Data-dependent values (counts, the chosen configuration, the block count)
+ *     stay in device memory and are only read by the kernels.
+ *   - Layouts are row-major.  Activations x [B][H]; router logits [B][E];
+ *     per-expert weights in nn.Linear order [out][in]: W1, W3 [E_loc][I][H],
+ *     W2 [E_loc][H][I].  FP8 weights are OCP E4M3FN codes with one fp32 scale per
+ *     128 x 128 block of each (out, in) matrix, w = q * s (the block-scaled FP8 of
+ *     RaMP section 3.3): s1, s3 [E_loc][I/128][H/128], s2 [E_loc][H/128][I/128].
+ *   - Supported dtype combinations (act/out, weights): (f32, f32), (bf16, bf16),
+ *     (bf16, fp8_e4m3).  The intermediate h and the per-slot outputs y_slots use
+ *     the activation dtype; accumulation is always fp32.
+ *   - Concurrent calls must not share one workspace or output buffer.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, bad range   */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but not built: dtype mix, shape limits      */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_query_sizes() asks     */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed        */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* The problem statement shared by every call (B tokens of H hidden activations,
+ * E experts of intermediate size I, top-k routing; this GPU holds the contiguous
+ * expert block [expert_begin, expert_begin + local_experts), as under expert
+ * parallelism in RaMP section 2.1; a single GPU with all experts has
+ * expert_begin = 0, local_experts = E). */
+typedef struct moe_problem {
+  int32_t tokens;        /* B >= 1                                              */
+  int32_t hidden;        /* H: multiple of 128                                  */
+  int32_t inter;         /* I: multiple of 128                                  */
+  int32_t num_experts;   /* E, 1 <= E <= 4096                                   */
+  int32_t expert_begin;  /* e0 >= 0                                             */
+  int32_t local_experts; /* E_loc >= 1, e0 + E_loc <= E, E_loc <= 1024          */
+  int32_t top_k;         /* k, 1 <= k <= min(E, 32)                             */
+  int32_t act_dtype;     /* moe_dtype of x, h, y_slots and y: MOE_F32/MOE_BF16  */
+  int32_t weight_dtype;  /* moe_dtype of W1, W3, W2                             */
+  int32_t renormalize;   /* 1: softmax over the k chosen logits (default);
+                            0: those experts' values of the softmax over all E  */
+} moe_problem;
+
+/* Buffer sizes a caller must provide for one problem. */
+typedef struct moe_sizes {
+  int64_t rows_max;        /* capacity (elements) of sorted_slots; rows of y_slots */
+  int64_t blocks_max;      /* capacity (elements) of block_expert                  */
+  int64_t y_slots_bytes;   /* rows_max * H * sizeof(act)                           */
+  int64_t workspace_bytes; /* grouped_ffn workspace: h [rows_max][I] + header      */
+  int64_t align_ws_bytes;  /* reserved, 0 in this version                          */
+} moe_sizes;
+
+/* ---- queries ------------------------------------------------------------- */
+
+/* Version of this ABI (bumped on any incompatible change). */
+int32_t moe_abi_version(void);
+
+/* Fills *out for problem *p.  Errors: MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED
+ * with the same rules as the compute calls. */
+moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out);
+
+/* Number V of tile configurations compiled into the polymorphic kernel. */
+int32_t moe_num_variants(void);
+
+/* Static description of configuration v, out[0..MOE_VARIANT_FIELDS-1]:
+ *   [0] BLOCK_M  token rows per tile (b_c of RaMP Eq. 1)
+ *   [1] BLOCK_N of the gate/up phase (output columns of W1 and of W3 per tile)
+ *   [2] BLOCK_N of the down phase
+ *   [3] BLOCK_K  reduction depth per pipeline stage
+ *   [4] waves along M, [5] waves along N, [6] waves splitting K inside a tile
+ *   [7] split-K of the down phase across tiles (1 = none)
+ * Errors: MOE_ERR_INVALID_ARG for v outside [0, V) or out == NULL. */
+#define MOE_VARIANT_FIELDS 8
+moe_status moe_variant_info(int32_t v, int32_t* out);
+
+/* The cost-model constants moe_select_config uses for problem *p on the current
+ * HIP device, per configuration v (arrays of V int32, host memory):
+ *   b[v]  = BLOCK_M;  q1[v] = I / BLOCK_N1 and q2[v] = (H / BLOCK_N2) * split_k,
+ *   the tiles of one row-block in each phase (q_c of RaMP Eq. 1, summed over the
+ *   two phases); S1[v], S2[v] = tiles resident on the GPU at once in each phase
+ *   = compute units * workgroups per compute unit (S_c of RaMP Eq. 1).
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP. */
+moe_status moe_cost_constants(const moe_problem* p, int32_t* b, int32_t* q1, int32_t* q2,
+                              int32_t* S1, int32_t* S2);
+
+/* ---- the five steps ------------------------------------------------------- */
+
+/* Step 1: top-k routing and histogram (RaMP 2.1, 2.3, 3.2).
+ *   logits   f32 [B][E]                      in
+ *   topk_ids i32 [B][k]  global expert ids   out, descending logit; equal logits
+ *                        go to the lower expert index and -0 equals +0
+ *   topk_w   f32 [B][k]                      out, softmax weights (see renormalize)
+ *   counts   i32 [E_loc]                     out, n_e = slots routed to local e
+ * NaN logits are outside the contract. */
+moe_status moe_route_topk(const moe_problem* p, const float* logits, int32_t* topk_ids,
+                          float* topk_w, int32_t* counts, void* stream);
+
+/* Step 2: choose the configuration (RaMP 3.1 Eq. 3, 3.2, 2.4 Eq. 2).
+ *   counts  i32 [E_loc]        in (from moe_route_topk)
+ *   theta   f32 [V][4]         in, th0..th3 per configuration (fit offline)
+ *   variant i32 [1]            out, argmin_v t_v (first index on ties)
+ *   t_hat   f32 [V] or NULL    out, the predictions (diagnostics)
+ * t_v = fmaf(th3, A, fmaf(th2, T, fmaf(th1, W, th0))) in fp32 with
+ * T = (q1 + q2) * sum_e ceil(n_e / b), W = ceil(q1 rt / S1) + ceil(q2 rt / S2),
+ * rt = sum_e ceil(n_e / b), A = #{e : n_e > 0}, constants of moe_cost_constants. */
+moe_status moe_select_config(const moe_problem* p, const int32_t* counts, const float* theta,
+                             int32_t* variant, float* t_hat, void* stream);
+
+/* Step 3: group and pad (RaMP 3.2).  With b = BLOCK_M of *variant:
+ *   sorted_slots i32 [rows_max]  out; rows [0, R): for local expert e = 0..E_loc-1
+ *                the slots s = t*k + j routed to e in ascending s, then -1 up to a
+ *                multiple of b; R = num_blocks * b.  Rows >= R are not written.
+ *   block_expert i32 [blocks_max] out; local expert of row-block i < num_blocks
+ *   num_blocks   i32 [1]          out
+ *   slot_pos     i32 [B*k]        out; row of slot s, or -1 if s is not local
+ * A *variant outside [0, V) yields num_blocks = 0 and slot_pos = -1 everywhere. */
+moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const int32_t* variant,
+                          int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
+                          int32_t* slot_pos, void* stream);
+
+/* Step 4: grouped expert FFN (RaMP 3.3; GC-MoE 2.1 Eq. 1).  For every row r < R:
+ *   h[r]       = silu(x[t] W1_e^T) * (x[t] W3_e^T)   (t = sorted_slots[r] / k)
+ *   y_slots[r] = h[r] W2_e^T                          (e = block_expert[r / b])
+ * Padding rows produce zeros.  x is [B][H] (act dtype); s1/s3/s2 are the fp8
+ * block scales (NULL unless weight_dtype is MOE_FP8_E4M3).  y_slots
+ * [rows_max][H] (act dtype).  workspace: >= workspace_bytes, 256-byte aligned;
+ * holds h.  Every configuration shares one persistent launch; the kernel reads
+ * *variant and *num_blocks from device memory. */
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
+                           const void* w2, const float* s1, const float* s3, const float* s2,
+                           const int32_t* sorted_slots, const int32_t* block_expert,
+                           const int32_t* num_blocks, const int32_t* variant, void* y_slots,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 5: combine (GC-MoE 2.1 Eq. 1; the slot-order reduction of its combine
+ * role).  y [B][H] (act dtype) = sum over j = 0..k-1 with slot_pos[t*k+j] >= 0 of
+ * topk_w[t][j] * y_slots[slot_pos[t*k+j]], in fp32, rounded to nearest even once;
+ * tokens with no local slot get zeros. */
+moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,
+                       const float* topk_w, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

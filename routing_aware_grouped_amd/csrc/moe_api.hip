@@ -1,0 +1,207 @@
+// moe_api.hip -- the C ABI of the fused-MoE library: host-side validation, buffer
+// sizing and kernel enqueue.  No call allocates, frees, synchronises or reads device
+// memory from the host, so every call can be captured into a HIP graph.
+#include <string.h>
+
+#include "moe_common.h"
+
+namespace moe {
+size_t align_lds_bytes(int B, int E_loc);
+}
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kWsHeader = 256;  // status word + padding, keeps h 256-byte aligned
+constexpr size_t kMaxLds = 160 * 1024;
+
+int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status validate(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->tokens < 1 || p->hidden < 128 || p->inter < 128) return MOE_ERR_INVALID_ARG;
+  if (p->hidden % 128 || p->inter % 128) return MOE_ERR_INVALID_ARG;
+  if (p->num_experts < 1 || p->num_experts > 4096) return MOE_ERR_INVALID_ARG;
+  if (p->expert_begin < 0 || p->local_experts < 1 || p->local_experts > 1024) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)p->expert_begin + p->local_experts > p->num_experts) return MOE_ERR_INVALID_ARG;
+  if (p->top_k < 1 || p->top_k > 32 || p->top_k > p->num_experts) return MOE_ERR_INVALID_ARG;
+  if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  const int a = p->act_dtype, w = p->weight_dtype;
+  if (a < MOE_F32 || a > MOE_FP8_E4M3 || w < MOE_F32 || w > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && w == MOE_BF16) ||
+                  (a == MOE_BF16 && w == MOE_FP8_E4M3);
+  if (!ok) return MOE_ERR_UNSUPPORTED;
+  // 32-bit slot and row indices
+  const int64_t slots = (int64_t)p->tokens * p->top_k;
+  if (slots >= (1ll << 30)) return MOE_ERR_UNSUPPORTED;
+  // the alignment step keeps its tables in one workgroup's LDS
+  if (align_lds_bytes(p->tokens, p->local_experts) > kMaxLds - 512) return MOE_ERR_UNSUPPORTED;
+  // the cost model converts tile and wave counts to fp32 exactly (< 2^24)
+  const int64_t rows = slots + (int64_t)(slots < p->local_experts ? slots : p->local_experts) * (kMaxBlockM - 1);
+  for (int v = 0; v < kNumVariants; ++v) {
+    const int64_t rt = rows / kVariants[v].bm;
+    const int64_t T = rt * (p->inter / kVariants[v].bn1 + (int64_t)(p->hidden / kVariants[v].bn2) * kVariants[v].splitk);
+    if (T >= (1ll << 24)) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+void sizes_of(const moe_problem* p, moe_sizes* s) {
+  const int64_t slots = (int64_t)p->tokens * p->top_k;
+  const int64_t active_max = slots < p->local_experts ? slots : p->local_experts;
+  s->rows_max = slots + active_max * (kMaxBlockM - 1);
+  s->blocks_max = s->rows_max / kMinBlockM + 1;
+  const int eb = elem_bytes(p->act_dtype);
+  s->y_slots_bytes = s->rows_max * p->hidden * eb;
+  int64_t hb = s->rows_max * p->inter * eb;
+  hb = (hb + 255) / 256 * 256;
+  s->workspace_bytes = kWsHeader + hb;
+  s->align_ws_bytes = 0;
+}
+
+int num_cus_current(hipError_t* err) {
+  static int cache[64] = {0};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  *err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (*err != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
+}
+
+moe_status fill_cost_table(const moe_problem* p, CostTable* t) {
+  hipError_t err;
+  const int cus = num_cus_current(&err);
+  if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
+  for (int v = 0; v < kNumVariants; ++v) {
+    t->b[v] = kVariants[v].bm;
+    t->q1[v] = p->inter / kVariants[v].bn1;
+    t->q2[v] = (p->hidden / kVariants[v].bn2) * kVariants[v].splitk;
+    t->S1[v] = cus * kWgPerCuPhase1;
+    t->S2[v] = cus * kWgPerCuPhase2;
+  }
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  const moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  sizes_of(p, out);
+  return MOE_OK;
+}
+
+int32_t moe_num_variants(void) { return kNumVariants; }
+
+moe_status moe_variant_info(int32_t v, int32_t* out) {
+  if (!out || v < 0 || v >= kNumVariants) return MOE_ERR_INVALID_ARG;
+  const VariantDesc& d = kVariants[v];
+  const int32_t vals[MOE_VARIANT_FIELDS] = {d.bm, d.bn1, d.bn2, d.bk, d.wm, d.wn, d.wk, d.splitk};
+  memcpy(out, vals, sizeof vals);
+  return MOE_OK;
+}
+
+moe_status moe_cost_constants(const moe_problem* p, int32_t* b, int32_t* q1, int32_t* q2,
+                              int32_t* S1, int32_t* S2) {
+  if (!b || !q1 || !q2 || !S1 || !S2) return MOE_ERR_INVALID_ARG;
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  CostTable t;
+  st = fill_cost_table(p, &t);
+  if (st != MOE_OK) return st;
+  for (int v = 0; v < kNumVariants; ++v) {
+    b[v] = t.b[v];
+    q1[v] = t.q1[v];
+    q2[v] = t.q2[v];
+    S1[v] = t.S1[v];
+    S2[v] = t.S2[v];
+  }
+  return MOE_OK;
+}
+
+moe_status moe_route_topk(const moe_problem* p, const float* logits, int32_t* topk_ids,
+                          float* topk_w, int32_t* counts, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_ids || !topk_w || !counts) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(counts, 4))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_route_topk(*p, logits, topk_ids, topk_w, counts, (hipStream_t)stream));
+}
+
+moe_status moe_select_config(const moe_problem* p, const int32_t* counts, const float* theta,
+                             int32_t* variant, float* t_hat, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!counts || !theta || !variant) return MOE_ERR_INVALID_ARG;
+  CostTable t;
+  st = fill_cost_table(p, &t);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_select_config(*p, counts, theta, t, variant, t_hat, (hipStream_t)stream));
+}
+
+moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const int32_t* variant,
+                          int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
+                          int32_t* slot_pos, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !variant || !sorted_slots || !block_expert || !num_blocks || !slot_pos)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_align_sort(*p, topk_ids, variant, sorted_slots, block_expert,
+                                      num_blocks, slot_pos, (hipStream_t)stream));
+}
+
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
+                           const void* w2, const float* s1, const float* s3, const float* s2,
+                           const int32_t* sorted_slots, const int32_t* block_expert,
+                           const int32_t* num_blocks, const int32_t* variant, void* y_slots,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w1 || !w3 || !w2 || !sorted_slots || !block_expert || !num_blocks || !variant ||
+      !y_slots || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!s1 || !s3 || !s2)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) ||
+      !aligned(y_slots, 16) || !aligned(workspace, 256))
+    return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!aligned(s1, 4) || !aligned(s3, 4) || !aligned(s2, 4))) return MOE_ERR_INVALID_ARG;
+  moe_sizes sz;
+  sizes_of(p, &sz);
+  if ((int64_t)workspace_bytes < sz.workspace_bytes) return MOE_ERR_WORKSPACE;
+  hipError_t err;
+  const int cus = num_cus_current(&err);
+  if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
+  void* h = (char*)workspace + kWsHeader;
+  return hip_status(launch_grouped_ffn(*p, x, w1, w3, w2, fp8 ? s1 : nullptr, fp8 ? s3 : nullptr,
+                                       fp8 ? s2 : nullptr, sorted_slots, block_expert, num_blocks,
+                                       variant, y_slots, h, cus, sz.rows_max, (hipStream_t)stream));
+}
+
+moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,
+                       const float* topk_w, void* y, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!y_slots || !slot_pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y_slots, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  moe_sizes sz;
+  sizes_of(p, &sz);
+  return hip_status(launch_combine(*p, y_slots, slot_pos, topk_w, y, sz.rows_max, (hipStream_t)stream));
+}
+
+}  // extern "C"

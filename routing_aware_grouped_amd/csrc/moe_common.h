@@ -1,0 +1,92 @@
+// moe_common.h -- shared device/host definitions of the gfx950 fused-MoE library.
+// Internal header of the GPU library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// vector types
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+
+// bf16 <-> f32 (round to nearest even; inputs are finite in this library)
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(r >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Compiled tile configurations of the polymorphic grouped FFN.  All share one
+// workgroup size (256 threads = 4 waves) and one launch per phase, so they are
+// one occupancy class (RaMP 3.3: one shared-memory buffer and one register
+// count for every entry).
+// ---------------------------------------------------------------------------
+struct VariantDesc {
+  int bm, bn1, bn2, bk, wm, wn, wk, splitk;
+};
+
+constexpr int kNumVariants = 4;
+constexpr int kThreads = 256;
+
+// BLOCK_M, BLOCK_N (gate/up), BLOCK_N (down), BLOCK_K, waves M x N x K, split-K
+constexpr VariantDesc kVariants[kNumVariants] = {
+    {16, 16, 16, 128, 1, 1, 4, 1},
+    {32, 32, 32, 64, 1, 2, 2, 1},
+    {64, 64, 64, 32, 2, 2, 1, 1},
+    {128, 64, 128, 32, 2, 2, 1, 1},
+};
+
+constexpr int kMinBlockM = 16;
+constexpr int kMaxBlockM = 128;
+
+// workgroups per CU of each persistent phase launch (one occupancy class)
+constexpr int kWgPerCuPhase1 = 2;
+constexpr int kWgPerCuPhase2 = 2;
+
+// Device-side table of the row-tile sizes for the selection/alignment kernels.
+struct CostTable {
+  int32_t b[kNumVariants];
+  int32_t q1[kNumVariants];
+  int32_t q2[kNumVariants];
+  int32_t S1[kNumVariants];
+  int32_t S2[kNumVariants];
+};
+
+// Host-side launchers (one per translation unit).
+hipError_t launch_route_topk(const moe_problem& p, const float* logits, int32_t* ids, float* w,
+                             int32_t* counts, hipStream_t s);
+hipError_t launch_select_config(const moe_problem& p, const int32_t* counts, const float* theta,
+                                const CostTable& tab, int32_t* variant, float* t_hat,
+                                hipStream_t s);
+hipError_t launch_align_sort(const moe_problem& p, const int32_t* ids, const int32_t* variant,
+                             int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
+                             int32_t* slot_pos, hipStream_t s);
+hipError_t launch_grouped_ffn(const moe_problem& p, const void* x, const void* w1,
+                              const void* w3, const void* w2, const float* s1, const float* s3,
+                              const float* s2, const int32_t* sorted_slots,
+                              const int32_t* block_expert, const int32_t* num_blocks,
+                              const int32_t* variant, void* y_slots, void* h, int num_cus,
+                              int64_t rows_max, hipStream_t s);
+hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
+                          const float* w, void* y, int64_t rows_max, hipStream_t s);
+
+
+}  // namespace moe

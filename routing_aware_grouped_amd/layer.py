@@ -1,0 +1,150 @@
+"""Device buffers for one fused-MoE problem and the five library calls in order.
+
+Holds no arithmetic of its own: torch allocates device memory, and `forward`
+enqueues moe_route_topk -> moe_select_config -> moe_align_sort ->
+moe_grouped_ffn -> moe_combine on one stream, with no host synchronisation, so a
+caller may capture it in a HIP graph.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_grouped_ffn,
+               moe_num_variants, moe_problem, moe_query_sizes, moe_route_topk, moe_select_config)
+
+_TORCH_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+
+@dataclasses.dataclass
+class Buffers:
+    p: moe_problem
+    logits: torch.Tensor
+    x: torch.Tensor
+    w1: torch.Tensor
+    w3: torch.Tensor
+    w2: torch.Tensor
+    s1: torch.Tensor | None
+    s3: torch.Tensor | None
+    s2: torch.Tensor | None
+    theta: torch.Tensor
+    topk_ids: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    variant: torch.Tensor
+    t_hat: torch.Tensor
+    sorted_slots: torch.Tensor
+    block_expert: torch.Tensor
+    num_blocks: torch.Tensor
+    slot_pos: torch.Tensor
+    y_slots: torch.Tensor
+    workspace: torch.Tensor
+    y: torch.Tensor
+
+
+def allocate(p: moe_problem, logits, x, w1, w3, w2, s1=None, s3=None, s2=None, theta=None,
+             device="cuda") -> Buffers:
+    """Output/intermediate buffers sized by moe_query_sizes; inputs are moved to
+    the device as given (already dtype-encoded)."""
+    sz = moe_query_sizes(p)
+    B, k, El = p.tokens, p.top_k, p.local_experts
+    V = moe_num_variants()
+    dev = torch.device(device)
+    act = _TORCH_ACT[p.act_dtype]
+
+    def d(t):
+        return None if t is None else t.to(dev).contiguous()
+
+    if theta is None:
+        theta = torch.zeros(V, 4, dtype=torch.float32)
+    return Buffers(
+        p=p, logits=d(logits), x=d(x), w1=d(w1), w3=d(w3), w2=d(w2), s1=d(s1), s3=d(s3), s2=d(s2),
+        theta=d(theta),
+        topk_ids=torch.empty(B, k, dtype=torch.int32, device=dev),
+        topk_w=torch.empty(B, k, dtype=torch.float32, device=dev),
+        counts=torch.empty(El, dtype=torch.int32, device=dev),
+        variant=torch.zeros(1, dtype=torch.int32, device=dev),
+        t_hat=torch.empty(V, dtype=torch.float32, device=dev),
+        sorted_slots=torch.empty(sz.rows_max, dtype=torch.int32, device=dev),
+        block_expert=torch.empty(sz.blocks_max, dtype=torch.int32, device=dev),
+        num_blocks=torch.zeros(1, dtype=torch.int32, device=dev),
+        slot_pos=torch.empty(B * k, dtype=torch.int32, device=dev),
+        y_slots=torch.empty(sz.rows_max, p.hidden, dtype=act, device=dev),
+        workspace=torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=dev),
+        y=torch.empty(B, p.hidden, dtype=act, device=dev),
+    )
+
+
+def route(b: Buffers, stream=None):
+    moe_route_topk(b.p, b.logits, b.topk_ids, b.topk_w, b.counts, stream)
+
+
+def select(b: Buffers, stream=None):
+    moe_select_config(b.p, b.counts, b.theta, b.variant, b.t_hat, stream)
+
+
+def align(b: Buffers, stream=None):
+    moe_align_sort(b.p, b.topk_ids, b.variant, b.sorted_slots, b.block_expert, b.num_blocks,
+                   b.slot_pos, stream)
+
+
+def ffn(b: Buffers, stream=None):
+    moe_grouped_ffn(b.p, b.x, b.w1, b.w3, b.w2, b.s1, b.s3, b.s2, b.sorted_slots, b.block_expert,
+                    b.num_blocks, b.variant, b.y_slots, b.workspace, None, stream)
+
+
+def combine(b: Buffers, stream=None):
+    moe_combine(b.p, b.y_slots, b.slot_pos, b.topk_w, b.y, stream)
+
+
+def forward(b: Buffers, stream=None, forced_variant: bool = False):
+    """The whole layer.  With forced_variant the select step is skipped and the
+    value already in b.variant is used (exhaustive timing of every configuration)."""
+    route(b, stream)
+    if not forced_variant:
+        select(b, stream)
+    align(b, stream)
+    ffn(b, stream)
+    combine(b, stream)
+
+
+def weight_tensors(layer):
+    """Host numpy (dtype-encoded) -> torch tensors of the library's element types."""
+    import numpy as np
+    wd = layer.shape.weight_dtype
+
+    def conv(a):
+        if wd == MOE_F32:
+            return torch.from_numpy(np.ascontiguousarray(a, np.float32))
+        if wd == MOE_BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).view(torch.float8_e4m3fn)
+
+    s = [None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32))
+         for a in (layer.s1, layer.s3, layer.s2)]
+    return conv(layer.w1), conv(layer.w3), conv(layer.w2), s[0], s[1], s[2]
+
+
+def act_tensor(layer, a):
+    import numpy as np
+    if layer.shape.act_dtype == MOE_F32:
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def problem_of(layer, renormalize: int = 1) -> moe_problem:
+    sh = layer.shape
+    return moe_problem(layer.tokens, sh.hidden, sh.inter, sh.num_experts, layer.expert_begin,
+                       sh.local_experts, sh.top_k, sh.act_dtype, sh.weight_dtype, renormalize)
+
+
+def from_layer(layer, theta=None, device="cuda", weights=None, renormalize: int = 1) -> Buffers:
+    """Buffers for a synthetic layer (see synth.Layer); `weights` reuses device
+    weight tensors (w1, w3, w2, s1, s3, s2) across loads."""
+    p = problem_of(layer, renormalize)
+    if weights is None:
+        weights = weight_tensors(layer)
+    w1, w3, w2, s1, s3, s2 = weights
+    return allocate(p, torch.from_numpy(layer.logits), act_tensor(layer, layer.x), w1, w3, w2, s1,
+                    s3, s2, theta=theta, device=device)

@@ -202,7 +202,7 @@ def make_layer(shape_name: str, tokens: int, alpha: float | None = None, rep: in
     (the weights of a layer do not change between batches)."""
     shape = SHAPES[shape_name]
     ss = seed_seq(shape_name, tokens, alpha, rep)
-    r_route, r_x, r_w = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3))
+    r_route, r_x = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(2))
     logits, p = routing_logits(shape, tokens, alpha, r_route)
     e0 = most_loaded_block(p, shape)
     x = _encode(r_x.standard_normal((tokens, shape.hidden), dtype=np.float32) * np.float32(x_std),
@@ -218,3 +218,52 @@ def layer_weights_for(shape_name: str) -> dict:
     shape = SHAPES[shape_name]
     return make_weights(shape, np.random.Generator(np.random.PCG64(
         np.random.SeedSequence([CFG_INDEX[shape_name], 7777]))))
+
+
+# ----------------------------------------------------------------------------------
+# On-device weight generation for the full-size shapes (seeded torch generator).
+# Same distribution and fp8 recipe as make_weights; a different stream of numbers.
+# ----------------------------------------------------------------------------------
+def make_weights_device(shape_name: str, device="cuda", std: float = 0.02, seed: int | None = None):
+    """Dict w1, w3, w2 (+ s1, s3, s2 for fp8) of torch tensors on `device`, dtype-
+    encoded (float32 / bfloat16 / float8_e4m3fn)."""
+    shape = SHAPES[shape_name]
+    El, H, I = shape.local_experts, shape.hidden, shape.inter
+    wd = shape.weight_dtype
+    g = torch.Generator(device=device)
+    g.manual_seed(CFG_INDEX[shape_name] * 1_000_003 + 7777 if seed is None else seed)
+    out = {}
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.float8_e4m3fn}[wd]
+    for name, (r, c) in (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I))):
+        q = torch.empty((El, r, c), dtype=tdt, device=device)
+        s = torch.empty((El, r // 128, c // 128), dtype=torch.float32, device=device) if wd == FP8 else None
+        for e in range(El):
+            w = torch.randn((r, c), generator=g, device=device, dtype=torch.float32) * std
+            if wd == FP8:
+                blk = w.reshape(r // 128, 128, c // 128, 128)
+                amax = blk.abs().amax(dim=(1, 3))
+                sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+                q[e] = (blk / sc[:, None, :, None]).clamp_(-448.0, 448.0).reshape(r, c).to(tdt)
+                s[e] = sc
+            else:
+                q[e] = w.to(tdt)
+        out[name] = q
+        out["s" + name[1]] = s
+    return out
+
+
+def host_weights(wdev: dict) -> dict:
+    """Device weights -> the numpy encodings make_weights returns."""
+    out = {}
+    for k, v in wdev.items():
+        if v is None:
+            out[k] = None
+            continue
+        t = v.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            out[k] = t.view(torch.int16).numpy().view(np.uint16)
+        elif t.dtype == torch.float8_e4m3fn:
+            out[k] = t.view(torch.uint8).numpy()
+        else:
+            out[k] = t.numpy()
+    return out

@@ -1,0 +1,25 @@
+"""The documented configuration menu of the grouped kernel, written out by the
+tests as a specification.  The library's moe_variant_info / moe_cost_constants
+are checked against it, and the oracle's cost-model inputs come from here (never
+from the library)."""
+
+# BLOCK_M, BLOCK_N gate/up, BLOCK_N down, BLOCK_K, waves M, N, K-split, split-K
+MENU = [
+    (16, 16, 16, 128, 1, 1, 4, 1),
+    (32, 32, 32, 64, 1, 2, 2, 1),
+    (64, 64, 64, 32, 2, 2, 1, 1),
+    (128, 64, 128, 32, 2, 2, 1, 1),
+]
+# workgroups per compute unit of the persistent gate/up and down launches
+WG_PER_CU = (2, 2)
+
+
+def cost_constants(hidden: int, inter: int, num_cus: int) -> dict:
+    """b, q1, q2, S1, S2 per configuration, per the definitions in include/moe.h."""
+    return {
+        "b": [m[0] for m in MENU],
+        "q1": [inter // m[1] for m in MENU],
+        "q2": [(hidden // m[2]) * m[7] for m in MENU],
+        "S1": [num_cus * WG_PER_CU[0]] * len(MENU),
+        "S2": [num_cus * WG_PER_CU[1]] * len(MENU),
+    }

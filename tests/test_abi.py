@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/moe.h
+declares, and its host-side validation returns the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_aware_grouped_amd as moe
+from tests import spec
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|int32_t|size_t)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 9
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    for n in ("moe_route_topk", "moe_select_config", "moe_align_sort", "moe_grouped_ffn",
+              "moe_combine"):
+        assert n in names
+
+
+def test_binding_mirrors_names():
+    for n in _declared():
+        assert callable(getattr(moe, n)), n
+
+
+def test_variant_menu_matches_spec():
+    assert moe.moe_abi_version() == 1
+    assert moe.moe_num_variants() == len(spec.MENU)
+    for v, m in enumerate(spec.MENU):
+        assert tuple(moe.moe_variant_info(v)) == m
+    for bad in (-1, len(spec.MENU)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_variant_info(bad)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def _p(**kw):
+    base = dict(tokens=64, hidden=128, inter=256, num_experts=8, top_k=2, act_dtype=moe.MOE_F32,
+                weight_dtype=moe.MOE_F32)
+    base.update(kw)
+    extra = {k: base.pop(k) for k in ("expert_begin", "local_experts", "renormalize") if k in base}
+    return moe.problem(base.pop("tokens"), base.pop("hidden"), base.pop("inter"),
+                       base.pop("num_experts"), base.pop("top_k"), **base, **extra)
+
+
+def test_query_sizes():
+    s = moe.moe_query_sizes(_p())
+    B, k, El, bmax = 64, 2, 8, max(m[0] for m in spec.MENU)
+    assert s.rows_max == B * k + min(El, B * k) * (bmax - 1)
+    assert s.blocks_max >= s.rows_max // min(m[0] for m in spec.MENU)
+    assert s.y_slots_bytes == s.rows_max * 128 * 4
+    assert s.workspace_bytes >= s.rows_max * 256 * 4
+    s2 = moe.moe_query_sizes(_p(tokens=4096, hidden=2048, inter=768, num_experts=128, top_k=8,
+                                act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16))
+    assert s2.y_slots_bytes == s2.rows_max * 2048 * 2
+    # monotone in the token count
+    prev = 0
+    for B in (1, 2, 17, 256, 4096):
+        r = moe.moe_query_sizes(_p(tokens=B)).rows_max
+        assert r >= prev
+        prev = r
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tokens=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(hidden=100), moe.MOE_ERR_INVALID_ARG),
+    (dict(inter=192), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=64, top_k=33), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_begin=4, local_experts=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(local_experts=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(renormalize=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=moe.MOE_F32, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=moe.MOE_FP8_E4M3, weight_dtype=moe.MOE_FP8_E4M3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(tokens=1 << 20, num_experts=1024, local_experts=1024, top_k=8), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_problems(kw, status):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_query_sizes(_p(**kw))
+    assert ei.value.status == status
+
+
+def test_compute_calls_validate_before_any_gpu_work():
+    p = _p()
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route_topk(p, 0, 0, 0, 0, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_select_config(p, 0, 0, 0, None, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_align_sort(p, 0x1000, 0x1000, 0, 0x1000, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_combine(p, 0x1000, 0x1000, 0x1000, 0x1004, stream=0)  # y misaligned
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    sz = moe.moe_query_sizes(p)
+    a = 0x10000
+    with pytest.raises(moe.MoeError) as ei:  # workspace one byte short
+        moe.moe_grouped_ffn(p, a, a, a, a, None, None, None, a, a, a, a, a, a,
+                            sz.workspace_bytes - 1, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    pf = _p(act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3)
+    with pytest.raises(moe.MoeError) as ei:  # fp8 weights need their scales
+        moe.moe_grouped_ffn(pf, a, a, a, a, None, None, None, a, a, a, a, a, a, 1 << 30, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_query_sizes(None)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG

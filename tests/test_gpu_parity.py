@@ -1,0 +1,262 @@
+"""GPU parity: every step of the HIP path against the CPU oracle on the same seeded
+inputs.  Integer outputs (ids, counts, chosen configuration, permutation, block
+table, inverse map) bit-exact; weights |d| <= 1e-6; Y within
+max|gpu - ref| / max|ref| <= 1e-5 (fp32), 1e-2 (bf16), 5e-2 (fp8 weights)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from routing_aware_grouped_amd import layer as L
+from tests import gpu_helpers as G
+from tests import spec
+
+pytestmark = pytest.mark.gpu
+V = len(spec.MENU)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+# ----------------------------------------------------------------- tiny fp32 ---
+@pytest.mark.parametrize("v", range(V))
+def test_tiny_fp32_every_variant(v):
+    G.say(f"tiny fp32 B=64 variant={v}")
+    layer = synth.make_layer("tiny", 64, None, 0)
+    out = G.fetch(G.run(layer, variant=v))
+    ids, w = G.check_routing(layer, out)
+    G.check_align(layer, out, ids)
+    G.check_y(layer, out, ids, w)
+
+
+def test_tiny_renormalize_off_and_selection():
+    layer = synth.make_layer("tiny", 64, None, 1)
+    b = G.run(layer, theta=G.theta_forcing(2), renormalize=0)
+    out = G.fetch(b)
+    assert out["variant"] == 2
+    ids, w = G.check_routing(layer, out, renormalize=0)
+    G.check_align(layer, out, ids)
+    G.check_y(layer, out, ids, w)
+
+
+def test_tiny_large_activations_and_ragged_tokens():
+    """x ~ N(0, 1) reaches SwiGLU's non-linear range; B = 37 leaves ragged tiles."""
+    layer = synth.make_layer("tiny", 37, None, 2, x_std=1.0)
+    for v in range(V):
+        out = G.fetch(G.run(layer, variant=v))
+        ids, w = G.check_routing(layer, out)
+        G.check_align(layer, out, ids)
+        G.check_y(layer, out, ids, w)
+
+
+# -------------------------------------------------------------- routing only ---
+@pytest.mark.parametrize("shape,B,alpha", [
+    ("qwen3", 1, 0.3), ("qwen3", 4096, 0.05), ("qwen3", 1000, 10.0), ("mixtral", 2048, 0.1),
+    ("mixtral", 3, 1.0), ("dsv3_share", 2048, 1.0), ("kimi_share", 4096, 0.05),
+    ("kimi_share", 65, 0.05)])
+def test_routing_and_permutation_full_batch(shape, B, alpha):
+    G.say(f"routing {shape} B={B} alpha={alpha}")
+    sh = synth.SHAPES[shape]
+    rng = np.random.default_rng([B, 3])
+    logits, p = synth.routing_logits(sh, B, alpha, rng)
+    e0 = synth.most_loaded_block(p, sh)
+    H, I = 256, 256  # the FFN is not exercised here; keep its buffers small
+    p_ = L.moe_problem(B, H, I, sh.num_experts, e0, sh.local_experts, sh.top_k, synth.BF16,
+                       synth.BF16, 1)
+    z = torch.zeros
+    w1 = z(sh.local_experts, I, H, dtype=torch.bfloat16)
+    w2 = z(sh.local_experts, H, I, dtype=torch.bfloat16)
+    for v in range(V):
+        b = L.allocate(p_, torch.from_numpy(logits), z(B, H, dtype=torch.bfloat16), w1, w1, w2,
+                       theta=G.theta_forcing(v))
+        L.route(b)
+        L.select(b)
+        L.align(b)
+        torch.cuda.synchronize()
+        out = G.fetch(b)
+        assert out["variant"] == v
+        lay = synth.Layer(sh, B, alpha, e0, logits, None, None, None, None)
+        ids, _ = G.check_routing(lay, out)
+        G.check_align(lay, out, ids)
+
+
+def test_routing_ties_and_signed_zeros():
+    """Equal logits go to the lower expert index; -0 equals +0."""
+    rng = np.random.default_rng(44)
+    for E, k in ((8, 2), (128, 8), (384, 8)):
+        B = 300
+        lg = rng.integers(-3, 4, size=(B, E)).astype(np.float32) * 0.5
+        zm = rng.random((B, E)) < 0.2
+        lg[zm] = np.where(rng.random(zm.sum()) < 0.5, -0.0, 0.0)
+        sh = synth.Shape("t", 128, 128, E, E, k, synth.BF16, synth.BF16, synth.BF16, "normal")
+        p_ = L.moe_problem(B, 128, 128, E, 0, E, k, synth.BF16, synth.BF16, 1)
+        w = torch.zeros(E, 128, 128, dtype=torch.bfloat16)
+        b = L.allocate(p_, torch.from_numpy(lg), torch.zeros(B, 128, dtype=torch.bfloat16), w, w, w)
+        L.route(b)
+        L.select(b)
+        L.align(b)
+        torch.cuda.synchronize()
+        out = G.fetch(b)
+        lay = synth.Layer(sh, B, None, 0, lg, None, None, None, None)
+        ids, _ = G.check_routing(lay, out)
+        G.check_align(lay, out, ids)
+
+
+# ------------------------------------------------------------------ selection --
+def test_select_config_bit_exact():
+    """Chosen index and every fp32 prediction equal the oracle's, on random loads
+    and random cost coefficients (including exact ties between configurations)."""
+    from routing_aware_grouped_amd import moe_cost_constants, moe_select_config
+    rng = np.random.default_rng(5)
+    ncu = G.num_cus()
+    for trial in range(60):
+        El = int(rng.choice([8, 32, 48, 128, 1000]))
+        H, I = (2048, 768) if trial % 2 else (7168, 2048)
+        p_ = L.moe_problem(64, H, I, El, 0, El, 8, synth.BF16, synth.BF16, 1)
+        cc = spec.cost_constants(H, I, ncu)
+        assert moe_cost_constants(p_) == cc
+        cnt = (rng.integers(0, 600, El) * (rng.random(El) < rng.random())).astype(np.int32)
+        th = (rng.random((V, 4)) * np.array([20, 5, 0.05, 0.5])).astype(np.float32)
+        if trial % 4 == 0:
+            th[V - 1] = th[0]
+        d_cnt = torch.from_numpy(cnt).cuda()
+        d_th = torch.from_numpy(th).cuda()
+        var = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        t_hat = torch.empty(V, dtype=torch.float32, device="cuda")
+        moe_select_config(p_, d_cnt, d_th, var, t_hat)
+        torch.cuda.synchronize()
+        ref_v, ref_t, _ = oracle.select(cnt, cc["b"], cc["q1"], cc["q2"], cc["S1"], cc["S2"], th)
+        assert int(var.item()) == ref_v
+        np.testing.assert_array_equal(t_hat.cpu().numpy().view(np.uint32), ref_t.view(np.uint32))
+
+
+# ------------------------------------------------------- bf16 / fp8 layers -----
+@pytest.mark.parametrize("shape,B,alpha,sample", [
+    ("qwen3", 1, 0.3, None), ("qwen3", 37, 1.0, None), ("qwen3", 130, 0.05, None),
+    ("mixtral", 1, 1.0, None), ("mixtral", 5, 0.1, None),
+    ("dsv3_share", 8, 1.0, None), ("dsv3_share", 96, 0.1, 24),
+    ("kimi_share", 64, 0.05, 24)])
+def test_layer_every_variant(shape, B, alpha, sample):
+    G.say(f"layer {shape} B={B} alpha={alpha}")
+    wdev, whost = G.weights(shape)
+    layer = synth.make_layer(shape, B, alpha, 0, weights=whost)
+    ids, w = oracle.route_topk(layer.logits, layer.shape.top_k)
+    toks = None
+    if sample is not None:
+        toks = np.random.default_rng(B).choice(B, sample, replace=False).astype(np.int32)
+    ref = None
+    for v in range(V):
+        out = G.fetch(G.run(layer, variant=v, wdev=wdev))
+        G.check_routing(layer, out)
+        G.check_align(layer, out, ids)
+        err, ref = G.check_y(layer, out, ids, w, toks, ref)
+        G.say(f"  variant {v}: rel err {err:.3g}")
+
+
+def test_one_hot_router_is_dense():
+    """All tokens on one expert: the layer equals that expert's dense FFN."""
+    wdev, whost = G.weights("qwen3")
+    layer = synth.make_layer("qwen3", 200, 1.0, 0, weights=whost)
+    layer.logits[:] = -10.0
+    layer.logits[:, 77] = 10.0  # expert 77 first for every token, then 0..6 (ties)
+    out = G.fetch(G.run(layer, theta=G.theta_forcing(3), wdev=wdev))
+    ids, w = G.check_routing(layer, out)
+    assert np.all(ids[:, 0] == 77)
+    G.check_align(layer, out, ids)
+    G.check_y(layer, out, ids, w, tokens=np.arange(0, 200, 7))
+
+
+def test_empty_rank_gives_zero_output():
+    """An expert block that receives no token: no tiles, and Y = 0."""
+    wdev, whost = G.weights("dsv3_share")
+    layer = synth.make_layer("dsv3_share", 16, 1.0, 0, weights=whost)
+    layer.logits[:, layer.expert_begin:layer.expert_begin + 32] = -50.0
+    out = G.fetch(G.run(layer, theta=G.theta_forcing(0), wdev=wdev))
+    ids, w = G.check_routing(layer, out)
+    assert out["num_blocks"] == 0 and np.all(out["counts"] == 0)
+    assert np.all(out["slot_pos"] == -1)
+    assert np.all(out["Y"] == 0.0)
+
+
+def test_out_of_range_variant_gives_no_tiles():
+    layer = synth.make_layer("tiny", 64, None, 3)
+    b = G.run(layer, variant=0)
+    b.variant.fill_(V + 3)
+    b.y.fill_(1.0)
+    L.align(b)
+    L.ffn(b)
+    L.combine(b)
+    torch.cuda.synchronize()
+    assert int(b.num_blocks.item()) == 0
+    assert torch.all(b.slot_pos == -1)
+    assert torch.all(b.y == 0)
+
+
+def test_fp8_decode_every_code():
+    """With one-hot tokens, W3 = 1 and W2 = I, each output element is
+    silu(s * q) of one fp8 weight code: every code must decode exactly as OCP
+    E4M3FN (checked element by element, not in aggregate)."""
+    H, I, E, B = 256, 128, 1, 256
+    codes = (np.arange(I)[:, None] * 256 + np.arange(H)[None, :]) % 256
+    codes[(codes & 0x7F) == 0x7F] = 0  # NaN codes are outside the contract
+    w1 = codes.astype(np.uint8)[None]
+    w3 = np.full((1, I, H), 0x38, np.uint8)  # 1.0
+    w2 = np.zeros((1, H, I), np.uint8)
+    w2[0, np.arange(I), np.arange(I)] = 0x38  # identity on the first I outputs
+    s1 = np.array([[[1.0, 0.25]]], np.float32)
+    s3 = np.ones((1, 1, 2), np.float32)
+    s2 = np.ones((1, 2, 1), np.float32)
+    x = np.zeros((B, H), np.float32)
+    x[np.arange(B), np.arange(B) % H] = 1.0
+    sh = synth.Shape("fp8codes", H, I, E, E, 1, synth.BF16, synth.FP8, synth.BF16, "normal")
+    layer = synth.Layer(sh, B, None, 0, np.zeros((B, E), np.float32), synth.to_bf16_bits(x),
+                        w1, w3, w2, s1, s3, s2)
+    out = G.fetch(G.run(layer, variant=0))
+    ids, w = oracle.route_topk(layer.logits, 1)
+    ref = oracle.layer_tokens(layer, ids, w, np.arange(B, dtype=np.int32))
+    gpu = out["Y"].astype(np.float64)
+    bad = np.abs(gpu - ref) > 1e-2 * np.abs(ref) + 1e-30
+    assert not bad.any(), f"{bad.sum()} elements differ, first at {np.argwhere(bad)[:4]}"
+
+
+def test_deterministic_repeat():
+    wdev, whost = G.weights("qwen3")
+    layer = synth.make_layer("qwen3", 300, 0.3, 1, weights=whost)
+    for v in range(V):
+        a = G.run(layer, variant=v, wdev=wdev).y.clone()
+        c = G.run(layer, variant=v, wdev=wdev).y.clone()
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_graph_replay_matches_eager():
+    """The five calls captured in one HIP graph replay to the eager result, with
+    eager work and synchronisation between replays."""
+    wdev, whost = G.weights("qwen3")
+    layer = synth.make_layer("qwen3", 64, 1.0, 2, weights=whost)
+    th = torch.tensor([[5.0, 0.0, 0.01, 0.1]] * V, dtype=torch.float32)
+    th[:, 0] += torch.arange(V, dtype=torch.float32)
+    b = L.from_layer(layer, theta=th, weights=G.device_weights(layer, wdev))
+    L.forward(b)
+    torch.cuda.synchronize()
+    eager = b.y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.forward(b, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    b.y.zero_()
+    with torch.cuda.graph(g):
+        L.forward(b)
+    for r in range(4):
+        b.y.fill_(float(r + 1))
+        b.sorted_slots.fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.y.view(torch.int16), eager.view(torch.int16)), r
