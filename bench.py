@@ -225,7 +225,25 @@ def main():
     ap.add_argument("--exhaustive", type=int, default=1,
                     help="1: also time every configuration at the headline point")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "known-size kernel that scales HBM byte counters) and exit")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for i in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            print(f"copy {args.calibrate_copy} MiB: read {n} B + write {n} B in {dt * 1e6:.1f} us "
+                  f"({2 * n / dt / 1e9:.1f} GB/s wall)", flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the layer on one GPU "
