@@ -22,7 +22,8 @@
  *   moe_grouped_ffn    the polymorphic grouped expert kernel: every compiled
  *                      configuration lives in one kernel that reads c* from device
  *                      memory (RaMP section 3.3); gate/up with fused SwiGLU, then
- *                      the down projection.
+ *                      the down projection (also callable one phase at a time:
+ *                      moe_grouped_gate_up, moe_grouped_down).
  *   moe_combine        y_t = sum_j g_{t,j} y_{t,j}, accumulated in fp32 in j order
  *                      (GC-MoE section 4, the combine role).
  *
@@ -110,7 +111,8 @@ int32_t moe_num_variants(void);
  *   [0] BLOCK_M  token rows per tile (b_c of RaMP Eq. 1)
  *   [1] BLOCK_N of the gate/up phase (output columns of W1 and of W3 per tile)
  *   [2] BLOCK_N of the down phase
- *   [3] BLOCK_K  reduction depth per pipeline stage
+ *   [3] BLOCK_K  reduction depth per pipeline stage for bf16 operands (the fp32
+ *                problem uses half of it; fp8 weights are staged as bf16)
  *   [4] waves along M, [5] waves along N, [6] waves splitting K inside a tile
  *   [7] split-K of the down phase across tiles (1 = none)
  * Errors: MOE_ERR_INVALID_ARG for v outside [0, V) or out == NULL. */
@@ -162,19 +164,40 @@ moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const i
                           int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
                           int32_t* slot_pos, void* stream);
 
-/* Step 4: grouped expert FFN (RaMP 3.3; GC-MoE 2.1 Eq. 1).  For every row r < R:
+/* Step 4: grouped expert FFN (RaMP 3.3 and A.8; GC-MoE 2.1 Eq. 1).  For every
+ * row r < R that holds a slot (sorted_slots[r] >= 0):
  *   h[r]       = silu(x[t] W1_e^T) * (x[t] W3_e^T)   (t = sorted_slots[r] / k)
  *   y_slots[r] = h[r] W2_e^T                          (e = block_expert[r / b])
- * Padding rows produce zeros.  x is [B][H] (act dtype); s1/s3/s2 are the fp8
- * block scales (NULL unless weight_dtype is MOE_FP8_E4M3).  y_slots
+ * Padding rows are neither read nor written.  x is [B][H] (act dtype); s1/s3/s2
+ * are the fp8 block scales (NULL unless weight_dtype is MOE_FP8_E4M3).  y_slots
  * [rows_max][H] (act dtype).  workspace: >= workspace_bytes, 256-byte aligned;
- * holds h.  Every configuration shares one persistent launch; the kernel reads
- * *variant and *num_blocks from device memory. */
+ * holds h.  The call enqueues two launches of one persistent polymorphic kernel,
+ * the gate/up phase and then the down phase (moe_grouped_gate_up followed by
+ * moe_grouped_down); each reads *variant and *num_blocks from device memory, so
+ * every compiled configuration runs under one fixed launch shape. */
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
                            const void* w2, const float* s1, const float* s3, const float* s2,
                            const int32_t* sorted_slots, const int32_t* block_expert,
                            const int32_t* num_blocks, const int32_t* variant, void* y_slots,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 4a alone: the grouped gate/up GEMM with the fused SwiGLU, writing h into
+ * workspace (as moe_grouped_ffn's first launch).  Arguments and errors as for
+ * moe_grouped_ffn; w2, s2 and y_slots are not used. */
+moe_status moe_grouped_gate_up(const moe_problem* p, const void* x, const void* w1,
+                               const void* w3, const float* s1, const float* s3,
+                               const int32_t* sorted_slots, const int32_t* block_expert,
+                               const int32_t* num_blocks, const int32_t* variant, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Step 4b alone: the grouped down GEMM, y_slots[r] = h[r] W2_e^T with h read from
+ * workspace (written by moe_grouped_gate_up for the same grouping and variant).
+ * Arguments and errors as for moe_grouped_ffn; x, w1, w3, s1 and s3 are not
+ * used. */
+moe_status moe_grouped_down(const moe_problem* p, const void* w2, const float* s2,
+                            const int32_t* sorted_slots, const int32_t* block_expert,
+                            const int32_t* num_blocks, const int32_t* variant, void* y_slots,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 5: combine (GC-MoE 2.1 Eq. 1; the slot-order reduction of its combine
  * role).  y [B][H] (act dtype) = sum over j = 0..k-1 with slot_pos[t*k+j] >= 0 of

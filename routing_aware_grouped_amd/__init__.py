@@ -61,6 +61,10 @@ _SIGS = {
     "moe_align_sort": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P], ctypes.c_int),
     "moe_grouped_ffn": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P, P, P, P,
                          ctypes.c_size_t, P], ctypes.c_int),
+    "moe_grouped_gate_up": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P,
+                             ctypes.c_size_t, P], ctypes.c_int),
+    "moe_grouped_down": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, ctypes.c_size_t, P],
+                         ctypes.c_int),
     "moe_combine": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
 }
 
@@ -153,14 +157,34 @@ def moe_align_sort(p, topk_ids, variant, sorted_slots, block_expert, num_blocks,
                                                   _ptr(num_blocks), _ptr(slot_pos), _stream(stream)))
 
 
+def _ws_bytes(workspace, workspace_bytes):
+    if workspace_bytes is None:
+        return workspace.numel() * workspace.element_size()
+    return int(workspace_bytes)
+
+
 def moe_grouped_ffn(p, x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks,
                     variant, y_slots, workspace, workspace_bytes=None, stream=None):
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         _pp(p), _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2),
         _ptr(sorted_slots), _ptr(block_expert), _ptr(num_blocks), _ptr(variant), _ptr(y_slots),
-        _ptr(workspace), int(workspace_bytes), _stream(stream)))
+        _ptr(workspace), _ws_bytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def moe_grouped_gate_up(p, x, w1, w3, s1, s3, sorted_slots, block_expert, num_blocks, variant,
+                        workspace, workspace_bytes=None, stream=None):
+    _check("moe_grouped_gate_up", lib().moe_grouped_gate_up(
+        _pp(p), _ptr(x), _ptr(w1), _ptr(w3), _ptr(s1), _ptr(s3), _ptr(sorted_slots),
+        _ptr(block_expert), _ptr(num_blocks), _ptr(variant), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def moe_grouped_down(p, w2, s2, sorted_slots, block_expert, num_blocks, variant, y_slots,
+                     workspace, workspace_bytes=None, stream=None):
+    _check("moe_grouped_down", lib().moe_grouped_down(
+        _pp(p), _ptr(w2), _ptr(s2), _ptr(sorted_slots), _ptr(block_expert), _ptr(num_blocks),
+        _ptr(variant), _ptr(y_slots), _ptr(workspace), _ws_bytes(workspace, workspace_bytes),
+        _stream(stream)))
 
 
 def moe_combine(p, y_slots, slot_pos, topk_w, y, stream=None):

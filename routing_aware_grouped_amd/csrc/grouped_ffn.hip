@@ -1,46 +1,77 @@
-// grouped_ffn.hip -- step 4: the polymorphic grouped expert FFN.
+// grouped_ffn.hip -- the polymorphic, persistent grouped expert FFN (both GEMMs in
+// one launch).
 //
-// For each padded row r of the expert grouping (expert e = block_expert[r / b]):
-//   phase 1:  h[r] = silu(x[t] W1_e^T) * (x[t] W3_e^T),  t = sorted_slots[r] / k
-//   phase 2:  y_slots[r] = h[r] W2_e^T
-// (GC-MoE arXiv 2611.04222, 2.1 Eq. 1: W1 stacks gate and up, W2 is the down
-// projection; RaMP arXiv 2604.26039, 2.1: each expert is a gated MLP.)  Padding rows
-// (sorted_slots = -1) read zeros and so produce zeros.
+// What is computed, for every padded row r of the expert grouping with
+// e = block_expert[r / b] and t = sorted_slots[r] / k (GC-MoE arXiv 2611.04222,
+// section 2.1, Eq. 1: W1 stacks gate and up, W2 is the down projection; RaMP arXiv
+// 2604.26039, section 2.1: each expert is a gated MLP):
+//   gate/up phase:  h[r]       = silu(x[t] W1_e^T) * (x[t] W3_e^T)
+//   down phase:     y_slots[r] = h[r] W2_e^T
+// Padding rows (sorted_slots = -1) are neither read nor written.
 //
-// Polymorphism (RaMP 3.3): every compiled tile configuration lives in one kernel per
-// phase.  Each workgroup reads the chosen index and the row-block count from device
-// memory and runs that configuration's tiles, so the launch shape is fixed and the
-// choice needs neither a host round trip nor a new launch.  The grid is persistent
-// (compute units x workgroups per unit, capped by the largest tile count any
-// configuration can produce); workgroups stride over the chosen configuration's
-// tiles.  All configurations share one 256-thread workgroup shape, one LDS budget
-// and one register allocation (one occupancy class).
+// Polymorphism (RaMP section 3.3 and appendix A.8): every compiled tile
+// configuration lives in this one kernel.  Each workgroup reads the chosen index
+// and the row-block count from device memory and runs that configuration, so the
+// launch shape is fixed and the choice needs no host round trip.  All
+// configurations share one workgroup size, one LDS allocation and one register
+// budget (one occupancy class).
 //
-// Tile order: the tile index runs over row-blocks fastest, so consecutive tiles
-// reuse one expert's weight panel; workgroup ids are remapped so that consecutive
-// tiles land on the same XCD (the hardware deals workgroups round-robin over the 8
-// XCDs, each with its own L2).
+// Scheduling.  The two GEMM phases are two launches of this kernel (the down
+// phase needs every column of h for its row-block, and a dependency between
+// workgroups of one launch would need a wait); each launch is persistent
+// (compute units x 1 workgroups) and deals its tiles out statically:
+// tile t = rb + nb * nt (row-block fastest, so the row-blocks of one expert that
+// share a weight slab are adjacent) goes to slot t mod G, and slots are numbered
+// so that 32 consecutive ones sit on one XCD (the hardware deals workgroup ids
+// round-robin over the 8 XCDs, each with its own L2).  There are no atomics and
+// no waits between workgroups; every loop has a static bound.
 //
-// Math: bf16 (and fp8-decoded) operands on v_mfma_f32_16x16x32_bf16, fp32
-// accumulation; the fp32 problem uses v_mfma_f32_16x16x4_f32 over the same k=32
-// fragments.  Rows are tokens (the MFMA A operand), columns are weight rows (B
-// operand), both K-contiguous in memory, so each lane's 8-element fragment is one
-// 16-byte (bf16), 8-byte (fp8) or 32-byte (f32) contiguous load.  FP8 E4M3FN weights
-// are decoded with the hardware converter, multiplied by their 128x128 block scale
-// in fp32 and rounded to bf16 (w = q * s).
+// Data movement.  Each pipeline stage covers BK elements of the reduction for the
+// tile's A rows (tokens, or h rows) and its weight rows.  Threads load 16-byte
+// chunks so that consecutive lanes read consecutive bytes of one row (a wave
+// instruction reads 1 KiB of contiguous rows: full cache lines, the pattern that
+// streams HBM fastest), hold them in registers RS stages ahead, and write them to
+// a double-buffered LDS tile.  LDS rows are XOR-swizzled in 16-byte units so that
+// the MFMA fragment reads (16 rows x 16 bytes per quarter wave) are conflict free.
+// FP8 E4M3FN weights are decoded once, while staging: w = q * s with the 128 x 128
+// block scale in fp32, rounded to bf16 (RaMP section 3.3's block-scaled FP8).
 //
-// Configurations (BLOCK_M x BLOCK_N per workgroup; waves M x N x K-split):
-//   small tiles stream weights straight from HBM into registers with a multi-step
-//   software prefetch; waves that split K inside a tile are summed through LDS in a
-//   fixed order, so results are deterministic.
+// Math.  v_mfma_f32_16x16x32_bf16 for bf16 operands (fp8 weights decoded to
+// bf16), v_mfma_f32_16x16x4_f32 for the fp32 problem; fp32 accumulation.  Waves
+// are arranged WM x WN x WK over the tile; waves that split K inside a tile add
+// their partial sums through LDS in a fixed order, so results are deterministic.
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// operand fragments: 8 consecutive k of one row, per lane
+// element types
 // ---------------------------------------------------------------------------
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+
+template <int WK_>
+struct Types;
+template <>
+struct Types<W_F32> {
+  using Act = float;
+  using Wt = float;
+  static constexpr int asz = 4, wsz = 4;
+};
+template <>
+struct Types<W_BF16> {
+  using Act = uint16_t;
+  using Wt = uint16_t;
+  static constexpr int asz = 2, wsz = 2;
+};
+template <>
+struct Types<W_FP8> {
+  using Act = uint16_t;
+  using Wt = uint8_t;
+  static constexpr int asz = 2, wsz = 1;
+};
+
+// MFMA operand fragment: 8 consecutive k of one row per lane
 template <bool F32>
 struct Frag;
 template <>
@@ -51,16 +82,6 @@ template <>
 struct Frag<true> {
   f32x4 lo, hi;
 };
-
-__device__ __forceinline__ void zero_frag(Frag<false>& f) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  f.v = __builtin_bit_cast(bf16x8, z);
-}
-__device__ __forceinline__ void zero_frag(Frag<true>& f) {
-  f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  f.lo = z;
-  f.hi = z;
-}
 
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<false>& a, const Frag<false>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
@@ -74,67 +95,35 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<true>& a, const Frag<
   for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[c], b.hi[c], acc, 0, 0, 0);
 }
 
-// 16-byte / 32-byte loads of 8 elements starting at p (element index already applied)
-__device__ __forceinline__ void load_frag(Frag<false>& f, const uint16_t* p) {
-  f.v = __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-}
-__device__ __forceinline__ void load_frag(Frag<true>& f, const float* p) {
-  f.lo = *(const f32x4*)p;
-  f.hi = *(const f32x4*)(p + 4);
+// LDS row swizzle in 16-byte units: lanes reading one 16-byte column of 16
+// consecutive rows land on distinct bank groups for 32- and 64-bank LDS.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
-// fp8 E4M3FN x8 (8 bytes) * scale -> bf16 x8
-__device__ __forceinline__ void fp8_to_frag(Frag<false>& f, u32x2 q, float s) {
-  u32x4 o;
+// 16 fp8 E4M3FN codes times one scale -> 16 bf16 (two 16-byte LDS chunks)
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& q, float s, u32x4& o0, u32x4& o1) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(q[h], false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(q[h], true);
-    o[2 * h] = pack_bf16x2(a[0] * s, a[1] * s);
-    o[2 * h + 1] = pack_bf16x2(b[0] * s, b[1] * s);
-  }
-  f.v = __builtin_bit_cast(bf16x8, o);
-}
-
-// ---------------------------------------------------------------------------
-// element types per problem
-// ---------------------------------------------------------------------------
-enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
-
-template <int WK_>
-struct Types;
-template <>
-struct Types<W_F32> {
-  using Act = float;
-  using Wt = float;
-  static constexpr bool F32 = true;
-};
-template <>
-struct Types<W_BF16> {
-  using Act = uint16_t;
-  using Wt = uint16_t;
-  static constexpr bool F32 = false;
-};
-template <>
-struct Types<W_FP8> {
-  using Act = uint16_t;
-  using Wt = uint8_t;
-  static constexpr bool F32 = false;
-};
-
-// load 8 weights of row `row` (of a [rows][K] matrix), k offset kk, for expert
-// matrix base w; fp8 applies the block scale of (row/128, kk/128)
-// (sidx is wave-uniform: all 64 lanes of a fragment fall in one 128x128 block)
-template <int WKIND>
-__device__ __forceinline__ void load_w(Frag<Types<WKIND>::F32>& f, const typename Types<WKIND>::Wt* w,
-                                       int64_t row, int K, int kk, const float* sc, int64_t sidx) {
-  if constexpr (WKIND == W_FP8) {
-    const u32x2 q = *(const u32x2*)(w + row * K + kk);
-    fp8_to_frag(f, q, sc[sidx]);
-  } else {
-    load_frag(f, w + row * K + kk);
+  for (int w = 0; w < 4; ++w) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(q[w], false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(q[w], true);
+    const uint32_t p0 = pack2_bf16(a[0] * s, a[1] * s);
+    const uint32_t p1 = pack2_bf16(b[0] * s, b[1] * s);
+    if (w < 2) {
+      o0[2 * w] = p0;
+      o0[2 * w + 1] = p1;
+    } else {
+      o1[2 * (w - 2)] = p0;
+      o1[2 * (w - 2) + 1] = p1;
+    }
   }
 }
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 template <typename T>
 __device__ __forceinline__ void store_out(T* p, float v);
@@ -144,13 +133,11 @@ __device__ __forceinline__ void store_out<float>(float* p, float v) {
 }
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
-  *p = f32_to_bf16_bits(v);
+  *p = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
 // ---------------------------------------------------------------------------
-// kernel arguments
+// kernel arguments and the tile queue
 // ---------------------------------------------------------------------------
 struct FfnArgs {
   const void* x;   // [B][H] act
@@ -164,154 +151,264 @@ struct FfnArgs {
   const int32_t* block_expert;
   const int32_t* num_blocks;
   const int32_t* variant;
-  void* h;        // [rows_max][I] act
-  void* y_slots;  // [rows_max][H] act
+  void* h;         // [rows_max][I] act
+  void* y_slots;   // [rows_max][H] act
   int H, I, k;
   int E_loc;
-  int slots;      // B * k
+  int slots;  // B * k
   int64_t rows_max;
 };
 
-__device__ __forceinline__ int xcd_tile_slot(int wg, int grid) {
-  // consecutive slots on one XCD: the hardware places workgroup wg on XCD wg % 8
-  const int per = grid >> 3;
-  if (per == 0 || (grid & 7)) return wg;
-  return (wg & 7) * per + (wg >> 3);
+// slot of workgroup wg so that consecutive slots share an XCD (workgroup wg runs
+// on XCD wg % 8)
+__device__ __forceinline__ int xcd_slot(int wg, int grid) {
+  if (grid & 7) return wg;
+  return (wg & 7) * (grid >> 3) + (wg >> 3);
 }
 
 // ---------------------------------------------------------------------------
-// one tile configuration, one phase
+// one tile configuration of one phase
+//   BM x BN tile (BN weight rows per matrix; the gate/up phase has two matrices),
+//   ROWB = LDS bytes per tile row per stage, waves WM x WN x WK, RS register
+//   stages in flight.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int WKS, int PF, int PHASE, int WKIND>
-struct TileRunner {
+template <int BM, int BN, int WM, int WN, int WK, int ROWB, int RS, int PHASE, int WKIND>
+struct Tile {
   using T = Types<WKIND>;
   using Act = typename T::Act;
   using Wt = typename T::Wt;
-  static constexpr bool F32 = T::F32;
-  static constexpr int MW = BM / WM;
-  static constexpr int NW = BN / WN;
-  static constexpr int FM = MW / 16;
-  static constexpr int FN = NW / 16;
-  static constexpr int NMAT = PHASE == 1 ? 2 : 1;  // gate and up share the A rows
-  static constexpr int NB = PF + 1;                // register ring of k-steps
-  static_assert(WM * WN * WKS == 4, "4 waves per workgroup");
-  static_assert(FM >= 1 && FN >= 1, "tile too small for the wave layout");
+  static constexpr bool F32 = WKIND == W_F32;
+  static constexpr bool FP8 = WKIND == W_FP8;
+  static constexpr int ASZ = T::asz, WSZ = T::wsz;
+  static constexpr int NMAT = PHASE == 1 ? 2 : 1;
+  static constexpr int BK = ROWB / ASZ;  // reduction elements per stage
+  static constexpr int C = ROWB / 16;    // 16-byte LDS chunks per row
+  static constexpr int ROWS = BM + NMAT * BN;
+  static constexpr int STAGE = ROWS * ROWB;  // LDS bytes per stage
+  static constexpr int EPC_A = 16 / ASZ;     // elements per global A chunk
+  static constexpr int EPC_B = 16 / WSZ;     // elements per global weight chunk
+  static constexpr int GCA = BK / EPC_A;     // global chunks per A row per stage
+  static constexpr int GCB = BK / EPC_B;     // global chunks per weight row per stage
+  static constexpr int GA = BM * GCA;
+  static constexpr int GB = NMAT * BN * GCB;
+  static constexpr int NA = (GA + kThreads - 1) / kThreads;
+  static constexpr int NB = (GB + kThreads - 1) / kThreads;
+  static constexpr int MW = BM / WM, NW = BN / WN;
+  static constexpr int FM = MW / 16, FN = NW / 16;
+  static constexpr int KSTEPS = BK / 32;
+  static constexpr int RED_FLOATS = (WK > 1) ? (WK - 1) * WM * WN * NMAT * FM * FN * 4 * 64 : 0;
+  static constexpr int LDS_BYTES =
+      (2 * STAGE > RED_FLOATS * 4 ? 2 * STAGE : RED_FLOATS * 4);
+  static_assert(WM * WN * WK * 64 == kThreads, "waves must cover the workgroup");
+  static_assert(FM >= 1 && FN >= 1 && MW % 16 == 0 && NW % 16 == 0, "wave tile too small");
+  static_assert(C >= 8 && (C & (C - 1)) == 0, "LDS rows must be a power of two of >= 128 bytes");
+  static_assert(KSTEPS % WK == 0, "K-split waves must divide the stage");
+  static_assert(!FP8 || GCB * 2 == C, "fp8 chunk pairs");
 
-  // LDS floats needed for the in-tile K-split reduction
-  static constexpr int kLdsFloats = (WKS > 1) ? (WKS - 1) * WM * WN * NMAT * FM * FN * 4 * 64 : 0;
-
-  struct Step {
-    Frag<F32> a[FM];
-    Frag<F32> b[NMAT][FN];
+  struct Regs {
+    u32x4 a[NA];
+    u32x4 b[NB];
+    float s[FP8 ? NB : 1];
   };
 
-  __device__ static void run(const FfnArgs& g, float* lds, int nblocks) {
+  // Runs tile (rb, nt) of this phase.  `rowok` is an LDS array of BM ints.
+  __device__ static void run(const FfnArgs& g, uint8_t* lds, int* rowok, int rb, int nt) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
-    const int tiles_n = N / BN;
-    const int total = nblocks * tiles_n;
-    const int wave = threadIdx.x / 64;
-    const int lane = threadIdx.x & 63;
-    const int wk = wave % WKS;
-    const int wn = (wave / WKS) % WN;
-    const int wm = wave / (WKS * WN);
-    const int lr = lane & 15;         // row (A) / column (B) inside a 16-block
-    const int lk = (lane >> 4) * 8;   // k offset of this lane inside a 32-chunk
-    const int nks = K / 32;           // k-steps of 32
-    const int nsteps = nks > wk ? (nks - wk + WKS - 1) / WKS : 0;
-    const Wt* wmat0 = (const Wt*)(PHASE == 1 ? g.w1 : g.w2);
-    const Wt* wmat1 = (const Wt*)(PHASE == 1 ? g.w3 : g.w2);
-    const float* smat0 = PHASE == 1 ? g.s1 : g.s2;
-    const float* smat1 = PHASE == 1 ? g.s3 : g.s2;
-    const int Kb = K / 128;  // scale blocks along K
-    const int Nb = N / 128;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wk = wave % WK;
+    const int wn = (wave / WK) % WN;
+    const int wm = wave / (WK * WN);
+    const int e = g.block_expert[rb];
+    const int64_t row0 = (int64_t)rb * BM;
+    const int n0 = nt * BN;
+    const int nst = (K + BK - 1) / BK;
 
-    for (int tile = xcd_tile_slot(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
-      const int rb = tile % nblocks;  // row-block (fastest: reuse of one weight panel)
-      const int nt = tile / nblocks;
-      const int e = g.block_expert[rb];
-      if ((unsigned)e >= (unsigned)g.E_loc) continue;  // uniform: whole workgroup skips
-      const int64_t row0 = (int64_t)rb * BM;
-      const int n0 = nt * BN + wn * NW;
+    // an expert index outside the local block cannot come from moe_align_sort;
+    // the whole workgroup skips such a tile rather than address beyond the weights
+    if ((unsigned)e >= (unsigned)g.E_loc) return;
 
-      // A rows of this lane: token rows (phase 1, gathered) or h rows (phase 2)
-      const Act* arow[FM];
-      bool avalid[FM];
+    // rows of this tile that hold a routed slot (others are padding); the barrier
+    // before it keeps the previous tile's epilogue reads of rowok apart
+    __syncthreads();
+    for (int r = tid; r < BM; r += kThreads) rowok[r] = g.sorted_slots[row0 + r];
+    __syncthreads();
+
+    // ---- per-thread chunk assignment ----
+    // chunk q = i * kThreads + tid of a stage: A chunk q is column q % GCA of tile
+    // row q / GCA; weight chunk q is column q % GCB of weight row (q / GCB) % BN of
+    // matrix q / (BN * GCB).  Row sources are 32-bit element offsets (the host
+    // keeps every operand below 2^31 elements); -1 marks a padding row.
+    int a_off[NA];
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int64_t r = row0 + wm * MW + fm * 16 + lr;
-        if (PHASE == 1) {
-          const int s = g.sorted_slots[r];
-          avalid[fm] = s >= 0 && s < g.slots;  // anything else is a padding row
-          arow[fm] = (const Act*)g.x + (int64_t)(s >= 0 ? s / g.k : 0) * K;
-        } else {
-          avalid[fm] = true;
-          arow[fm] = (const Act*)g.h + r * K;
+    for (int i = 0; i < NA; ++i) {
+      const int q = i * kThreads + tid;
+      a_off[i] = -1;
+      if (q < GA) {
+        const int row = q / GCA, c = q % GCA;
+        const int s = rowok[row];
+        if (s >= 0 && s < g.slots) {
+          const int64_t arow = PHASE == 1 ? (int64_t)(s / g.k) : row0 + row;
+          a_off[i] = (int)(arow * K) + c * EPC_A;
         }
       }
-      // B rows of this lane: weight rows n of expert e
-      int64_t brow[FN];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) brow[fn] = (int64_t)e * N + n0 + fn * 16 + lr;
-      // fp8 scale index base per fragment (all 64 lanes share one 128x128 block)
-      int64_t sbase[FN];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) sbase[fn] = ((int64_t)e * Nb + (n0 + fn * 16) / 128) * Kb;
+    }
+    const Act* abase = (const Act*)(PHASE == 1 ? g.x : g.h);
+    const Wt* wmat0 = (const Wt*)(PHASE == 1 ? g.w1 : g.w2);
+    const Wt* wmat1 = (const Wt*)(PHASE == 1 ? g.w3 : g.w2);
+    const int64_t wrow0 = (int64_t)e * N + n0;  // first weight row of the tile
+    const float* smat0 = PHASE == 1 ? g.s1 : g.s2;
+    const float* smat1 = PHASE == 1 ? g.s3 : g.s2;
 
-      f32x4 acc[NMAT][FM][FN];
+    auto load_stage = [&](Regs& R, int s) {
+      const int k0 = s * BK;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+      for (int i = 0; i < NA; ++i) {
+        const int q = i * kThreads + tid;
+        const int kel = (q % GCA) * EPC_A;
+        if (a_off[i] >= 0 && k0 + kel < K)
+          R.a[i] = *(const u32x4*)(abase + a_off[i] + k0);
+        else
+          R.a[i] = u32x4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < NB; ++i) {
+        const int q = i * kThreads + tid;
+        const int m = q / (BN * GCB);
+        const int row = (q / GCB) % BN;
+        const int kel = (q % GCB) * EPC_B;
+        if (q < GB && k0 + kel < K) {
+          const Wt* wm_ = m == 0 ? wmat0 : wmat1;
+          R.b[i] = *(const u32x4*)(wm_ + (wrow0 + row) * K + k0 + kel);
+          if constexpr (FP8) {
+            const float* sm = m == 0 ? smat0 : smat1;
+            R.s[i] = sm[((int64_t)e * (N / 128) + (n0 + row) / 128) * (K / 128) + (k0 + kel) / 128];
+          }
+        } else {
+          R.b[i] = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (FP8) R.s[i] = 0.f;
+        }
+      }
+    };
+    auto write_stage = [&](const Regs& R, uint8_t* buf) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NA; ++i) {
+        const int q = i * kThreads + tid;
+        if (q < GA) {
+          const int row = q / GCA, c = q % GCA;
+          *(u32x4*)(buf + row * ROWB + ((c ^ swz(row)) << 4)) = R.a[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int q = i * kThreads + tid;
+        if (q < GB) {
+          const int row = BM + q / GCB;  // LDS row: matrices follow each other
+          const int c = q % GCB;
+          const int sw = swz(row);
+          uint8_t* rp = buf + row * ROWB;
+          if constexpr (FP8) {
+            u32x4 o0, o1;
+            fp8x16_to_bf16(R.b[i], R.s[i], o0, o1);
+            *(u32x4*)(rp + (((2 * c) ^ sw) << 4)) = o0;
+            *(u32x4*)(rp + (((2 * c + 1) ^ sw) << 4)) = o1;
+          } else {
+            *(u32x4*)(rp + ((c ^ sw) << 4)) = R.b[i];
+          }
+        }
+      }
+    };
 
-      Step buf[NB];
-      auto load_step = [&](Step& st, int step) {
-        const int kk0 = (wk + step * WKS) * 32;  // wave-uniform
-        const int kk = kk0 + lk;
+    // ---- accumulators ----
+    f32x4 acc[NMAT][FM][FN];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          if (avalid[fm])
-            load_frag(st.a[fm], arow[fm] + kk);
-          else
-            zero_frag(st.a[fm]);
-        }
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          load_w<WKIND>(st.b[0][fn], wmat0, brow[fn], K, kk, smat0, sbase[fn] + kk0 / 128);
-          if (NMAT == 2)
-            load_w<WKIND>(st.b[NMAT - 1][fn], wmat1, brow[fn], K, kk, smat1, sbase[fn] + kk0 / 128);
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int lr = lane & 15;   // row of the fragment
+    const int lg = lane >> 4;   // k-group of 8 inside a 32-step
+    auto read_frag = [&](const uint8_t* buf, int row, int step, Frag<F32>& f) {
+      const uint8_t* rp = buf + row * ROWB;
+      const int sw = swz(row);
+      if constexpr (F32) {
+        const int c0 = step * 8 + 2 * lg;
+        f.lo = *(const f32x4*)(rp + ((c0 ^ sw) << 4));
+        f.hi = *(const f32x4*)(rp + (((c0 + 1) ^ sw) << 4));
+      } else {
+        const int c0 = step * 4 + lg;
+        f.v = __builtin_bit_cast(bf16x8, *(const u32x4*)(rp + ((c0 ^ sw) << 4)));
+      }
+    };
+    auto compute_stage = [&](const uint8_t* buf, int s) {
+      const int k0 = s * BK;
+#pragma unroll
+      for (int jj = 0; jj < KSTEPS / WK; ++jj) {
+        const int step = jj * WK + wk;
+        if (k0 + step * 32 < K) {
+          Frag<F32> fa[FM];
+          Frag<F32> fb[NMAT][FN];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) read_frag(buf, BM + m * BN + wn * NW + j * 16 + lr, step, fb[m][j]);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) mma(acc[m][i][j], fa[i], fb[m][j]);
         }
-      };
-      auto compute_step = [&](const Step& st) {
+      }
+    };
+
+    // ---- pipeline: RS register stages ahead, two LDS buffers ----
+    Regs R[RS];
+#pragma unroll
+    for (int u = 0; u < RS; ++u)
+      if (u < nst) load_stage(R[u], u);
+    for (int s0 = 0; s0 < nst; s0 += RS) {
+#pragma unroll
+      for (int u = 0; u < RS; ++u) {
+        const int s = s0 + u;
+        if (s < nst) {
+          uint8_t* buf = lds + (s & 1) * STAGE;
+          write_stage(R[u], buf);
+          if (s + RS < nst) load_stage(R[u], s + RS);
+          __syncthreads();
+          compute_stage(buf, s);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done reading the stage buffers
+
+    // ---- in-tile K split: waves wk > 0 hand their sums to wave wk = 0 ----
+    if constexpr (WK > 1) {
+      float* red = (float*)lds;
+      constexpr int PER = NMAT * FM * FN * 4 * 64;
+      const int slot = (wm * WN + wn) * (WK - 1);
+      if (wk > 0) {
+        float* dst = red + (slot + wk - 1) * PER;
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) mma(acc[m][i][j], st.a[i], st.b[m][j]);
-      };
-
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int u = 0; u < PF; ++u)
-        if (u < nsteps) load_step(buf[u], u);
-      for (int base = 0; base < nsteps; base += NB) {
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          const int step = base + u;
-          if (step < nsteps) {
-            if (step + PF < nsteps) load_step(buf[(u + PF) % NB], step + PF);
-            compute_step(buf[u]);
-          }
-        }
+              for (int c = 0; c < 4; ++c) dst[(((m * FM + i) * FN + j) * 4 + c) * 64 + lane] = acc[m][i][j][c];
       }
-
-      // in-tile K-split: waves wk > 0 hand their partial sums to wave wk = 0
-      if constexpr (WKS > 1) {
-        const int slot_base = ((wm * WN + wn) * (WKS - 1)) * NMAT * FM * FN * 4 * 64;
-        if (wk > 0) {
-          float* dst = lds + slot_base + (wk - 1) * NMAT * FM * FN * 4 * 64;
+      __syncthreads();
+      if (wk == 0) {
+#pragma unroll
+        for (int q = 0; q < WK - 1; ++q) {
+          const float* src = red + (slot + q) * PER;
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -319,108 +416,124 @@ struct TileRunner {
 #pragma unroll
               for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                  dst[(((m * FM + i) * FN + j) * 4 + c) * 64 + lane] = acc[m][i][j][c];
+                for (int c = 0; c < 4; ++c) acc[m][i][j][c] += src[(((m * FM + i) * FN + j) * 4 + c) * 64 + lane];
         }
-        __syncthreads();
-        if (wk == 0) {
-#pragma unroll
-          for (int q = 0; q < WKS - 1; ++q) {
-            const float* src = lds + slot_base + q * NMAT * FM * FN * 4 * 64;
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-              for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                  for (int c = 0; c < 4; ++c)
-                    acc[m][i][j][c] += src[(((m * FM + i) * FN + j) * 4 + c) * 64 + lane];
-          }
-        }
-        __syncthreads();
-        if (wk != 0) continue;
       }
+      __syncthreads();  // the reduction area is free again
+    }
 
-      // epilogue: lane holds rows 4*(lane/16)+c, column lane%16 of each 16x16 block
+    // ---- epilogue: lane holds rows 4*(lane/16)+c, column lane%16 of each block ----
+    if (wk == 0) {
       Act* out = (Act*)(PHASE == 1 ? g.h : g.y_slots);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int c = 0; c < 4; ++c) {
+          const int r = wm * MW + i * 16 + (lane >> 4) * 4 + c;
+          if (rowok[r] < 0) continue;
+          Act* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int64_t r = row0 + wm * MW + i * 16 + (lane >> 4) * 4 + c;
-            const int n = n0 + j * 16 + lr;
-            float v;
-            if (PHASE == 1)
-              v = silu_mul(acc[0][i][j][c], acc[NMAT - 1][i][j][c]);
-            else
-              v = acc[0][i][j][c];
-            store_out<Act>(out + r * N + n, v);
+          for (int j = 0; j < FN; ++j) {
+            const float v = PHASE == 1 ? silu_mul(acc[0][i][j][c], acc[NMAT - 1][i][j][c]) : acc[0][i][j][c];
+            store_out<Act>(orow + j * 16, v);
           }
+        }
     }
   }
 };
 
+// ---------------------------------------------------------------------------
 // configuration table: must match kVariants in moe_common.h
+//   Cfg<V, PHASE, WKIND>::R is the tile runner of configuration V in that phase.
+// ---------------------------------------------------------------------------
 template <int V, int PHASE, int WKIND>
 struct Cfg;
-#define MOE_CFG(V, BM, BN1, BN2, WM, WN, WKS, PF)                                           \
-  template <int PHASE, int WKIND>                                                         \
-  struct Cfg<V, PHASE, WKIND> {                                                           \
-    using R = TileRunner<BM, (PHASE == 1 ? BN1 : BN2), WM, WN, WKS, PF, PHASE, WKIND>;    \
-  };                                                                                      \
+#define MOE_CFG(V, BM, BN1, BN2, ROWB, WM, WN, WK, RS)                                          \
+  template <int PHASE, int WKIND>                                                             \
+  struct Cfg<V, PHASE, WKIND> {                                                               \
+    static constexpr int BN = PHASE == 1 ? BN1 : BN2;                                         \
+    using R = Tile<BM, BN, WM, WN, WK, ROWB, RS, PHASE, WKIND>;                                \
+  };                                                                                          \
   static_assert(kVariants[V].bm == BM && kVariants[V].bn1 == BN1 && kVariants[V].bn2 == BN2 && \
-                    kVariants[V].wm == WM && kVariants[V].wn == WN && kVariants[V].wk == WKS &&  \
-                    kVariants[V].splitk == 1 && kVariants[V].bk == 32 * WKS,                    \
+                    kVariants[V].rowb == ROWB && kVariants[V].wm == WM &&                     \
+                    kVariants[V].wn == WN && kVariants[V].wk == WK && kVariants[V].splitk == 1, \
                 "kernel configuration table out of sync with kVariants");
-MOE_CFG(0, 16, 16, 16, 1, 1, 4, 3)
-MOE_CFG(1, 32, 32, 32, 1, 2, 2, 2)
-MOE_CFG(2, 64, 64, 64, 2, 2, 1, 1)
-MOE_CFG(3, 128, 64, 128, 2, 2, 1, 1)
+MOE_CFG(0, 16, 16, 16, 1024, 1, 1, 4, 1)
+MOE_CFG(1, 32, 32, 32, 512, 1, 2, 2, 1)
+MOE_CFG(2, 64, 64, 64, 256, 2, 2, 1, 1)
+MOE_CFG(3, 128, 128, 128, 128, 2, 2, 1, 1)
 #undef MOE_CFG
 
-template <int PHASE, int WKIND>
-constexpr int lds_floats() {
-  int m = 1;
-  m = Cfg<0, PHASE, WKIND>::R::kLdsFloats > m ? Cfg<0, PHASE, WKIND>::R::kLdsFloats : m;
-  m = Cfg<1, PHASE, WKIND>::R::kLdsFloats > m ? Cfg<1, PHASE, WKIND>::R::kLdsFloats : m;
-  m = Cfg<2, PHASE, WKIND>::R::kLdsFloats > m ? Cfg<2, PHASE, WKIND>::R::kLdsFloats : m;
-  m = Cfg<3, PHASE, WKIND>::R::kLdsFloats > m ? Cfg<3, PHASE, WKIND>::R::kLdsFloats : m;
+template <int WKIND>
+constexpr int lds_bytes() {
+  int m = 0;
+#define MOE_LDS(V)                                                                            \
+  m = Cfg<V, 1, WKIND>::R::LDS_BYTES > m ? Cfg<V, 1, WKIND>::R::LDS_BYTES : m;                \
+  m = Cfg<V, 2, WKIND>::R::LDS_BYTES > m ? Cfg<V, 2, WKIND>::R::LDS_BYTES : m;
+  MOE_LDS(0) MOE_LDS(1) MOE_LDS(2) MOE_LDS(3)
+#undef MOE_LDS
   return m;
 }
 
+// The tiles of configuration V in phase PHASE, dealt out statically.
+template <int V, int PHASE, int WKIND>
+__device__ void run_phase(const FfnArgs& g, uint8_t* lds, int* rowok, int nb) {
+  using R = typename Cfg<V, PHASE, WKIND>::R;
+  const int q = (PHASE == 1 ? g.I : g.H) / Cfg<V, PHASE, WKIND>::BN;
+  const int total = nb * q;
+  for (int t = xcd_slot(blockIdx.x, gridDim.x); t < total; t += gridDim.x) R::run(g, lds, rowok, t % nb, t / nb);
+}
+
 template <int PHASE, int WKIND>
-__global__ void __launch_bounds__(kThreads) ffn_phase_kernel(FfnArgs g) {
-  __shared__ float lds[lds_floats<PHASE, WKIND>()];
+__global__ void __launch_bounds__(kThreads) ffn_kernel(FfnArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int rowok[kMaxBlockM];
   const int v = *g.variant;
   int nb = *g.num_blocks;
-  if (nb <= 0 || v < 0 || v >= kNumVariants) return;
+  if (v < 0 || v >= kNumVariants || nb <= 0) return;  // no tiles (align_sort wrote none)
   // never address rows beyond the buffers, whatever the device state says
   const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
   nb = nb < nb_cap ? nb : nb_cap;
   switch (v) {
-    case 0: Cfg<0, PHASE, WKIND>::R::run(g, lds, nb); break;
-    case 1: Cfg<1, PHASE, WKIND>::R::run(g, lds, nb); break;
-    case 2: Cfg<2, PHASE, WKIND>::R::run(g, lds, nb); break;
-    case 3: Cfg<3, PHASE, WKIND>::R::run(g, lds, nb); break;
-    default: break;  // out-of-range index: align_sort already produced no rows
+    case 0: run_phase<0, PHASE, WKIND>(g, lds, rowok, nb); break;
+    case 1: run_phase<1, PHASE, WKIND>(g, lds, rowok, nb); break;
+    case 2: run_phase<2, PHASE, WKIND>(g, lds, rowok, nb); break;
+    case 3: run_phase<3, PHASE, WKIND>(g, lds, rowok, nb); break;
+    default: break;
   }
 }
 
-template <int WKIND>
-hipError_t launch_w(const FfnArgs& g, int grid1, int grid2, hipStream_t s) {
-  ffn_phase_kernel<1, WKIND><<<grid1, kThreads, 0, s>>>(g);
-  hipError_t e = hipGetLastError();
+template <int PHASE, int WKIND>
+hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
+  constexpr int lds = lds_bytes<WKIND>();
+  static_assert(lds <= 160 * 1024 - 1024, "LDS budget");
+  static int done[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  ffn_phase_kernel<2, WKIND><<<grid2, kThreads, 0, s>>>(g);
+  if (dev >= 0 && dev < 64 && !done[dev]) {
+    e = hipFuncSetAttribute((const void*)ffn_kernel<PHASE, WKIND>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    done[dev] = 1;
+  }
+  ffn_kernel<PHASE, WKIND><<<grid, kThreads, lds, s>>>(g);
   return hipGetLastError();
+}
+
+template <int WKIND>
+hipError_t launch_w(const FfnArgs& g, int phases, int grid, hipStream_t s) {
+  if (phases & 1) {
+    const hipError_t e = launch_phase<1, WKIND>(g, grid, s);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 2) return launch_phase<2, WKIND>(g, grid, s);
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_grouped_ffn(const moe_problem& p, const void* x, const void* w1,
+hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,
@@ -429,25 +542,11 @@ hipError_t launch_grouped_ffn(const moe_problem& p, const void* x, const void* w
   FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
             h, y_slots, p.hidden, p.inter, p.top_k, p.local_experts, p.tokens * p.top_k,
             rows_max};
-  // persistent grid: compute units x workgroups per unit, capped by the most tiles
-  // any configuration can produce for this problem
-  int64_t max_t1 = 0, max_t2 = 0;
-  for (int v = 0; v < kNumVariants; ++v) {
-    const int64_t rb = rows_max / kVariants[v].bm;
-    const int64_t t1 = rb * (p.inter / kVariants[v].bn1);
-    const int64_t t2 = rb * (p.hidden / kVariants[v].bn2);
-    max_t1 = t1 > max_t1 ? t1 : max_t1;
-    max_t2 = t2 > max_t2 ? t2 : max_t2;
-  }
-  int64_t g1 = (int64_t)num_cus * kWgPerCuPhase1, g2 = (int64_t)num_cus * kWgPerCuPhase2;
-  g1 = g1 < max_t1 ? g1 : max_t1;
-  g2 = g2 < max_t2 ? g2 : max_t2;
-  if (g1 < 1) g1 = 1;
-  if (g2 < 1) g2 = 1;
+  const int grid = num_cus * kWgPerCu;
   switch (p.weight_dtype) {
-    case MOE_F32: return launch_w<W_F32>(g, (int)g1, (int)g2, s);
-    case MOE_BF16: return launch_w<W_BF16>(g, (int)g1, (int)g2, s);
-    case MOE_FP8_E4M3: return launch_w<W_FP8>(g, (int)g1, (int)g2, s);
+    case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);
+    case MOE_BF16: return launch_w<W_BF16>(g, phases, grid, s);
+    case MOE_FP8_E4M3: return launch_w<W_FP8>(g, phases, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

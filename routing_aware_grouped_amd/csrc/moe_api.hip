@@ -39,6 +39,14 @@ moe_status validate(const moe_problem* p) {
   if (slots >= (1ll << 30)) return MOE_ERR_UNSUPPORTED;
   // the alignment step keeps its tables in one workgroup's LDS
   if (align_lds_bytes(p->tokens, p->local_experts) > kMaxLds - 512) return MOE_ERR_UNSUPPORTED;
+  // the grouped FFN addresses activation, h and y_slots rows with 32-bit element
+  // offsets
+  {
+    const int64_t rmax = slots + (int64_t)(slots < p->local_experts ? slots : p->local_experts) * (kMaxBlockM - 1);
+    const int64_t wide = p->hidden > p->inter ? p->hidden : p->inter;
+    if (rmax * wide >= (1ll << 31) || (int64_t)p->tokens * p->hidden >= (1ll << 31))
+      return MOE_ERR_UNSUPPORTED;
+  }
   // the cost model converts tile and wave counts to fp32 exactly (< 2^24)
   const int64_t rows = slots + (int64_t)(slots < p->local_experts ? slots : p->local_experts) * (kMaxBlockM - 1);
   for (int v = 0; v < kNumVariants; ++v) {
@@ -83,8 +91,8 @@ moe_status fill_cost_table(const moe_problem* p, CostTable* t) {
     t->b[v] = kVariants[v].bm;
     t->q1[v] = p->inter / kVariants[v].bn1;
     t->q2[v] = (p->hidden / kVariants[v].bn2) * kVariants[v].splitk;
-    t->S1[v] = cus * kWgPerCuPhase1;
-    t->S2[v] = cus * kWgPerCuPhase2;
+    t->S1[v] = cus * kWgPerCu;
+    t->S2[v] = cus * kWgPerCu;
   }
   return MOE_OK;
 }
@@ -95,7 +103,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
@@ -110,7 +118,7 @@ int32_t moe_num_variants(void) { return kNumVariants; }
 moe_status moe_variant_info(int32_t v, int32_t* out) {
   if (!out || v < 0 || v >= kNumVariants) return MOE_ERR_INVALID_ARG;
   const VariantDesc& d = kVariants[v];
-  const int32_t vals[MOE_VARIANT_FIELDS] = {d.bm, d.bn1, d.bn2, d.bk, d.wm, d.wn, d.wk, d.splitk};
+  const int32_t vals[MOE_VARIANT_FIELDS] = {d.bm, d.bn1, d.bn2, d.rowb / 2, d.wm, d.wn, d.wk, d.splitk};
   memcpy(out, vals, sizeof vals);
   return MOE_OK;
 }
@@ -165,22 +173,32 @@ moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const i
                                       num_blocks, slot_pos, (hipStream_t)stream));
 }
 
-moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
-                           const void* w2, const float* s1, const float* s3, const float* s2,
-                           const int32_t* sorted_slots, const int32_t* block_expert,
-                           const int32_t* num_blocks, const int32_t* variant, void* y_slots,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and enqueue of the grouped FFN entry points.  phases: 1 gate/up
+// (needs x, w1, w3, s1, s3), 2 down (needs w2, s2, y_slots), 3 both.
+moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, const void* w1,
+                              const void* w3, const void* w2, const float* s1, const float* s3,
+                              const float* s2, const int32_t* sorted_slots,
+                              const int32_t* block_expert, const int32_t* num_blocks,
+                              const int32_t* variant, void* y_slots, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   moe_status st = validate(p);
   if (st != MOE_OK) return st;
-  if (!x || !w1 || !w3 || !w2 || !sorted_slots || !block_expert || !num_blocks || !variant ||
-      !y_slots || !workspace)
-    return MOE_ERR_INVALID_ARG;
+  const bool up = phases & 1, down = phases & 2;
   const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
-  if (fp8 && (!s1 || !s3 || !s2)) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) ||
-      !aligned(y_slots, 16) || !aligned(workspace, 256))
+  if (!sorted_slots || !block_expert || !num_blocks || !variant || !workspace)
     return MOE_ERR_INVALID_ARG;
-  if (fp8 && (!aligned(s1, 4) || !aligned(s3, 4) || !aligned(s2, 4))) return MOE_ERR_INVALID_ARG;
+  if (up && (!x || !w1 || !w3 || (fp8 && (!s1 || !s3)))) return MOE_ERR_INVALID_ARG;
+  if (down && (!w2 || !y_slots || (fp8 && !s2))) return MOE_ERR_INVALID_ARG;
+  if (up && (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w3, 16) ||
+             (fp8 && (!aligned(s1, 4) || !aligned(s3, 4)))))
+    return MOE_ERR_INVALID_ARG;
+  if (down && (!aligned(w2, 16) || !aligned(y_slots, 16) || (fp8 && !aligned(s2, 4))))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
   moe_sizes sz;
   sizes_of(p, &sz);
   if ((int64_t)workspace_bytes < sz.workspace_bytes) return MOE_ERR_WORKSPACE;
@@ -188,9 +206,42 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, 
   const int cus = num_cus_current(&err);
   if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
   void* h = (char*)workspace + kWsHeader;
-  return hip_status(launch_grouped_ffn(*p, x, w1, w3, w2, fp8 ? s1 : nullptr, fp8 ? s3 : nullptr,
-                                       fp8 ? s2 : nullptr, sorted_slots, block_expert, num_blocks,
-                                       variant, y_slots, h, cus, sz.rows_max, (hipStream_t)stream));
+  return hip_status(launch_grouped_ffn(*p, phases, x, w1, w3, w2, fp8 ? s1 : nullptr,
+                                       fp8 ? s3 : nullptr, fp8 ? s2 : nullptr, sorted_slots,
+                                       block_expert, num_blocks, variant, y_slots, h, cus,
+                                       sz.rows_max, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
+                           const void* w2, const float* s1, const float* s3, const float* s2,
+                           const int32_t* sorted_slots, const int32_t* block_expert,
+                           const int32_t* num_blocks, const int32_t* variant, void* y_slots,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_ffn_phases(3, p, x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert,
+                            num_blocks, variant, y_slots, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_grouped_gate_up(const moe_problem* p, const void* x, const void* w1,
+                               const void* w3, const float* s1, const float* s3,
+                               const int32_t* sorted_slots, const int32_t* block_expert,
+                               const int32_t* num_blocks, const int32_t* variant, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return grouped_ffn_phases(1, p, x, w1, w3, nullptr, s1, s3, nullptr, sorted_slots,
+                            block_expert, num_blocks, variant, nullptr, workspace,
+                            workspace_bytes, stream);
+}
+
+moe_status moe_grouped_down(const moe_problem* p, const void* w2, const float* s2,
+                            const int32_t* sorted_slots, const int32_t* block_expert,
+                            const int32_t* num_blocks, const int32_t* variant, void* y_slots,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_ffn_phases(2, p, nullptr, nullptr, nullptr, w2, nullptr, nullptr, s2,
+                            sorted_slots, block_expert, num_blocks, variant, y_slots, workspace,
+                            workspace_bytes, stream);
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,

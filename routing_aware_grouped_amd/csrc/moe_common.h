@@ -35,33 +35,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---------------------------------------------------------------------------
 // Compiled tile configurations of the polymorphic grouped FFN.  All share one
-// workgroup size (256 threads = 4 waves) and one launch per phase, so they are
-// one occupancy class (RaMP 3.3: one shared-memory buffer and one register
-// count for every entry).
+// workgroup size (256 threads = 4 waves), one launch (both GEMM phases), one LDS
+// allocation and one register budget, so they are one occupancy class (RaMP,
+// section 3.3: one shared-memory buffer and one register count for every entry).
+//   bm    token rows per tile (b_c of RaMP Eq. 1)
+//   bn1   weight rows per tile of W1 and of W3 in the gate/up phase
+//   bn2   weight rows per tile of W2 in the down phase
+//   rowb  LDS bytes per tile row per pipeline stage (BLOCK_K = rowb / 2 for
+//         bf16 operands, rowb / 4 for fp32)
+//   wm, wn, wk  waves along M, along N, and splitting K inside a tile
+//   splitk      tiles splitting K of the down phase (1 = none)
 // ---------------------------------------------------------------------------
 struct VariantDesc {
-  int bm, bn1, bn2, bk, wm, wn, wk, splitk;
+  int bm, bn1, bn2, rowb, wm, wn, wk, splitk;
 };
 
 constexpr int kNumVariants = 4;
 constexpr int kThreads = 256;
 
-// BLOCK_M, BLOCK_N (gate/up), BLOCK_N (down), BLOCK_K, waves M x N x K, split-K
 constexpr VariantDesc kVariants[kNumVariants] = {
-    {16, 16, 16, 128, 1, 1, 4, 1},
-    {32, 32, 32, 64, 1, 2, 2, 1},
-    {64, 64, 64, 32, 2, 2, 1, 1},
-    {128, 64, 128, 32, 2, 2, 1, 1},
+    {16, 16, 16, 1024, 1, 1, 4, 1},
+    {32, 32, 32, 512, 1, 2, 2, 1},
+    {64, 64, 64, 256, 2, 2, 1, 1},
+    {128, 128, 128, 128, 2, 2, 1, 1},
 };
 
 constexpr int kMinBlockM = 16;
 constexpr int kMaxBlockM = 128;
 
-// workgroups per CU of each persistent phase launch (one occupancy class)
-constexpr int kWgPerCuPhase1 = 2;
-constexpr int kWgPerCuPhase2 = 2;
+// workgroups per CU of the persistent grouped-FFN launch
+constexpr int kWgPerCu = 1;
 
-// Device-side table of the row-tile sizes for the selection/alignment kernels.
+// Device-side table of the cost-model constants (RaMP Eq. 1) per configuration.
 struct CostTable {
   int32_t b[kNumVariants];
   int32_t q1[kNumVariants];
@@ -79,7 +84,8 @@ hipError_t launch_select_config(const moe_problem& p, const int32_t* counts, con
 hipError_t launch_align_sort(const moe_problem& p, const int32_t* ids, const int32_t* variant,
                              int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
                              int32_t* slot_pos, hipStream_t s);
-hipError_t launch_grouped_ffn(const moe_problem& p, const void* x, const void* w1,
+// phases: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both (two launches)
+hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,

@@ -11,8 +11,9 @@ import dataclasses
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_grouped_ffn,
-               moe_num_variants, moe_problem, moe_query_sizes, moe_route_topk, moe_select_config)
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_grouped_down,
+               moe_grouped_ffn, moe_grouped_gate_up, moe_num_variants, moe_problem,
+               moe_query_sizes, moe_route_topk, moe_select_config)
 
 _TORCH_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
@@ -92,6 +93,16 @@ def align(b: Buffers, stream=None):
 def ffn(b: Buffers, stream=None):
     moe_grouped_ffn(b.p, b.x, b.w1, b.w3, b.w2, b.s1, b.s3, b.s2, b.sorted_slots, b.block_expert,
                     b.num_blocks, b.variant, b.y_slots, b.workspace, None, stream)
+
+
+def gate_up(b: Buffers, stream=None):
+    moe_grouped_gate_up(b.p, b.x, b.w1, b.w3, b.s1, b.s3, b.sorted_slots, b.block_expert,
+                        b.num_blocks, b.variant, b.workspace, None, stream)
+
+
+def down(b: Buffers, stream=None):
+    moe_grouped_down(b.p, b.w2, b.s2, b.sorted_slots, b.block_expert, b.num_blocks, b.variant,
+                     b.y_slots, b.workspace, None, stream)
 
 
 def combine(b: Buffers, stream=None):

@@ -34,7 +34,7 @@ def test_binding_mirrors_names():
 
 
 def test_variant_menu_matches_spec():
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     assert moe.moe_num_variants() == len(spec.MENU)
     for v, m in enumerate(spec.MENU):
         assert tuple(moe.moe_variant_info(v)) == m
@@ -115,6 +115,18 @@ def test_compute_calls_validate_before_any_gpu_work():
     pf = _p(act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3)
     with pytest.raises(moe.MoeError) as ei:  # fp8 weights need their scales
         moe.moe_grouped_ffn(pf, a, a, a, a, None, None, None, a, a, a, a, a, a, 1 << 30, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # the gate/up phase needs x
+        moe.moe_grouped_gate_up(p, None, a, a, None, None, a, a, a, a, a, 1 << 30, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # the down phase needs y_slots
+        moe.moe_grouped_down(p, a, None, a, a, a, a, None, a, 1 << 30, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # workspace one byte short
+        moe.moe_grouped_down(p, a, None, a, a, a, a, a, a, sz.workspace_bytes - 1, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as ei:  # fp8 down needs its scales
+        moe.moe_grouped_down(pf, a, None, a, a, a, a, a, a, 1 << 30, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_query_sizes(None)

@@ -260,3 +260,21 @@ def test_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(b.y.view(torch.int16), eager.view(torch.int16)), r
+
+
+def test_split_phases_match_ffn():
+    """moe_grouped_gate_up then moe_grouped_down give the same y_slots, bit for bit,
+    as moe_grouped_ffn (they enqueue the same two launches)."""
+    wdev, whost = G.weights("qwen3")
+    layer = synth.make_layer("qwen3", 77, 0.3, 4, weights=whost)
+    for v in range(V):
+        b = G.run(layer, variant=v, wdev=wdev)
+        nb = int(b.num_blocks.item())
+        R = nb * spec.MENU[v][0]
+        rows = b.sorted_slots[:R] >= 0
+        ref = b.y_slots[:R][rows].clone()
+        b.y_slots.zero_()
+        L.gate_up(b)
+        L.down(b)
+        torch.cuda.synchronize()
+        assert torch.equal(b.y_slots[:R][rows].view(torch.int16), ref.view(torch.int16)), v
