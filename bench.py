@@ -4,23 +4,40 @@
 Metric: fused-MoE layer microseconds, and the fraction of the HBM or bf16 MFMA
 roofline, over token counts x Dirichlet(alpha) routing skew.
 
-One step = one pass of the whole layer (route/top-k + histogram, on-GPU
-configuration choice, align/sort, grouped gate/up + SwiGLU, grouped down,
-combine) over one synthetic batch, replayed from a HIP graph with the inputs
-resident in HBM and the caches cold (a 1 GiB scratch write evicts L2 and the
-Infinity Cache before every timed replay; the write is outside the timed events).
+One step = one pass of the whole layer over one synthetic batch:
+- route/top-k + histogram;
+- on-GPU configuration choice;
+- align/sort;
+- grouped gate/up + SwiGLU;
+- grouped down;
+- combine.
+
+It is replayed from a HIP graph with the inputs resident in HBM and the caches
+cold. Before every timed replay a 1 GiB scratch write evicts L2 and the Infinity
+Cache; the write is outside the timed events.
 
 The headline point is the Mixtral-8x7B-shaped layer (H 4096, I 14336, 8 experts,
-top-2, bf16) at 128 tokens, alpha = 1.  The same run sweeps tokens
-{1, 16, 128, 512, 2048} x alpha {0.1, 1, 10, 100}, times every compiled tile
-configuration on each point (exhaustive search) and reports the gap of the
-on-GPU choice.  Work accounting follows GC-MoE's conventions: FLOPs = 6 * routed
-slots * H * I; algorithmic bytes = the distinct active experts' weights (+ fp8
-scales) counted once, plus activation rows read and outputs written.
+top-2, bf16) at 128 tokens, alpha = 1.
+
+The same run sweeps the four full-size workloads over their token counts and
+alphas:
+- Mixtral-shaped;
+- Qwen3-30B-A3B-shaped;
+- the DeepSeek-V3 one-GPU expert share;
+- the Kimi-K2 one-GPU expert share.
+
+On every sweep point it times each compiled tile configuration (exhaustive
+search) and reports the gap of the on-GPU choice.
+
+Work accounting follows GC-MoE's conventions:
+- FLOPs = 6 * routed slots * H * I;
+- algorithmic bytes = the distinct active experts' weights (+ fp8 scales), counted
+  once, plus the activation rows read and the outputs written.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,6 +51,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5166e15  # flop/s, dense bf16 MFMA (256 CU x 2.4 GHz x 4096)
 METRIC = "fused-MoE layer µs + % of HBM/MFMA roofline vs tokens × Dirichlet α skew"
+KERNEL_SOURCES = ["routing_aware_grouped_amd/csrc/grouped_ffn.hip",
+                  "routing_aware_grouped_amd/csrc/moe_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 SWEEPS = {
     "mixtral": dict(tokens=[1, 16, 128, 512, 2048], alphas=[0.1, 1.0, 10.0, 100.0]),
@@ -49,27 +69,54 @@ def log(msg):
 
 # ------------------------------------------------------------------ accounting --
 def work(layer, ids_np):
-    """Algorithmic FLOPs and bytes of one layer invocation on this load."""
+    """Algorithmic FLOPs and bytes of one layer invocation on this load, and of its
+    gate/up kernel alone (h and y_slots are intermediates, not counted)."""
+    import numpy as np
+    import synth
     sh = layer.shape
     H, I, k, El, e0 = sh.hidden, sh.inter, sh.top_k, sh.local_experts, layer.expert_begin
     B = layer.tokens
     loc = (ids_np >= e0) & (ids_np < e0 + El)
     S = int(loc.sum())
-    cnt = __import__("numpy").bincount((ids_np[loc] - e0).ravel(), minlength=El)
+    cnt = np.bincount((ids_np[loc] - e0).ravel(), minlength=El)
     A = int((cnt > 0).sum())
     U = int(loc.any(axis=1).sum())
-    wb = 1 if sh.weight_dtype == 2 else 2
-    scale_b = 3 * (H // 128) * (I // 128) * 4 if sh.weight_dtype == 2 else 0
-    wbytes = A * (3 * H * I * wb + scale_b)
-    ffn_bytes = wbytes + U * H * 2 + S * H * 2      # weights + gathered x rows + slot outputs
-    layer_bytes = wbytes + U * H * 2 + B * H * 2 + B * sh.num_experts * 4 + B * k * 8
-    flops = 6 * S * H * I
-    return dict(S=S, A=A, U=U, flops=flops, ffn_bytes=ffn_bytes, layer_bytes=layer_bytes,
-                eff_exp=__import__("synth").eff_exp(cnt), counts=cnt)
+    wb = 1 if sh.weight_dtype == synth.FP8 else (4 if sh.weight_dtype == synth.F32 else 2)
+    ab = 4 if sh.act_dtype == synth.F32 else 2
+    mat_scale = (H // 128) * (I // 128) * 4 if sh.weight_dtype == synth.FP8 else 0
+    wbytes = A * (3 * H * I * wb + 3 * mat_scale)
+    layer_bytes = wbytes + U * H * ab + B * H * ab + B * sh.num_experts * 4 + B * k * 8
+    gate_up_bytes = A * (2 * H * I * wb + 2 * mat_scale) + U * H * ab
+    return dict(S=S, A=A, U=U, flops=6 * S * H * I, layer_bytes=layer_bytes,
+                gate_up_bytes=gate_up_bytes, gate_up_flops=4 * S * H * I,
+                eff_exp=synth.eff_exp(cnt), counts=cnt)
 
 
 def roof_us(w):
     return max(w["layer_bytes"] / HBM_PEAK, w["flops"] / MFMA_BF16_PEAK) * 1e6
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    ent = d.get("workloads", {}).get(workload_key)
+    if not ent:
+        return None
+    return int(ent["fetch_kib"] * 1024 * d["fetch_factor"] + ent["write_kib"] * 1024 * d["write_factor"])
 
 
 # ---------------------------------------------------------------------- timing --
@@ -128,23 +175,27 @@ def load_theta(shape_name, V):
             d = json.load(f)
         th = torch.tensor(d["theta"], dtype=torch.float32)
         if th.shape == (V, 4):
-            return th, path
+            return th, os.path.relpath(path, ROOT)
     # no fitted table: predict time by waves alone (th1 = 1)
     th = torch.zeros(V, 4, dtype=torch.float32)
     th[:, 1] = 1.0
     return th, None
 
 
-# ----------------------------------------------------------------------- main --
+# ----------------------------------------------------------------------- points --
+def device_weights(wdev):
+    return (wdev["w1"], wdev["w3"], wdev["w2"], wdev["s1"], wdev["s3"], wdev["s2"])
+
+
 def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, V, reps, warmup,
               exhaustive=True, rep=0):
     layer = synth.make_layer(shape, tokens, alpha, rep, weights=whost)
-    wts = (wdev["w1"], wdev["w3"], wdev["w2"], wdev["s1"], wdev["s3"], wdev["s2"])
-    b = L.from_layer(layer, theta=theta, weights=wts)
+    b = L.from_layer(layer, theta=theta, weights=device_weights(wdev))
     L.forward(b)
     torch.cuda.synchronize()
     ids = b.topk_ids.cpu().numpy()
     chosen = int(b.variant.item())
+    t_hat = b.t_hat.cpu().numpy().tolist()
     w = work(layer, ids)
     g_chosen = T.graph(lambda: L.forward(b))
     t_chosen = stats(T.time_graph(g_chosen, reps, warmup))
@@ -153,7 +204,8 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
                us_p10=round(t_chosen["p10"], 3), us_p90=round(t_chosen["p90"], 3),
                roof_us=round(roof_us(w), 3),
                hbm_frac=round(w["layer_bytes"] / (t_chosen["median"] * 1e-6) / HBM_PEAK, 4),
-               mfma_frac=round(w["flops"] / (t_chosen["median"] * 1e-6) / MFMA_BF16_PEAK, 4))
+               mfma_frac=round(w["flops"] / (t_chosen["median"] * 1e-6) / MFMA_BF16_PEAK, 4),
+               counts=[int(c) for c in w["counts"]], t_hat=[round(x, 4) for x in t_hat])
     res["binding"] = "hbm" if w["layer_bytes"] / HBM_PEAK >= w["flops"] / MFMA_BF16_PEAK else "mfma"
     res["roof_frac"] = round(res["roof_us"] / res["us"], 4)
     if exhaustive:
@@ -167,30 +219,32 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
         res["us_per_variant"] = [round(x, 3) for x in per_v]
         res["best_variant"] = best
         res["gap_to_exhaustive"] = round(per_v[chosen] / per_v[best] - 1.0, 4)
+        b.variant.fill_(chosen)
         del g_forced
     del g_chosen
     return res, layer, b, w
 
 
 def kernel_segments(torch, L, b, T, reps):
-    """Per-step event timing of each library call, eager, cold cache."""
-    names = ["route_topk", "select_config", "align_sort", "grouped_ffn", "combine"]
-    fns = [L.route, L.select, L.align, L.ffn, L.combine]
+    """Per-call HIP-event timing on the launch stream, eager, each step cold."""
+    names = ["route_topk", "select_config", "align_sort", "grouped_gate_up", "grouped_down",
+             "combine"]
+    fns = [L.route, L.select, L.align, L.gate_up, L.down, L.combine]
     acc = {n: [] for n in names}
     for _ in range(reps):
-        T.flush()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
-        evs[0].record()
-        for f, e in zip(fns, evs[1:]):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(fns))]
+        for i, f in enumerate(fns):
+            T.flush()
+            evs[2 * i].record()
             f(b)
-            e.record()
+            evs[2 * i + 1].record()
         torch.cuda.synchronize()
         for i, n in enumerate(names):
-            acc[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+            acc[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3)
     return {n: statistics.fmean(v) for n, v in acc.items()}
 
 
-def cpu_baseline(np, synth, oracle, layer, sample_tokens, budget_s=30.0):
+def cpu_baseline(np, oracle, layer, sample_tokens):
     """The CPU oracle as it stands, on a bounded token sample of the same load;
     reported as microseconds per layer scaled by B / sample."""
     n = min(layer.tokens, sample_tokens)
@@ -198,7 +252,7 @@ def cpu_baseline(np, synth, oracle, layer, sample_tokens, budget_s=30.0):
     nthreads = oracle.max_threads()
     t0 = time.perf_counter()
     ids, w = oracle.route_topk(layer.logits, layer.shape.top_k)
-    cnt = oracle.counts(ids, layer.expert_begin, layer.shape.local_experts)
+    oracle.counts(ids, layer.expert_begin, layer.shape.local_experts)
     oracle.align(ids, layer.expert_begin, layer.shape.local_experts, 16)
     t_route = time.perf_counter() - t0
     t1 = time.perf_counter()
@@ -206,10 +260,39 @@ def cpu_baseline(np, synth, oracle, layer, sample_tokens, budget_s=30.0):
     t_ffn = time.perf_counter() - t1
     us = (t_route + t_ffn * layer.tokens / n) * 1e6
     return dict(value=round(us, 1), unit="us/layer", cores=nthreads, kind="oracle",
-                sample=f"{n} of {layer.tokens} tokens through O5-O6 (scaled x{layer.tokens / n:.2f}); "
-                       f"O1-O4 on the full batch; measured {t_route + t_ffn:.1f} s"), int(cnt.sum())
+                sample=f"{n} of {layer.tokens} tokens through the expert FFN and combine (scaled "
+                       f"x{layer.tokens / n:.2f}); routing, counts and align on the full batch; "
+                       f"measured {t_route + t_ffn:.1f} s")
 
 
+def sweep_shape(torch, np, synth, L, T, shape, V, reps, log_prefix=""):
+    sw = SWEEPS[shape]
+    wdev = synth.make_weights_device(shape)
+    theta, theta_src = load_theta(shape, V)
+    nowts = {"w1": None, "w3": None, "w2": None, "s1": None, "s3": None, "s2": None}
+    out = []
+    for tok in sw["tokens"]:
+        for a in sw["alphas"]:
+            tb = 8 * tok if shape == "dsv3_share" else tok
+            r, *_ = run_point(torch, np, synth, L, T, shape, tb, a, wdev, nowts, theta, V, reps, 3,
+                              exhaustive=True)
+            if shape == "dsv3_share":
+                r["tokens_per_gpu"] = tok
+            log(f"[bench] {shape} B={tb} alpha={a}: {r['us']:.1f} us, v={r['variant']} "
+                f"best={r['best_variant']} gap={r['gap_to_exhaustive']:.3f} "
+                f"roof={r['roof_frac']:.3f} ({r['binding']}) per-variant {r['us_per_variant']}")
+            out.append(r)
+    del wdev
+    torch.cuda.empty_cache()
+    gaps = [max(r["gap_to_exhaustive"], 0.0) for r in out]
+    chooser = dict(geomean_gap=round(math.exp(statistics.fmean([math.log1p(x) for x in gaps])) - 1, 4),
+                   worst_gap=round(max(gaps), 4),
+                   within_5pct=round(sum(g_ <= 0.05 for g_ in gaps) / len(gaps), 3),
+                   theta=theta_src or "untuned default (th1 = 1: fewest waves)")
+    return dict(points=out, chooser=chooser)
+
+
+# ----------------------------------------------------------------------- main --
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,8 +301,9 @@ def main():
     ap.add_argument("--shape", default="mixtral", choices=sorted(SWEEPS))
     ap.add_argument("--tokens", type=int, default=128)
     ap.add_argument("--alpha", type=float, default=1.0)
-    ap.add_argument("--sweep", type=int, default=1, help="1: also run the tokens x alpha sweep")
-    ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--sweep", default="mixtral,qwen3,dsv3_share,kimi_share",
+                    help="comma-separated workloads to sweep ('' for none)")
+    ap.add_argument("--sweep-reps", type=int, default=15)
     ap.add_argument("--cpu", type=int, default=1, help="1: time the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=128)
     ap.add_argument("--exhaustive", type=int, default=1,
@@ -229,6 +313,12 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size kernel that scales HBM byte counters) and exit")
     args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the layer on one GPU "
+              "(one GPU's expert share at its real size); no multi-GPU figure is produced.",
+              file=sys.stderr)
+        sys.exit(2)
 
     if args.calibrate_copy:
         import torch
@@ -245,12 +335,6 @@ def main():
                   f"({2 * n / dt / 1e9:.1f} GB/s wall)", flush=True)
         return
 
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the layer on one GPU "
-              "(one GPU's expert share at its real size); no multi-GPU figure is produced.",
-              file=sys.stderr)
-        sys.exit(2)
-
     import numpy as np
     import torch
 
@@ -265,9 +349,8 @@ def main():
     T = Timer(torch)
     log(f"[bench] generating {args.shape} weights on the GPU")
     wdev = synth.make_weights_device(args.shape)
-    whost = synth.host_weights(wdev)
-    theta_cpu, theta_src = load_theta(args.shape, V)
-    theta = theta_cpu
+    whost = synth.host_weights(wdev) if args.cpu else {k: None for k in wdev}
+    theta, theta_src = load_theta(args.shape, V)
 
     # ---- headline point: K timed steps ------------------------------------------------
     log(f"[bench] headline {args.shape} B={args.tokens} alpha={args.alpha}")
@@ -285,44 +368,39 @@ def main():
     log(f"[bench] headline median {st['median']:.1f} us; segments " +
         ", ".join(f"{k} {v:.1f}" for k, v in seg.items()))
 
-    t_ffn = seg["grouped_ffn"] * 1e-6
-    bound = "hbm" if w["ffn_bytes"] / HBM_PEAK >= w["flops"] / MFMA_BF16_PEAK else "mfma"
+    # dominant kernel: the grouped gate/up launch (2/3 of the weight bytes and FLOPs)
+    t_gu = seg["grouped_gate_up"] * 1e-6
+    bound = "hbm" if w["gate_up_bytes"] / HBM_PEAK >= w["gate_up_flops"] / MFMA_BF16_PEAK else "mfma"
     if bound == "hbm":
-        achieved, peak, unit = w["ffn_bytes"] / t_ffn / 1e9, HBM_PEAK / 1e9, "GB/s"
+        achieved, peak, unit = w["gate_up_bytes"] / t_gu / 1e9, HBM_PEAK / 1e9, "GB/s"
     else:
-        achieved, peak, unit = w["flops"] / t_ffn / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
-    roofline = dict(kernel="grouped_ffn (gate/up+SwiGLU launch and down launch)", bound=bound,
-                    achieved=round(achieved, 2), peak=round(peak, 1), unit=unit,
-                    frac=round(achieved / peak, 4), traffic=None,
-                    alg_bytes=int(w["ffn_bytes"]), alg_flops=int(w["flops"]),
-                    avg_duration_us=round(seg["grouped_ffn"], 3))
+        achieved, peak, unit = w["gate_up_flops"] / t_gu / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
+    wl_key = f"{args.shape}:B{args.tokens}:a{args.alpha:g}:v{head['variant']}"
+    roofline = dict(bound=bound, achieved=round(achieved, 2), peak=round(peak, 1), unit=unit,
+                    frac=round(achieved / peak, 4), traffic=measured_traffic(wl_key),
+                    kernel="ffn_kernel<1,*> (moe_grouped_gate_up: grouped gate/up GEMM + SwiGLU)",
+                    alg_bytes_per_launch=int(w["gate_up_bytes"]),
+                    alg_flops_per_launch=int(w["gate_up_flops"]),
+                    avg_launch_us=round(seg["grouped_gate_up"], 3), traffic_key=wl_key,
+                    kernel_source_sha=kernel_source_hash())
 
     # ---- CPU oracle baseline ------------------------------------------------------------
     cpu = None
     if args.cpu:
         log("[bench] timing the CPU oracle on a token sample")
-        cpu, _ = cpu_baseline(np, synth, oracle, layer, args.cpu_sample)
+        cpu = cpu_baseline(np, oracle, layer, args.cpu_sample)
+    del whost
 
-    # ---- sweep ------------------------------------------------------------------------------
-    sweep = []
-    if args.sweep:
-        sw = SWEEPS[args.shape]
-        for tok in sw["tokens"]:
-            for a in sw["alphas"]:
-                tb = 8 * tok if args.shape == "dsv3_share" else tok
-                r, *_ = run_point(torch, np, synth, L, T, args.shape, tb, a, wdev, whost, theta, V,
-                                  args.sweep_reps, 3, exhaustive=True)
-                log(f"[bench] sweep B={tb} alpha={a}: {r['us']:.1f} us, v={r['variant']} "
-                    f"best={r['best_variant']} gap={r['gap_to_exhaustive']:.3f} "
-                    f"roof={r['roof_frac']:.3f} ({r['binding']})")
-                sweep.append(r)
-    gaps = [max(r["gap_to_exhaustive"], 0.0) for r in sweep]
-    chooser = None
-    if gaps:
-        chooser = dict(geomean_gap=round(math.exp(statistics.fmean([math.log1p(x) for x in gaps])) - 1, 4),
-                       worst_gap=round(max(gaps), 4),
-                       within_5pct=round(sum(g_ <= 0.05 for g_ in gaps) / len(gaps), 3),
-                       theta=theta_src or "untuned default (th1 = 1: fewest waves)")
+    # ---- sweeps -------------------------------------------------------------------------
+    sweeps = {}
+    shapes = [s for s in args.sweep.split(",") if s]
+    if shapes:
+        del b, g
+        del wdev
+        torch.cuda.empty_cache()
+    for shp in shapes:
+        log(f"[bench] sweep {shp}")
+        sweeps[shp] = sweep_shape(torch, np, synth, L, T, shp, V, args.sweep_reps)
 
     sh = layer.shape
     out = {
@@ -336,7 +414,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if sh.act_dtype == 1 else "f32",
+        "dtype": {synth.F32: "f32", synth.BF16: "bf16"}[sh.act_dtype],
         "data": "synthetic (Dirichlet-skewed Gumbel-top-k routing, N(0,0.02) activations/weights)",
         "config": {"workload": f"{args.shape}-shaped fused MoE layer", "tokens": args.tokens,
                    "alpha": args.alpha, "hidden": sh.hidden, "inter": sh.inter,
@@ -346,14 +424,15 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "layer": dict(variant=head["variant"], best_variant=head.get("best_variant"),
-                      gap_to_exhaustive=head.get("gap_to_exhaustive"), roof_us=head["roof_us"],
+                      gap_to_exhaustive=head.get("gap_to_exhaustive"),
+                      us_per_variant=head.get("us_per_variant"), roof_us=head["roof_us"],
                       roof_frac=round(head["roof_us"] / st["median"], 4), binding=head["binding"],
                       hbm_frac=round(w["layer_bytes"] / (st["median"] * 1e-6) / HBM_PEAK, 4),
                       mfma_frac=round(w["flops"] / (st["median"] * 1e-6) / MFMA_BF16_PEAK, 4),
                       segments_us={k: round(v, 3) for k, v in seg.items()},
+                      theta=theta_src or "untuned default (th1 = 1: fewest waves)",
                       timed_wall_s=round(t_wall, 3), p10=round(st["p10"], 3), p90=round(st["p90"], 3)),
-        "chooser": chooser,
-        "sweep": sweep,
+        "sweeps": sweeps,
     }
     line = json.dumps(out)
     print(line, flush=True)

@@ -159,6 +159,9 @@ struct FfnArgs {
   int64_t rows_max;
 };
 
+// ring slots of per-tile metadata (see Tile::run_all)
+constexpr int kMetaSlots = 4;
+
 // slot of workgroup wg so that consecutive slots share an XCD (workgroup wg runs
 // on XCD wg % 8)
 __device__ __forceinline__ int xcd_slot(int wg, int grid) {
@@ -197,13 +200,14 @@ struct Tile {
   static constexpr int FM = MW / 16, FN = NW / 16;
   static constexpr int KSTEPS = BK / 32;
   static constexpr int RED_FLOATS = (WK > 1) ? (WK - 1) * WM * WN * NMAT * FM * FN * 4 * 64 : 0;
-  static constexpr int LDS_BYTES =
-      (2 * STAGE > RED_FLOATS * 4 ? 2 * STAGE : RED_FLOATS * 4);
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static_assert(RED_FLOATS * 4 <= STAGE, "the K-split sums reuse one stage buffer");
   static_assert(WM * WN * WK * 64 == kThreads, "waves must cover the workgroup");
   static_assert(FM >= 1 && FN >= 1 && MW % 16 == 0 && NW % 16 == 0, "wave tile too small");
   static_assert(C >= 8 && (C & (C - 1)) == 0, "LDS rows must be a power of two of >= 128 bytes");
   static_assert(KSTEPS % WK == 0, "K-split waves must divide the stage");
   static_assert(!FP8 || GCB * 2 == C, "fp8 chunk pairs");
+  static_assert(GA % kThreads == 0 && GB % kThreads == 0, "every thread owns whole chunks");
 
   struct Regs {
     u32x4 a[NA];
@@ -211,128 +215,161 @@ struct Tile {
     float s[FP8 ? NB : 1];
   };
 
-  // Runs tile (rb, nt) of this phase.  `rowok` is an LDS array of BM ints.
-  __device__ static void run(const FfnArgs& g, uint8_t* lds, int* rowok, int rb, int nt) {
+  // Tile metadata kept in LDS, in a ring of kMetaSlots slots: the BM slot ids of
+  // the tile's rows, the number of leading rows that hold a slot, and the local
+  // expert.  A slot is refilled at least one barrier after its last reader.
+  static constexpr int META = BM + 2;
+
+  // Runs every tile of this phase that belongs to workgroup slot `slot` of `G`:
+  // tiles t = slot, slot + G, ... (t = rb + nb * nt).  The tiles' stages form one
+  // continuous pipeline, so the next tile's first loads are in flight while the
+  // current tile finishes.
+  __device__ __forceinline__ static void run_all(const FfnArgs& g, uint8_t* lds, int* meta3,
+                                                int nb, int slot, int G) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
+    const int total = nb * (N / BN);
+    if (slot >= total) return;
+    const int ntile = (total - slot + G - 1) / G;
+    const int nst = (K + BK - 1) / BK;
+    const int nv = ntile * nst;  // stages of all tiles of this workgroup
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int wk = wave % WK;
     const int wn = (wave / WK) % WN;
     const int wm = wave / (WK * WN);
-    const int e = g.block_expert[rb];
-    const int64_t row0 = (int64_t)rb * BM;
-    const int n0 = nt * BN;
-    const int nst = (K + BK - 1) / BK;
-
-    // an expert index outside the local block cannot come from moe_align_sort;
-    // the whole workgroup skips such a tile rather than address beyond the weights
-    if ((unsigned)e >= (unsigned)g.E_loc) return;
-
-    // rows of this tile that hold a routed slot (others are padding); the barrier
-    // before it keeps the previous tile's epilogue reads of rowok apart
-    __syncthreads();
-    for (int r = tid; r < BM; r += kThreads) rowok[r] = g.sorted_slots[row0 + r];
-    __syncthreads();
-
-    // ---- per-thread chunk assignment ----
-    // chunk q = i * kThreads + tid of a stage: A chunk q is column q % GCA of tile
-    // row q / GCA; weight chunk q is column q % GCB of weight row (q / GCB) % BN of
-    // matrix q / (BN * GCB).  Row sources are 32-bit element offsets (the host
-    // keeps every operand below 2^31 elements); -1 marks a padding row.
-    int a_off[NA];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = i * kThreads + tid;
-      a_off[i] = -1;
-      if (q < GA) {
-        const int row = q / GCA, c = q % GCA;
-        const int s = rowok[row];
-        if (s >= 0 && s < g.slots) {
-          const int64_t arow = PHASE == 1 ? (int64_t)(s / g.k) : row0 + row;
-          a_off[i] = (int)(arow * K) + c * EPC_A;
-        }
-      }
-    }
     const Act* abase = (const Act*)(PHASE == 1 ? g.x : g.h);
     const Wt* wmat0 = (const Wt*)(PHASE == 1 ? g.w1 : g.w2);
     const Wt* wmat1 = (const Wt*)(PHASE == 1 ? g.w3 : g.w2);
-    const int64_t wrow0 = (int64_t)e * N + n0;  // first weight row of the tile
     const float* smat0 = PHASE == 1 ? g.s1 : g.s2;
     const float* smat1 = PHASE == 1 ? g.s3 : g.s2;
 
-    auto load_stage = [&](Regs& R, int s) {
-      const int k0 = s * BK;
+    // ---- tile metadata ----
+    // Thread r < BM fetches the slot ids of rows r and r + 1 of a tile (rows that
+    // hold a slot come first in a row-block) into registers one pipeline step
+    // before they are stored to the tile's ring slot, so the wait for them never
+    // drains the stage loads issued in between.
+    int ms0 = -1, ms1 = -1, me = -1;
+    auto fetch_meta = [&](int j) __attribute__((always_inline)) {
+      const int t = slot + j * G;
+      const int rb = t % nb;
+      const int64_t row0 = (int64_t)rb * BM;
+      if (tid < BM) {
+        ms0 = g.sorted_slots[row0 + tid];
+        ms1 = tid + 1 < BM ? g.sorted_slots[row0 + tid + 1] : -1;
+      }
+      if (tid == 0) me = g.block_expert[rb];
+    };
+    auto store_meta = [&](int j) __attribute__((always_inline)) {  // all threads; the caller's next barrier publishes it
+      int* m = meta3 + (j % kMetaSlots) * META;
+      if (tid < BM) {
+        const bool v0 = ms0 >= 0 && ms0 < g.slots;
+        const bool v1 = ms1 >= 0 && ms1 < g.slots;
+        m[tid] = v0 ? ms0 : -1;
+        if (v0 && !v1) m[BM] = tid + 1;    // last row of the leading run
+        if (tid == 0 && !v0) m[BM] = 0;    // no row holds a slot
+      }
+      if (tid == 0) m[BM + 1] = me;
+    };
+
+    // ---- one stage: global -> registers, registers -> LDS ----
+    // Both steps are branch-free, so the compiler can count the loads in flight
+    // exactly and each stage waits only for its own data.  A chunk that holds no
+    // operand (a padding row, columns beyond K, a tile past the workgroup's last)
+    // is still loaded, from a valid fallback address, and still written: padding
+    // rows of A only reach output rows that are never stored, reduction steps
+    // beyond K are never computed, and a missing tile is never computed.
+    // The load cursor (l_j, l_s) is the tile and stage of the next load; the
+    // tile's row sources are computed once, when the cursor enters it.
+    int l_j = 0, l_s = 0;
+    int l_aoff[NA];  // element offset of each A chunk's row start (-1: no operand)
+    int64_t l_wrow0 = 0;
+    int l_n0 = 0, l_e = 0;
+    bool l_eok = false;
+    auto enter_load_tile = [&](int j) __attribute__((always_inline)) {
+      const int* m = meta3 + (j % kMetaSlots) * META;
+      const int t = slot + j * G;
+      const int rb = t % nb;
+      l_n0 = (t / nb) * BN;
+      l_e = m[BM + 1];
+      l_eok = j < ntile && (unsigned)l_e < (unsigned)g.E_loc;
+      if (!l_eok) {
+        l_e = 0;
+        l_n0 = 0;
+      }
+      l_wrow0 = (int64_t)l_e * N + l_n0;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int q = i * kThreads + tid;
+        const int row = q / GCA, c = q % GCA;
+        const int sl = m[row];
+        l_aoff[i] = -1;
+        if (l_eok && sl >= 0 && sl < g.slots) {
+          const int64_t arow = PHASE == 1 ? (int64_t)(sl / g.k) : (int64_t)rb * BM + row;
+          l_aoff[i] = (int)(arow * K) + c * EPC_A;
+        }
+      }
+    };
+    auto load_stage = [&](Regs& R) __attribute__((always_inline)) {
+      if (l_s == 0) enter_load_tile(l_j);
+      const int k0 = l_s * BK;
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int q = i * kThreads + tid;
         const int kel = (q % GCA) * EPC_A;
-        if (a_off[i] >= 0 && k0 + kel < K)
-          R.a[i] = *(const u32x4*)(abase + a_off[i] + k0);
-        else
-          R.a[i] = u32x4{0u, 0u, 0u, 0u};
+        const bool ok = l_aoff[i] >= 0 && k0 + kel < K;
+        R.a[i] = *(const u32x4*)(abase + (ok ? (int64_t)l_aoff[i] + k0 : 0));
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int q = i * kThreads + tid;
-        const int m = q / (BN * GCB);
+        const int mt = q / (BN * GCB);
         const int row = (q / GCB) % BN;
         const int kel = (q % GCB) * EPC_B;
-        if (q < GB && k0 + kel < K) {
-          const Wt* wm_ = m == 0 ? wmat0 : wmat1;
-          R.b[i] = *(const u32x4*)(wm_ + (wrow0 + row) * K + k0 + kel);
-          if constexpr (FP8) {
-            const float* sm = m == 0 ? smat0 : smat1;
-            R.s[i] = sm[((int64_t)e * (N / 128) + (n0 + row) / 128) * (K / 128) + (k0 + kel) / 128];
-          }
-        } else {
-          R.b[i] = u32x4{0u, 0u, 0u, 0u};
-          if constexpr (FP8) R.s[i] = 0.f;
+        const bool ok = l_eok && k0 + kel < K;
+        const Wt* wm_ = mt == 0 ? wmat0 : wmat1;
+        R.b[i] = *(const u32x4*)(wm_ + (ok ? (l_wrow0 + row) * K + k0 + kel : 0));
+        if constexpr (FP8) {
+          const float* sm = mt == 0 ? smat0 : smat1;
+          R.s[i] = sm[ok ? ((int64_t)l_e * (N / 128) + (l_n0 + row) / 128) * (K / 128) + (k0 + kel) / 128 : 0];
         }
       }
+      if (++l_s == nst) {
+        l_s = 0;
+        ++l_j;
+      }
     };
-    auto write_stage = [&](const Regs& R, uint8_t* buf) {
+    auto write_stage = [&](const Regs& R, uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int q = i * kThreads + tid;
-        if (q < GA) {
-          const int row = q / GCA, c = q % GCA;
-          *(u32x4*)(buf + row * ROWB + ((c ^ swz(row)) << 4)) = R.a[i];
-        }
+        const int row = q / GCA, c = q % GCA;
+        *(u32x4*)(buf + row * ROWB + ((c ^ swz(row)) << 4)) = R.a[i];
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int q = i * kThreads + tid;
-        if (q < GB) {
-          const int row = BM + q / GCB;  // LDS row: matrices follow each other
-          const int c = q % GCB;
-          const int sw = swz(row);
-          uint8_t* rp = buf + row * ROWB;
-          if constexpr (FP8) {
-            u32x4 o0, o1;
-            fp8x16_to_bf16(R.b[i], R.s[i], o0, o1);
-            *(u32x4*)(rp + (((2 * c) ^ sw) << 4)) = o0;
-            *(u32x4*)(rp + (((2 * c + 1) ^ sw) << 4)) = o1;
-          } else {
-            *(u32x4*)(rp + ((c ^ sw) << 4)) = R.b[i];
-          }
+        const int c = q % GCB;
+        const int row = BM + q / GCB;  // LDS row: matrices follow each other
+        const int sw = swz(row);
+        uint8_t* rp = buf + row * ROWB;
+        if constexpr (FP8) {
+          u32x4 o0, o1;
+          fp8x16_to_bf16(R.b[i], R.s[i], o0, o1);
+          *(u32x4*)(rp + (((2 * c) ^ sw) << 4)) = o0;
+          *(u32x4*)(rp + (((2 * c + 1) ^ sw) << 4)) = o1;
+        } else {
+          *(u32x4*)(rp + ((c ^ sw) << 4)) = R.b[i];
         }
       }
     };
 
-    // ---- accumulators ----
+    // ---- MFMA over one stage ----
     f32x4 acc[NMAT][FM][FN];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     const int lr = lane & 15;   // row of the fragment
     const int lg = lane >> 4;   // k-group of 8 inside a 32-step
-    auto read_frag = [&](const uint8_t* buf, int row, int step, Frag<F32>& f) {
+    auto read_frag = [&](const uint8_t* buf, int row, int step, Frag<F32>& f) __attribute__((always_inline)) {
       const uint8_t* rp = buf + row * ROWB;
       const int sw = swz(row);
       if constexpr (F32) {
@@ -344,8 +381,37 @@ struct Tile {
         f.v = __builtin_bit_cast(bf16x8, *(const u32x4*)(rp + ((c0 ^ sw) << 4)));
       }
     };
-    auto compute_stage = [&](const uint8_t* buf, int s) {
-      const int k0 = s * BK;
+    // 16-row groups with no routed slot are skipped (their rows are never stored).
+    // A stage whose rows are all live for this wave and that lies inside K takes a
+    // straight-line path (every fragment read and MFMA unconditional, so reads and
+    // MFMAs interleave freely); only the last row-block of an expert and the last
+    // stage of a ragged K take the guarded path.
+    auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jj = 0; jj < KSTEPS / WK; ++jj) {
+        const int step = jj * WK + wk;
+        Frag<F32> fa[FM];
+        Frag<F32> fb[NMAT][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa[i], fb[mt][j]);
+      }
+    };
+    auto compute_stage = [&](const uint8_t* buf, int k0, int nvalid) __attribute__((always_inline)) {
+      if (wm * MW >= nvalid) return;
+      if (wm * MW + MW <= nvalid && k0 + BK <= K) {
+        compute_full(buf);
+        return;
+      }
 #pragma unroll
       for (int jj = 0; jj < KSTEPS / WK; ++jj) {
         const int step = jj * WK + wk;
@@ -353,91 +419,131 @@ struct Tile {
           Frag<F32> fa[FM];
           Frag<F32> fb[NMAT][FN];
 #pragma unroll
-          for (int i = 0; i < FM; ++i) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
+          for (int i = 0; i < FM; ++i)
+            if (wm * MW + i * 16 < nvalid) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m)
+          for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) read_frag(buf, BM + m * BN + wn * NW + j * 16 + lr, step, fb[m][j]);
+            for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m)
+          for (int i = 0; i < FM; ++i)
+            if (wm * MW + i * 16 < nvalid) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+              for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-              for (int j = 0; j < FN; ++j) mma(acc[m][i][j], fa[i], fb[m][j]);
+                for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa[i], fb[mt][j]);
+            }
         }
       }
     };
 
-    // ---- pipeline: RS register stages ahead, two LDS buffers ----
-    Regs R[RS];
+    // ---- epilogue of tile j: K-split reduction, SwiGLU, stores ----
+    auto epilogue = [&](int j, uint8_t* red_area) __attribute__((always_inline)) {
+      const int* m = meta3 + (j % kMetaSlots) * META;
+      const int t = slot + j * G;
+      const int64_t row0 = (int64_t)(t % nb) * BM;
+      const int n0 = (t / nb) * BN;
+      if ((unsigned)m[BM + 1] >= (unsigned)g.E_loc) return;  // uniform: no such tile
+      if constexpr (WK > 1) {
+        // waves wk > 0 hand their sums to wave wk = 0 through the LDS buffer just
+        // computed on (the barrier first lets every wave finish reading it)
+        float* red = (float*)red_area;
+        constexpr int PER = NMAT * FM * FN * 4 * 64;
+        const int rslot = (wm * WN + wn) * (WK - 1);
+        __syncthreads();
+        if (wk > 0) {
+          float* dst = red + (rslot + wk - 1) * PER;
 #pragma unroll
-    for (int u = 0; u < RS; ++u)
-      if (u < nst) load_stage(R[u], u);
-    for (int s0 = 0; s0 < nst; s0 += RS) {
-#pragma unroll
-      for (int u = 0; u < RS; ++u) {
-        const int s = s0 + u;
-        if (s < nst) {
-          uint8_t* buf = lds + (s & 1) * STAGE;
-          write_stage(R[u], buf);
-          if (s + RS < nst) load_stage(R[u], s + RS);
-          __syncthreads();
-          compute_stage(buf, s);
-        }
-      }
-    }
-    __syncthreads();  // every wave is done reading the stage buffers
-
-    // ---- in-tile K split: waves wk > 0 hand their sums to wave wk = 0 ----
-    if constexpr (WK > 1) {
-      float* red = (float*)lds;
-      constexpr int PER = NMAT * FM * FN * 4 * 64;
-      const int slot = (wm * WN + wn) * (WK - 1);
-      if (wk > 0) {
-        float* dst = red + (slot + wk - 1) * PER;
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-              for (int c = 0; c < 4; ++c) dst[(((m * FM + i) * FN + j) * 4 + c) * 64 + lane] = acc[m][i][j][c];
-      }
-      __syncthreads();
-      if (wk == 0) {
-#pragma unroll
-        for (int q = 0; q < WK - 1; ++q) {
-          const float* src = red + (slot + q) * PER;
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m)
+          for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-              for (int j = 0; j < FN; ++j)
+              for (int jn = 0; jn < FN; ++jn)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[m][i][j][c] += src[(((m * FM + i) * FN + j) * 4 + c) * 64 + lane];
+                for (int c = 0; c < 4; ++c)
+                  dst[(((mt * FM + i) * FN + jn) * 4 + c) * 64 + lane] = acc[mt][i][jn][c];
         }
-      }
-      __syncthreads();  // the reduction area is free again
-    }
-
-    // ---- epilogue: lane holds rows 4*(lane/16)+c, column lane%16 of each block ----
-    if (wk == 0) {
-      Act* out = (Act*)(PHASE == 1 ? g.h : g.y_slots);
+        __syncthreads();
+        if (wk == 0) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+          for (int qq = 0; qq < WK - 1; ++qq) {
+            const float* src = red + (rslot + qq) * PER;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = wm * MW + i * 16 + (lane >> 4) * 4 + c;
-          if (rowok[r] < 0) continue;
-          Act* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
+            for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const float v = PHASE == 1 ? silu_mul(acc[0][i][j][c], acc[NMAT - 1][i][j][c]) : acc[0][i][j][c];
-            store_out<Act>(orow + j * 16, v);
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int jn = 0; jn < FN; ++jn)
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    acc[mt][i][jn][c] += src[(((mt * FM + i) * FN + jn) * 4 + c) * 64 + lane];
           }
         }
+      }
+      // lane holds rows 4*(lane/16)+c, column lane%16 of each 16x16 block
+      if (wk == 0) {
+        Act* out = (Act*)(PHASE == 1 ? g.h : g.y_slots);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = wm * MW + i * 16 + (lane >> 4) * 4 + c;
+            if (m[r] < 0) continue;
+            Act* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn) {
+              const float v = PHASE == 1 ? silu_mul(acc[0][i][jn][c], acc[NMAT - 1][i][jn][c])
+                                         : acc[0][i][jn][c];
+              store_out<Act>(orow + jn * 16, v);
+            }
+          }
+      }
+    };
+
+    // ---- the pipeline: RS register stages ahead, two LDS buffers ----
+    // Tiles whose first stage is among the first RS + 1 are described before the
+    // loop; a later tile j' is fetched at the step whose load is the last stage
+    // before it and stored at the next step, before that step's barrier and the
+    // load of its first stage.
+    Regs R[RS];
+    for (int j = 0; j < ntile && j * nst <= RS; ++j) {
+      fetch_meta(j);
+      store_meta(j);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < RS; ++u)
+      if (u < nv) load_stage(R[u]);
+    int c_j = 0, c_s = 0;  // tile and stage being written and computed
+    for (int v0 = 0; v0 < nv; v0 += RS) {
+#pragma unroll
+      for (int u = 0; u < RS; ++u) {
+        const int v = v0 + u;
+        if (v < nv) {
+          const int* m = meta3 + (c_j % kMetaSlots) * META;
+          uint8_t* buf = lds + (v & 1) * STAGE;
+          write_stage(R[u], buf);
+          const bool more = v + RS < nv;  // a real load follows this step
+          if (more && l_s == 0 && v >= 1) store_meta(l_j);
+          if (v + RS + 1 < nv && l_s == nst - 1) fetch_meta(l_j + 1);
+          __syncthreads();
+          load_stage(R[u]);  // past the last stage it reads fallback addresses
+          if (c_s == 0) {
+#pragma unroll
+            for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          if ((unsigned)m[BM + 1] < (unsigned)g.E_loc) compute_stage(buf, c_s * BK, m[BM]);
+          if (c_s == nst - 1) epilogue(c_j, buf);
+          if (++c_s == nst) {
+            c_s = 0;
+            ++c_j;
+          }
+        }
+      }
     }
   }
 };
@@ -448,20 +554,23 @@ struct Tile {
 // ---------------------------------------------------------------------------
 template <int V, int PHASE, int WKIND>
 struct Cfg;
-#define MOE_CFG(V, BM, BN1, BN2, ROWB, WM, WN, WK, RS)                                          \
+#define MOE_CFG(V, BM, BN1, BN2, ROWB1, ROWB2, WM, WN, WK, RS)                                 \
   template <int PHASE, int WKIND>                                                             \
   struct Cfg<V, PHASE, WKIND> {                                                               \
     static constexpr int BN = PHASE == 1 ? BN1 : BN2;                                         \
-    using R = Tile<BM, BN, WM, WN, WK, ROWB, RS, PHASE, WKIND>;                                \
+    using R = Tile<BM, BN, WM, WN, WK, (PHASE == 1 ? ROWB1 : ROWB2), RS, PHASE, WKIND>;        \
   };                                                                                          \
   static_assert(kVariants[V].bm == BM && kVariants[V].bn1 == BN1 && kVariants[V].bn2 == BN2 && \
-                    kVariants[V].rowb == ROWB && kVariants[V].wm == WM &&                     \
+                    kVariants[V].rowb == ROWB1 && kVariants[V].wm == WM &&                    \
                     kVariants[V].wn == WN && kVariants[V].wk == WK && kVariants[V].splitk == 1, \
                 "kernel configuration table out of sync with kVariants");
-MOE_CFG(0, 16, 16, 16, 1024, 1, 1, 4, 1)
-MOE_CFG(1, 32, 32, 32, 512, 1, 2, 2, 1)
-MOE_CFG(2, 64, 64, 64, 256, 2, 2, 1, 1)
-MOE_CFG(3, 128, 128, 128, 128, 2, 2, 1, 1)
+// Two workgroups share a compute unit, so each stage buffer holds at most 32 KiB:
+// every stage carries 16 KiB of weights (the down phase has one weight matrix, so
+// its LDS rows are twice as wide).
+MOE_CFG(0, 16, 16, 16, 512, 1024, 1, 1, 4, 2)
+MOE_CFG(1, 32, 32, 32, 256, 512, 1, 2, 2, 2)
+MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2)
+MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2)
 #undef MOE_CFG
 
 template <int WKIND>
@@ -477,17 +586,15 @@ constexpr int lds_bytes() {
 
 // The tiles of configuration V in phase PHASE, dealt out statically.
 template <int V, int PHASE, int WKIND>
-__device__ void run_phase(const FfnArgs& g, uint8_t* lds, int* rowok, int nb) {
+__device__ __forceinline__ void run_phase(const FfnArgs& g, uint8_t* lds, int* meta3, int nb) {
   using R = typename Cfg<V, PHASE, WKIND>::R;
-  const int q = (PHASE == 1 ? g.I : g.H) / Cfg<V, PHASE, WKIND>::BN;
-  const int total = nb * q;
-  for (int t = xcd_slot(blockIdx.x, gridDim.x); t < total; t += gridDim.x) R::run(g, lds, rowok, t % nb, t / nb);
+  R::run_all(g, lds, meta3, nb, xcd_slot(blockIdx.x, gridDim.x), gridDim.x);
 }
 
 template <int PHASE, int WKIND>
-__global__ void __launch_bounds__(kThreads) ffn_kernel(FfnArgs g) {
+__global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int rowok[kMaxBlockM];
+  __shared__ int meta3[kMetaSlots * (kMaxBlockM + 2)];
   const int v = *g.variant;
   int nb = *g.num_blocks;
   if (v < 0 || v >= kNumVariants || nb <= 0) return;  // no tiles (align_sort wrote none)
@@ -495,10 +602,10 @@ __global__ void __launch_bounds__(kThreads) ffn_kernel(FfnArgs g) {
   const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
   nb = nb < nb_cap ? nb : nb_cap;
   switch (v) {
-    case 0: run_phase<0, PHASE, WKIND>(g, lds, rowok, nb); break;
-    case 1: run_phase<1, PHASE, WKIND>(g, lds, rowok, nb); break;
-    case 2: run_phase<2, PHASE, WKIND>(g, lds, rowok, nb); break;
-    case 3: run_phase<3, PHASE, WKIND>(g, lds, rowok, nb); break;
+    case 0: run_phase<0, PHASE, WKIND>(g, lds, meta3, nb); break;
+    case 1: run_phase<1, PHASE, WKIND>(g, lds, meta3, nb); break;
+    case 2: run_phase<2, PHASE, WKIND>(g, lds, meta3, nb); break;
+    case 3: run_phase<3, PHASE, WKIND>(g, lds, meta3, nb); break;
     default: break;
   }
 }
@@ -506,7 +613,7 @@ __global__ void __launch_bounds__(kThreads) ffn_kernel(FfnArgs g) {
 template <int PHASE, int WKIND>
 hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
   constexpr int lds = lds_bytes<WKIND>();
-  static_assert(lds <= 160 * 1024 - 1024, "LDS budget");
+  static_assert((lds + 4096) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
   static int done[64] = {0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

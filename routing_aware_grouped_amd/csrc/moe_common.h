@@ -54,17 +54,17 @@ constexpr int kNumVariants = 4;
 constexpr int kThreads = 256;
 
 constexpr VariantDesc kVariants[kNumVariants] = {
-    {16, 16, 16, 1024, 1, 1, 4, 1},
-    {32, 32, 32, 512, 1, 2, 2, 1},
-    {64, 64, 64, 256, 2, 2, 1, 1},
-    {128, 128, 128, 128, 2, 2, 1, 1},
+    {16, 16, 16, 512, 1, 1, 4, 1},
+    {32, 32, 32, 256, 1, 2, 2, 1},
+    {64, 64, 64, 128, 2, 2, 1, 1},
+    {128, 64, 128, 128, 2, 2, 1, 1},
 };
 
 constexpr int kMinBlockM = 16;
 constexpr int kMaxBlockM = 128;
 
 // workgroups per CU of the persistent grouped-FFN launch
-constexpr int kWgPerCu = 1;
+constexpr int kWgPerCu = 2;
 
 // Device-side table of the cost-model constants (RaMP Eq. 1) per configuration.
 struct CostTable {

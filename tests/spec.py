@@ -5,13 +5,13 @@ from the library)."""
 
 # BLOCK_M, BLOCK_N gate/up, BLOCK_N down, BLOCK_K, waves M, N, K-split, split-K
 MENU = [
-    (16, 16, 16, 512, 1, 1, 4, 1),
-    (32, 32, 32, 256, 1, 2, 2, 1),
-    (64, 64, 64, 128, 2, 2, 1, 1),
-    (128, 128, 128, 64, 2, 2, 1, 1),
+    (16, 16, 16, 256, 1, 1, 4, 1),
+    (32, 32, 32, 128, 1, 2, 2, 1),
+    (64, 64, 64, 64, 2, 2, 1, 1),
+    (128, 64, 128, 64, 2, 2, 1, 1),
 ]
 # workgroups per compute unit of the persistent grouped-FFN launch (both phases)
-WG_PER_CU = (1, 1)
+WG_PER_CU = (2, 2)
 
 
 def cost_constants(hidden: int, inter: int, num_cus: int) -> dict:
