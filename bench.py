@@ -168,6 +168,9 @@ def stats(us):
 
 # ---------------------------------------------------------------------- theta --
 def load_theta(shape_name, V):
+    """The fitted chooser coefficients of a workload (routing_aware_grouped_amd.tune),
+    and a label saying where they came from and whether they were fit on the
+    current kernel sources."""
     import torch
     path = os.path.join(ROOT, "routing_aware_grouped_amd", "theta", f"{shape_name}.json")
     if os.path.exists(path):
@@ -175,7 +178,9 @@ def load_theta(shape_name, V):
             d = json.load(f)
         th = torch.tensor(d["theta"], dtype=torch.float32)
         if th.shape == (V, 4):
-            return th, os.path.relpath(path, ROOT)
+            fresh = d.get("kernel_source_sha") == kernel_source_hash()
+            return th, (os.path.relpath(path, ROOT) +
+                        ("" if fresh else " (fit on an older kernel build)"))
     # no fitted table: predict time by waves alone (th1 = 1)
     th = torch.zeros(V, 4, dtype=torch.float32)
     th[:, 1] = 1.0
