@@ -37,7 +37,6 @@ Work accounting follows GC-MoE's conventions:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -51,8 +50,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5166e15  # flop/s, dense bf16 MFMA (256 CU x 2.4 GHz x 4096)
 METRIC = "fused-MoE layer µs + % of HBM/MFMA roofline vs tokens × Dirichlet α skew"
-KERNEL_SOURCES = ["routing_aware_grouped_amd/csrc/grouped_ffn.hip",
-                  "routing_aware_grouped_amd/csrc/moe_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 SWEEPS = {
@@ -97,11 +94,8 @@ def roof_us(w):
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from routing_aware_grouped_amd.tune import kernel_source_hash as h
+    return h()
 
 
 def measured_traffic(workload_key):

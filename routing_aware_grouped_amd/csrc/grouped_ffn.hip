@@ -1,5 +1,5 @@
-// grouped_ffn.hip -- the polymorphic, persistent grouped expert FFN (both GEMMs in
-// one launch).
+// grouped_ffn.hip -- the polymorphic, persistent grouped expert FFN (one kernel,
+// launched once for the gate/up GEMM and once for the down GEMM).
 //
 // What is computed, for every padded row r of the expert grouping with
 // e = block_expert[r / b] and t = sorted_slots[r] / k (GC-MoE arXiv 2611.04222,
@@ -19,10 +19,10 @@
 // Scheduling.  The two GEMM phases are two launches of this kernel (the down
 // phase needs every column of h for its row-block, and a dependency between
 // workgroups of one launch would need a wait); each launch is persistent
-// (compute units x 1 workgroups) and deals its tiles out statically:
+// (compute units x kWgPerCu workgroups) and deals its tiles out statically:
 // tile t = rb + nb * nt (row-block fastest, so the row-blocks of one expert that
 // share a weight slab are adjacent) goes to slot t mod G, and slots are numbered
-// so that 32 consecutive ones sit on one XCD (the hardware deals workgroup ids
+// so that G / 8 consecutive ones sit on one XCD (the hardware deals workgroup ids
 // round-robin over the 8 XCDs, each with its own L2).  There are no atomics and
 // no waits between workgroups; every loop has a static bound.
 //

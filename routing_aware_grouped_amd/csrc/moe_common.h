@@ -35,7 +35,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---------------------------------------------------------------------------
 // Compiled tile configurations of the polymorphic grouped FFN.  All share one
-// workgroup size (256 threads = 4 waves), one launch (both GEMM phases), one LDS
+// workgroup size (256 threads = 4 waves), one launch shape per GEMM phase, one LDS
 // allocation and one register budget, so they are one occupancy class (RaMP,
 // section 3.3: one shared-memory buffer and one register count for every entry).
 //   bm    token rows per tile (b_c of RaMP Eq. 1)

@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -50,11 +51,21 @@ FIT_ALPHAS = [0.03, 0.5, 3.0, 30.0]
 FIT_REP0 = 100
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks and empty lines, so that an
+    edit of a comment leaves the hash (and the timings filed under it) valid."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash() -> str:
+    """First 16 hex digits of the sha256 of the grouped FFN's code (comments
+    stripped); timings, fitted theta and counter summaries are filed under it."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(HERE, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
