@@ -115,8 +115,9 @@ int32_t moe_num_variants(void);
  *                problem uses half of it; fp8 weights are staged as bf16)
  *   [4] waves along M, [5] waves along N, [6] waves splitting K inside a tile
  *   [7] split-K of the down phase across tiles (1 = none)
+ *   [8] 1 if weights are read with non-temporal (streaming) loads, 0 if cached
  * Errors: MOE_ERR_INVALID_ARG for v outside [0, V) or out == NULL. */
-#define MOE_VARIANT_FIELDS 8
+#define MOE_VARIANT_FIELDS 9
 moe_status moe_variant_info(int32_t v, int32_t* out);
 
 /* The cost-model constants moe_select_config uses for problem *p on the current

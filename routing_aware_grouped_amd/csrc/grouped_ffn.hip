@@ -175,7 +175,7 @@ __device__ __forceinline__ int xcd_slot(int wg, int grid) {
 //   ROWB = LDS bytes per tile row per stage, waves WM x WN x WK, RS register
 //   stages in flight.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int WK, int ROWB, int RS, int PHASE, int WKIND>
+template <int BM, int BN, int WM, int WN, int WK, int ROWB, int RS, int STREAM, int PHASE, int WKIND>
 struct Tile {
   using T = Types<WKIND>;
   using Act = typename T::Act;
@@ -329,7 +329,11 @@ struct Tile {
         const int kel = (q % GCB) * EPC_B;
         const bool ok = l_eok && k0 + kel < K;
         const Wt* wm_ = mt == 0 ? wmat0 : wmat1;
-        R.b[i] = *(const u32x4*)(wm_ + (ok ? (l_wrow0 + row) * K + k0 + kel : 0));
+        const u32x4* src = (const u32x4*)(wm_ + (ok ? (l_wrow0 + row) * K + k0 + kel : 0));
+        if constexpr (STREAM)
+          R.b[i] = __builtin_nontemporal_load(src);
+        else
+          R.b[i] = *src;
         if constexpr (FP8) {
           const float* sm = mt == 0 ? smat0 : smat1;
           R.s[i] = sm[ok ? ((int64_t)l_e * (N / 128) + (l_n0 + row) / 128) * (K / 128) + (k0 + kel) / 128 : 0];
@@ -554,23 +558,28 @@ struct Tile {
 // ---------------------------------------------------------------------------
 template <int V, int PHASE, int WKIND>
 struct Cfg;
-#define MOE_CFG(V, BM, BN1, BN2, ROWB1, ROWB2, WM, WN, WK, RS)                                 \
+#define MOE_CFG(V, BM, BN1, BN2, ROWB1, ROWB2, WM, WN, WK, RS, STREAM)                         \
   template <int PHASE, int WKIND>                                                             \
   struct Cfg<V, PHASE, WKIND> {                                                               \
     static constexpr int BN = PHASE == 1 ? BN1 : BN2;                                         \
-    using R = Tile<BM, BN, WM, WN, WK, (PHASE == 1 ? ROWB1 : ROWB2), RS, PHASE, WKIND>;        \
+    using R = Tile<BM, BN, WM, WN, WK, (PHASE == 1 ? ROWB1 : ROWB2), RS, STREAM, PHASE, WKIND>; \
   };                                                                                          \
   static_assert(kVariants[V].bm == BM && kVariants[V].bn1 == BN1 && kVariants[V].bn2 == BN2 && \
                     kVariants[V].rowb == ROWB1 && kVariants[V].wm == WM &&                    \
-                    kVariants[V].wn == WN && kVariants[V].wk == WK && kVariants[V].splitk == 1, \
+                    kVariants[V].wn == WN && kVariants[V].wk == WK && kVariants[V].splitk == 1 && \
+                    kVariants[V].stream == STREAM,                                            \
                 "kernel configuration table out of sync with kVariants");
 // Two workgroups share a compute unit, so each stage buffer holds at most 32 KiB:
 // every stage carries 16 KiB of weights (the down phase has one weight matrix, so
-// its LDS rows are twice as wide).
-MOE_CFG(0, 16, 16, 16, 512, 1024, 1, 1, 4, 2)
-MOE_CFG(1, 32, 32, 32, 256, 512, 1, 2, 2, 2)
-MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2)
-MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2)
+// its LDS rows are twice as wide).  The small-M configurations read each weight
+// tile once (one row-block per expert is the common case), so they stream the
+// weights with non-temporal loads, which sustain a markedly higher HBM rate; the
+// largest one serves many row-blocks per expert that re-read each weight tile
+// from L2, so it keeps cached loads.
+MOE_CFG(0, 16, 16, 16, 512, 1024, 1, 1, 4, 2, 1)
+MOE_CFG(1, 32, 32, 32, 256, 512, 1, 2, 2, 2, 1)
+MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2, 1)
+MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2, 0)
 #undef MOE_CFG
 
 template <int WKIND>

@@ -103,7 +103,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
@@ -118,7 +118,7 @@ int32_t moe_num_variants(void) { return kNumVariants; }
 moe_status moe_variant_info(int32_t v, int32_t* out) {
   if (!out || v < 0 || v >= kNumVariants) return MOE_ERR_INVALID_ARG;
   const VariantDesc& d = kVariants[v];
-  const int32_t vals[MOE_VARIANT_FIELDS] = {d.bm, d.bn1, d.bn2, d.rowb / 2, d.wm, d.wn, d.wk, d.splitk};
+  const int32_t vals[MOE_VARIANT_FIELDS] = {d.bm, d.bn1, d.bn2, d.rowb / 2, d.wm, d.wn, d.wk, d.splitk, d.stream};
   memcpy(out, vals, sizeof vals);
   return MOE_OK;
 }

@@ -45,19 +45,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 //         bf16 operands, rowb / 4 for fp32)
 //   wm, wn, wk  waves along M, along N, and splitting K inside a tile
 //   splitk      tiles splitting K of the down phase (1 = none)
+//   stream      1: weights are read with non-temporal (streaming) loads, for the
+//               small-M configurations where each weight tile is read once;
+//               0: cached loads, for row-blocks that re-read a weight tile
 // ---------------------------------------------------------------------------
 struct VariantDesc {
-  int bm, bn1, bn2, rowb, wm, wn, wk, splitk;
+  int bm, bn1, bn2, rowb, wm, wn, wk, splitk, stream;
 };
 
 constexpr int kNumVariants = 4;
 constexpr int kThreads = 256;
 
 constexpr VariantDesc kVariants[kNumVariants] = {
-    {16, 16, 16, 512, 1, 1, 4, 1},
-    {32, 32, 32, 256, 1, 2, 2, 1},
-    {64, 64, 64, 128, 2, 2, 1, 1},
-    {128, 64, 128, 128, 2, 2, 1, 1},
+    {16, 16, 16, 512, 1, 1, 4, 1, 1},
+    {32, 32, 32, 256, 1, 2, 2, 1, 1},
+    {64, 64, 64, 128, 2, 2, 1, 1, 1},
+    {128, 64, 128, 128, 2, 2, 1, 1, 0},
 };
 
 constexpr int kMinBlockM = 16;

@@ -3,12 +3,13 @@ tests as a specification.  The library's moe_variant_info / moe_cost_constants
 are checked against it, and the oracle's cost-model inputs come from here (never
 from the library)."""
 
-# BLOCK_M, BLOCK_N gate/up, BLOCK_N down, BLOCK_K, waves M, N, K-split, split-K
+# BLOCK_M, BLOCK_N gate/up, BLOCK_N down, BLOCK_K, waves M, N, K-split, split-K,
+# streaming (non-temporal) weight loads
 MENU = [
-    (16, 16, 16, 256, 1, 1, 4, 1),
-    (32, 32, 32, 128, 1, 2, 2, 1),
-    (64, 64, 64, 64, 2, 2, 1, 1),
-    (128, 64, 128, 64, 2, 2, 1, 1),
+    (16, 16, 16, 256, 1, 1, 4, 1, 1),
+    (32, 32, 32, 128, 1, 2, 2, 1, 1),
+    (64, 64, 64, 64, 2, 2, 1, 1, 1),
+    (128, 64, 128, 64, 2, 2, 1, 1, 0),
 ]
 # workgroups per compute unit of the persistent grouped-FFN launch (both phases)
 WG_PER_CU = (2, 2)
