@@ -91,7 +91,7 @@ typedef struct moe_sizes {
   int64_t rows_max;        /* capacity (elements) of sorted_slots; rows of y_slots */
   int64_t blocks_max;      /* capacity (elements) of block_expert                  */
   int64_t y_slots_bytes;   /* rows_max * H * sizeof(act)                           */
-  int64_t workspace_bytes; /* grouped_ffn workspace: h [rows_max][I] + header      */
+  int64_t workspace_bytes; /* grouped_ffn workspace: header, h, partial tiles       */
   int64_t align_ws_bytes;  /* reserved, 0 in this version                          */
 } moe_sizes;
 
@@ -172,10 +172,12 @@ moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const i
  * Padding rows are neither read nor written.  x is [B][H] (act dtype); s1/s3/s2
  * are the fp8 block scales (NULL unless weight_dtype is MOE_FP8_E4M3).  y_slots
  * [rows_max][H] (act dtype).  workspace: >= workspace_bytes, 256-byte aligned;
- * holds h.  The call enqueues two launches of one persistent polymorphic kernel,
- * the gate/up phase and then the down phase (moe_grouped_gate_up followed by
- * moe_grouped_down); each reads *variant and *num_blocks from device memory, so
- * every compiled configuration runs under one fixed launch shape. */
+ * holds h and the fp32 partial sums of the tiles that a phase's last round splits
+ * across workgroups.  The call enqueues, for the gate/up phase and then the down
+ * phase (moe_grouped_gate_up followed by moe_grouped_down), one launch of a
+ * persistent polymorphic kernel and one of its fix-up kernel, which adds the
+ * split tiles' partial sums; each reads *variant and *num_blocks from device
+ * memory, so every compiled configuration runs under one fixed launch shape. */
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
                            const void* w2, const float* s1, const float* s3, const float* s2,
                            const int32_t* sorted_slots, const int32_t* block_expert,

@@ -153,6 +153,7 @@ struct FfnArgs {
   const int32_t* variant;
   void* h;         // [rows_max][I] act
   void* y_slots;   // [rows_max][H] act
+  float* part;     // [grid][2][NMAT * BM * BN] fp32 sums of split tail tiles
   int H, I, k;
   int E_loc;
   int slots;  // B * k
@@ -200,6 +201,8 @@ struct Tile {
   static constexpr int FM = MW / 16, FN = NW / 16;
   static constexpr int KSTEPS = BK / 32;
   static constexpr int RED_FLOATS = (WK > 1) ? (WK - 1) * WM * WN * NMAT * FM * FN * 4 * 64 : 0;
+  static constexpr int NFRAG = NMAT * FM * FN;   // 16x16 accumulator blocks per wave
+  static constexpr int PIECE = NMAT * BM * BN;   // floats of one partial tile
   static constexpr int LDS_BYTES = 2 * STAGE;
   static_assert(RED_FLOATS * 4 <= STAGE, "the K-split sums reuse one stage buffer");
   static_assert(WM * WN * WK * 64 == kThreads, "waves must cover the workgroup");
@@ -208,6 +211,7 @@ struct Tile {
   static_assert(KSTEPS % WK == 0, "K-split waves must divide the stage");
   static_assert(!FP8 || GCB * 2 == C, "fp8 chunk pairs");
   static_assert(GA % kThreads == 0 && GB % kThreads == 0, "every thread owns whole chunks");
+  static_assert(WM * WN * NFRAG * 256 == PIECE && PIECE <= kPieceMax, "partial tile layout");
 
   struct Regs {
     u32x4 a[NA];
@@ -220,19 +224,80 @@ struct Tile {
   // expert.  A slot is refilled at least one barrier after its last reader.
   static constexpr int META = BM + 2;
 
-  // Runs every tile of this phase that belongs to workgroup slot `slot` of `G`:
-  // tiles t = slot, slot + G, ... (t = rb + nb * nt).  The tiles' stages form one
-  // continuous pipeline, so the next tile's first loads are in flight while the
-  // current tile finishes.
+  // Stores one tile's sums (lane holds rows 4*(lane/16)+c, column lane%16 of each
+  // 16x16 block): h = silu(gate) * up in the gate/up phase, y_slots in the down
+  // phase.  Rows without a slot (m[r] < 0) are not stored.
+  __device__ __forceinline__ static void store_acc(const FfnArgs& g, const f32x4 (&acc)[NMAT][FM][FN],
+                                                  const int* m, int64_t row0, int n0, int wm,
+                                                  int wn, int lane) {
+    const int N = PHASE == 1 ? g.I : g.H;
+    Act* out = (Act*)(PHASE == 1 ? g.h : g.y_slots);
+    const int lr = lane & 15;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = wm * MW + i * 16 + (lane >> 4) * 4 + c;
+        if (m[r] < 0) continue;
+        Act* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) {
+          const float v = PHASE == 1 ? silu_mul(acc[0][i][jn][c], acc[NMAT - 1][i][jn][c])
+                                     : acc[0][i][jn][c];
+          store_out<Act>(orow + jn * 16, v);
+        }
+      }
+  }
+
+  // Whether the r tail tiles of a phase are split across all G workgroups.  A
+  // last round in which at least half of the workgroups stream weights still runs
+  // near the HBM rate, so streaming configurations split only smaller tails; the
+  // cached configuration (compute-bound loads) always splits.
+  __device__ __forceinline__ static bool split_tail(int r, int G) {
+    return r > 0 && (!STREAM || 2 * r < G);
+  }
+
+  // Runs the work of workgroup slot `slot` of `G` (hybrid Stream-K).  The phase's
+  // tiles t = rb + nb * nt come in F = total / G full rounds, dealt round-robin
+  // (tiles slot, slot + G, ...), so the row-blocks that share a weight slab run at
+  // the same time on one XCD.  The r = total - F * G tiles left over would leave
+  // most workgroups idle in a last round; when split_tail says so, their r * nst
+  // reduction stages are cut into G equal contiguous ranges, one per workgroup, so
+  // every workgroup streams the same number of stages to within one (otherwise
+  // they are dealt as one more round of whole tiles).  A range spans at most two
+  // tail tiles; a tail tile that a range holds only in part is a piece, whose fp32
+  // sums go to g.part (two piece slots per workgroup), and the fix-up launch that
+  // follows adds the pieces of each split tile in reduction order and stores it.
+  // (No workgroup ever waits for another, and no atomics are used.)
+  // All the work items (whole tiles, then pieces) form one continuous pipeline, so
+  // the next item's first loads are in flight while the current one finishes.
   __device__ __forceinline__ static void run_all(const FfnArgs& g, uint8_t* lds, int* meta3,
                                                 int nb, int slot, int G) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
     const int total = nb * (N / BN);
-    if (slot >= total) return;
-    const int ntile = (total - slot + G - 1) / G;
     const int nst = (K + BK - 1) / BK;
-    const int nv = ntile * nst;  // stages of all tiles of this workgroup
+    const int F = total / G;                        // full rounds
+    const int r = total - F * G;                    // tail tiles
+    const bool split = split_tail(r, G);
+    const int Fw = F + (!split && slot < r ? 1 : 0);  // whole tiles of this workgroup
+    const int64_t Ut = split ? (int64_t)r * nst : 0;  // tail stages cut into ranges
+    const int64_t u0 = (int64_t)slot * Ut / G;      // this workgroup's tail range
+    const int len = (int)((int64_t)(slot + 1) * Ut / G - u0);
+    const int tp0 = (int)(u0 / nst);                // its first tail tile
+    const int sb0 = (int)(u0 - (int64_t)tp0 * nst);  // and the stage it starts at
+    const int npc = len == 0 ? 0 : (sb0 + len > nst ? 2 : 1);
+    const int nitem = Fw + npc;
+    const int nv = Fw * nst + len;  // stages of all items of this workgroup
+    if (nv == 0) return;
+    // item j: tile, and its stage range [item_sb, item_se)
+    auto item_tile = [&](int j) __attribute__((always_inline)) {
+      return j < Fw ? slot + j * G : F * G + tp0 + (j - Fw);
+    };
+    auto item_sb = [&](int j) __attribute__((always_inline)) { return j == Fw ? sb0 : 0; };
+    auto item_se = [&](int j) __attribute__((always_inline)) {
+      return j < Fw ? nst : (j == Fw ? (sb0 + len < nst ? sb0 + len : nst) : sb0 + len - nst);
+    };
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -252,7 +317,7 @@ struct Tile {
     // drains the stage loads issued in between.
     int ms0 = -1, ms1 = -1, me = -1;
     auto fetch_meta = [&](int j) __attribute__((always_inline)) {
-      const int t = slot + j * G;
+      const int t = item_tile(j);
       const int rb = t % nb;
       const int64_t row0 = (int64_t)rb * BM;
       if (tid < BM) {
@@ -282,18 +347,19 @@ struct Tile {
     // beyond K are never computed, and a missing tile is never computed.
     // The load cursor (l_j, l_s) is the tile and stage of the next load; the
     // tile's row sources are computed once, when the cursor enters it.
-    int l_j = 0, l_s = 0;
+    int l_j = 0, l_s = item_sb(0), l_se = item_se(0);
+    bool l_new = true;  // the next load is the first of item l_j
     int l_aoff[NA];  // element offset of each A chunk's row start (-1: no operand)
     int64_t l_wrow0 = 0;
     int l_n0 = 0, l_e = 0;
     bool l_eok = false;
     auto enter_load_tile = [&](int j) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
-      const int t = slot + j * G;
+      const int t = item_tile(j);
       const int rb = t % nb;
       l_n0 = (t / nb) * BN;
       l_e = m[BM + 1];
-      l_eok = j < ntile && (unsigned)l_e < (unsigned)g.E_loc;
+      l_eok = j < nitem && (unsigned)l_e < (unsigned)g.E_loc;
       if (!l_eok) {
         l_e = 0;
         l_n0 = 0;
@@ -312,7 +378,8 @@ struct Tile {
       }
     };
     auto load_stage = [&](Regs& R) __attribute__((always_inline)) {
-      if (l_s == 0) enter_load_tile(l_j);
+      if (l_new) enter_load_tile(l_j);
+      l_new = false;
       const int k0 = l_s * BK;
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
@@ -339,9 +406,11 @@ struct Tile {
           R.s[i] = sm[ok ? ((int64_t)l_e * (N / 128) + (l_n0 + row) / 128) * (K / 128) + (k0 + kel) / 128 : 0];
         }
       }
-      if (++l_s == nst) {
-        l_s = 0;
+      if (++l_s == l_se) {  // past the last item the cursor runs on harmlessly
         ++l_j;
+        l_s = item_sb(l_j);
+        l_se = item_se(l_j);
+        l_new = true;
       }
     };
     auto write_stage = [&](const Regs& R, uint8_t* buf) __attribute__((always_inline)) {
@@ -441,10 +510,11 @@ struct Tile {
       }
     };
 
-    // ---- epilogue of tile j: K-split reduction, SwiGLU, stores ----
-    auto epilogue = [&](int j, uint8_t* red_area) __attribute__((always_inline)) {
+    // ---- epilogue of item j: K-split reduction, then the tile's stores, or the
+    // piece's fp32 sums to its slot of g.part ----
+    auto epilogue = [&](int j, uint8_t* red_area, bool whole) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
-      const int t = slot + j * G;
+      const int t = item_tile(j);
       const int64_t row0 = (int64_t)(t % nb) * BM;
       const int n0 = (t / nb) * BN;
       if ((unsigned)m[BM + 1] >= (unsigned)g.E_loc) return;  // uniform: no such tile
@@ -484,33 +554,32 @@ struct Tile {
           }
         }
       }
-      // lane holds rows 4*(lane/16)+c, column lane%16 of each 16x16 block
       if (wk == 0) {
-        Act* out = (Act*)(PHASE == 1 ? g.h : g.y_slots);
+        if (whole) {
+          store_acc(g, acc, m, row0, n0, wm, wn, lane);
+        } else {
+          // piece slot j - Fw of this workgroup; 16 bytes per lane, wave-contiguous
+          float* dst = g.part + ((int64_t)slot * 2 + (j - Fw)) * PIECE + (wm * WN + wn) * NFRAG * 256;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+          for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = wm * MW + i * 16 + (lane >> 4) * 4 + c;
-            if (m[r] < 0) continue;
-            Act* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int jn = 0; jn < FN; ++jn) {
-              const float v = PHASE == 1 ? silu_mul(acc[0][i][jn][c], acc[NMAT - 1][i][jn][c])
-                                         : acc[0][i][jn][c];
-              store_out<Act>(orow + jn * 16, v);
-            }
-          }
+              for (int jn = 0; jn < FN; ++jn)
+                *(f32x4*)(dst + (((mt * FM + i) * FN + jn) * 64 + lane) * 4) = acc[mt][i][jn];
+        }
       }
     };
 
     // ---- the pipeline: RS register stages ahead, two LDS buffers ----
-    // Tiles whose first stage is among the first RS + 1 are described before the
-    // loop; a later tile j' is fetched at the step whose load is the last stage
+    // Items whose first stage is among the first RS + 1 are described before the
+    // loop; a later item j' is fetched at the step whose load is the last stage
     // before it and stored at the next step, before that step's barrier and the
     // load of its first stage.
     Regs R[RS];
-    for (int j = 0; j < ntile && j * nst <= RS; ++j) {
+    for (int j = 0; j < nitem; ++j) {
+      const int start = j <= Fw ? j * nst : Fw * nst + item_se(Fw) - sb0;  // first stage of item j
+      if (start > RS) break;
       fetch_meta(j);
       store_meta(j);
     }
@@ -518,7 +587,7 @@ struct Tile {
 #pragma unroll
     for (int u = 0; u < RS; ++u)
       if (u < nv) load_stage(R[u]);
-    int c_j = 0, c_s = 0;  // tile and stage being written and computed
+    int c_j = 0, c_s = item_sb(0), c_sb = c_s, c_se = item_se(0);  // item and stage being computed
     for (int v0 = 0; v0 < nv; v0 += RS) {
 #pragma unroll
       for (int u = 0; u < RS; ++u) {
@@ -528,11 +597,11 @@ struct Tile {
           uint8_t* buf = lds + (v & 1) * STAGE;
           write_stage(R[u], buf);
           const bool more = v + RS < nv;  // a real load follows this step
-          if (more && l_s == 0 && v >= 1) store_meta(l_j);
-          if (v + RS + 1 < nv && l_s == nst - 1) fetch_meta(l_j + 1);
+          if (more && l_new && v >= 1) store_meta(l_j);
+          if (v + RS + 1 < nv && l_s == l_se - 1) fetch_meta(l_j + 1);
           __syncthreads();
           load_stage(R[u]);  // past the last stage it reads fallback addresses
-          if (c_s == 0) {
+          if (c_s == c_sb) {
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
@@ -541,14 +610,82 @@ struct Tile {
                 for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
           if ((unsigned)m[BM + 1] < (unsigned)g.E_loc) compute_stage(buf, c_s * BK, m[BM]);
-          if (c_s == nst - 1) epilogue(c_j, buf);
-          if (++c_s == nst) {
-            c_s = 0;
+          if (c_s == c_se - 1) epilogue(c_j, buf, c_sb == 0 && c_se == nst);
+          if (++c_s == c_se) {
             ++c_j;
+            c_s = c_sb = item_sb(c_j);
+            c_se = item_se(c_j);
           }
         }
       }
     }
+  }
+
+  // The fix-up of tail tile tq (the tile F * G + tq of the schedule in run_all):
+  // if more than one workgroup's range holds part of it, add their pieces in
+  // reduction order (workgroup order) and store the tile.  Workgroup w's tail
+  // range is [w * Ut / G, (w + 1) * Ut / G); the owner of tail stage u is the last
+  // w whose range starts at or before u.  With Ut >= G every range is non-empty,
+  // the tile's pieces belong to owners w0..w1, and only w0's range can start
+  // before the tile (its piece is then in its slot 1).  With Ut < G every range
+  // holds at most one stage, so each of the tile's nst stages is its own piece,
+  // in slot 0 of its owner.
+  __device__ __forceinline__ static void fixup(const FfnArgs& g, int* meta, int nb, int G, int tq) {
+    const int N = PHASE == 1 ? g.I : g.H;
+    const int K = PHASE == 1 ? g.H : g.I;
+    const int total = nb * (N / BN);
+    const int nst = (K + BK - 1) / BK;
+    const int F = total / G;
+    const int r = total - F * G;
+    if (tq >= r || !split_tail(r, G)) return;
+    const int64_t Ut = (int64_t)r * nst;
+    const int64_t ub = (int64_t)tq * nst;
+    const int w0 = (int)(((ub + 1) * G - 1) / Ut);
+    const int w1 = (int)(((ub + nst) * G - 1) / Ut);
+    if (w0 == w1) return;  // one range holds the whole tile; run_all stored it
+    const int t = F * G + tq;
+    const int rb = t % nb;
+    const int64_t row0 = (int64_t)rb * BM;
+    const int n0 = (t / nb) * BN;
+    if ((unsigned)g.block_expert[rb] >= (unsigned)g.E_loc) return;
+    const int tid = threadIdx.x;
+    if (tid < BM) {
+      const int sl = g.sorted_slots[row0 + tid];
+      meta[tid] = (sl >= 0 && sl < g.slots) ? sl : -1;
+    }
+    __syncthreads();
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wk = wave % WK;
+    const int wn = (wave / WK) % WN;
+    const int wm = wave / (WK * WN);
+    if (wk != 0) return;
+    f32x4 acc[NMAT][FM][FN];
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto add_piece = [&](int w, int pc) __attribute__((always_inline)) {
+      const float* src = g.part + ((int64_t)w * 2 + pc) * PIECE + (wm * WN + wn) * NFRAG * 256;
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn)
+            acc[mt][i][jn] += *(const f32x4*)(src + (((mt * FM + i) * FN + jn) * 64 + lane) * 4);
+    };
+    if (Ut >= G) {
+      const bool w0_before = (int64_t)w0 * Ut / G < ub;
+      for (int w = w0; w <= w1; ++w) add_piece(w, w == w0 && w0_before ? 1 : 0);
+    } else {
+      // (u + 1) * G <= Ut * G < G * G fits 32 bits
+      for (int u = (int)ub; u < (int)ub + nst; ++u)
+        add_piece((int)(((unsigned)(u + 1) * (unsigned)G - 1u) / (unsigned)Ut), 0);
+    }
+    store_acc(g, acc, meta, row0, n0, wm, wn, lane);
   }
 };
 
@@ -619,6 +756,26 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   }
 }
 
+// The fix-up of one phase's split tail tiles (Tile::fixup), one workgroup per
+// tail tile; the grid is the main launch's, which bounds the tail tiles.
+template <int PHASE, int WKIND>
+__global__ void __launch_bounds__(kThreads) ffn_fixup_kernel(FfnArgs g) {
+  __shared__ int meta[kMaxBlockM + 2];
+  const int v = *g.variant;
+  int nb = *g.num_blocks;
+  if (v < 0 || v >= kNumVariants || nb <= 0) return;
+  const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
+  nb = nb < nb_cap ? nb : nb_cap;
+  const int G = gridDim.x, tq = blockIdx.x;
+  switch (v) {
+    case 0: Cfg<0, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
+    case 1: Cfg<1, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
+    case 2: Cfg<2, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
+    case 3: Cfg<3, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
+    default: break;
+  }
+}
+
 template <int PHASE, int WKIND>
 hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
   constexpr int lds = lds_bytes<WKIND>();
@@ -634,6 +791,9 @@ hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
     done[dev] = 1;
   }
   ffn_kernel<PHASE, WKIND><<<grid, kThreads, lds, s>>>(g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ffn_fixup_kernel<PHASE, WKIND><<<grid, kThreads, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -653,12 +813,12 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,
-                              const int32_t* variant, void* y_slots, void* h, int num_cus,
-                              int64_t rows_max, hipStream_t s) {
+                              const int32_t* variant, void* y_slots, void* h, float* part,
+                              int num_cus, int64_t rows_max, hipStream_t s) {
   FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
-            h, y_slots, p.hidden, p.inter, p.top_k, p.local_experts, p.tokens * p.top_k,
-            rows_max};
-  const int grid = num_cus * kWgPerCu;
+            h, y_slots, part, p.hidden, p.inter, p.top_k, p.local_experts,
+            p.tokens * p.top_k, rows_max};
+  const int grid = num_cus * kWgPerCu < kMaxGrid ? num_cus * kWgPerCu : kMaxGrid;
   switch (p.weight_dtype) {
     case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);
     case MOE_BF16: return launch_w<W_BF16>(g, phases, grid, s);

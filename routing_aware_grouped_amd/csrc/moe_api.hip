@@ -13,7 +13,8 @@ using namespace moe;
 
 namespace {
 
-constexpr int64_t kWsHeader = 256;  // status word + padding, keeps h 256-byte aligned
+// workspace: a 256-byte header (reserved), h, then the partial tiles
+constexpr int64_t kWsHeader = 256;
 constexpr size_t kMaxLds = 160 * 1024;
 
 int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
@@ -66,7 +67,7 @@ void sizes_of(const moe_problem* p, moe_sizes* s) {
   s->y_slots_bytes = s->rows_max * p->hidden * eb;
   int64_t hb = s->rows_max * p->inter * eb;
   hb = (hb + 255) / 256 * 256;
-  s->workspace_bytes = kWsHeader + hb;
+  s->workspace_bytes = kWsHeader + hb + kPartBytes;
   s->align_ws_bytes = 0;
 }
 
@@ -206,9 +207,10 @@ moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, c
   const int cus = num_cus_current(&err);
   if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
   void* h = (char*)workspace + kWsHeader;
+  float* part = (float*)((char*)workspace + (sz.workspace_bytes - kPartBytes));
   return hip_status(launch_grouped_ffn(*p, phases, x, w1, w3, w2, fp8 ? s1 : nullptr,
                                        fp8 ? s3 : nullptr, fp8 ? s2 : nullptr, sorted_slots,
-                                       block_expert, num_blocks, variant, y_slots, h, cus,
+                                       block_expert, num_blocks, variant, y_slots, h, part, cus,
                                        sz.rows_max, (hipStream_t)stream));
 }
 

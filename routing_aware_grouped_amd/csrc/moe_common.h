@@ -69,6 +69,22 @@ constexpr int kMaxBlockM = 128;
 // workgroups per CU of the persistent grouped-FFN launch
 constexpr int kWgPerCu = 2;
 
+// The persistent grouped-FFN grid is min(CUs * kWgPerCu, kMaxGrid) workgroups.
+// Each may leave up to two partial tiles of at most kPieceMax fp32 sums in the
+// workspace (the split tail tiles), so the workspace size does not depend on the
+// device.
+constexpr int kMaxGrid = 1024;
+constexpr int piece_floats(const VariantDesc& d) {
+  return 2 * d.bm * d.bn1 > d.bm * d.bn2 ? 2 * d.bm * d.bn1 : d.bm * d.bn2;
+}
+constexpr int piece_max() {
+  int m = 0;
+  for (int v = 0; v < kNumVariants; ++v) m = piece_floats(kVariants[v]) > m ? piece_floats(kVariants[v]) : m;
+  return m;
+}
+constexpr int kPieceMax = piece_max();
+constexpr int64_t kPartBytes = (int64_t)kMaxGrid * 2 * kPieceMax * 4;
+
 // Device-side table of the cost-model constants (RaMP Eq. 1) per configuration.
 struct CostTable {
   int32_t b[kNumVariants];
@@ -92,8 +108,8 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,
-                              const int32_t* variant, void* y_slots, void* h, int num_cus,
-                              int64_t rows_max, hipStream_t s);
+                              const int32_t* variant, void* y_slots, void* h, float* part,
+                              int num_cus, int64_t rows_max, hipStream_t s);
 hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
                           const float* w, void* y, int64_t rows_max, hipStream_t s);
 

@@ -24,3 +24,14 @@ def cost_constants(hidden: int, inter: int, num_cus: int) -> dict:
         "S1": [num_cus * WG_PER_CU[0]] * len(MENU),
         "S2": [num_cus * WG_PER_CU[1]] * len(MENU),
     }
+
+
+# The persistent grouped-FFN grid: min(CUs * workgroups per CU, MAX_GRID).
+MAX_GRID = 1024
+
+
+def splits_tail(r: int, grid: int, stream: int) -> bool:
+    """Whether a phase's last r (< grid) tiles are split by reduction stages across
+    the whole grid (hybrid Stream-K): always for the cached configuration, and for
+    streaming ones when fewer than half of the workgroups would be busy."""
+    return r > 0 and (not stream or 2 * r < grid)
