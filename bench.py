@@ -226,9 +226,8 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
 
 def kernel_segments(torch, L, b, T, reps):
     """Per-call HIP-event timing on the launch stream, eager, each step cold."""
-    names = ["route_topk", "select_config", "align_sort", "grouped_gate_up", "grouped_down",
-             "combine"]
-    fns = [L.route, L.select, L.align, L.gate_up, L.down, L.combine]
+    names = ["route_select_align", "grouped_gate_up", "grouped_down", "combine"]
+    fns = [L.route_select_align, L.gate_up, L.down, L.combine]
     acc = {n: [] for n in names}
     for _ in range(reps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(fns))]

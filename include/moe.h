@@ -19,6 +19,7 @@
  *                      2.4, Eq. 2), written to device memory.
  *   moe_align_sort     the routed slots grouped by expert and padded into the
  *                      chosen configuration's tiles (RaMP section 3.2).
+ *   moe_route_select_align  the three steps above fused into fewer launches.
  *   moe_grouped_ffn    the polymorphic grouped expert kernel: every compiled
  *                      configuration lives in one kernel that reads c* from device
  *                      memory (RaMP section 3.3); gate/up with fused SwiGLU, then
@@ -164,6 +165,21 @@ moe_status moe_select_config(const moe_problem* p, const int32_t* counts, const 
 moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const int32_t* variant,
                           int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
                           int32_t* slot_pos, void* stream);
+
+/* Steps 1-3 fused: exactly moe_route_topk, then moe_select_config (when theta is
+ * not NULL), then moe_align_sort, with the same arguments and bit-identical
+ * outputs, in fewer launches.  RaMP section 3.2 describes one selection kernel
+ * that counts, chooses and lays out the tiles; here a batch that one workgroup
+ * routes (B <= 4 * (1024 / L), L the lanes per token: the smallest power of two
+ * >= E up to 64) runs in a single one-workgroup launch, a larger one as the
+ * routing launch(es) followed by one select-and-align workgroup.  theta NULL: no
+ * selection; the configuration already in *variant is used and t_hat is not
+ * written (t_hat may be NULL in any case).  Errors: as the three calls. */
+moe_status moe_route_select_align(const moe_problem* p, const float* logits, const float* theta,
+                                  int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  int32_t* variant, float* t_hat, int32_t* sorted_slots,
+                                  int32_t* block_expert, int32_t* num_blocks, int32_t* slot_pos,
+                                  void* stream);
 
 /* Step 4: grouped expert FFN (RaMP 3.3 and A.8; GC-MoE 2.1 Eq. 1).  For every
  * row r < R that holds a slot (sorted_slots[r] >= 0):

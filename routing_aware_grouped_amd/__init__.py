@@ -59,6 +59,8 @@ _SIGS = {
     "moe_route_topk": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
     "moe_select_config": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
     "moe_align_sort": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P], ctypes.c_int),
+    "moe_route_select_align": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P, P, P],
+                               ctypes.c_int),
     "moe_grouped_ffn": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P, P, P, P,
                          ctypes.c_size_t, P], ctypes.c_int),
     "moe_grouped_gate_up": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P,
@@ -155,6 +157,14 @@ def moe_align_sort(p, topk_ids, variant, sorted_slots, block_expert, num_blocks,
     _check("moe_align_sort", lib().moe_align_sort(_pp(p), _ptr(topk_ids), _ptr(variant),
                                                   _ptr(sorted_slots), _ptr(block_expert),
                                                   _ptr(num_blocks), _ptr(slot_pos), _stream(stream)))
+
+
+def moe_route_select_align(p, logits, theta, topk_ids, topk_w, counts, variant, t_hat,
+                           sorted_slots, block_expert, num_blocks, slot_pos, stream=None):
+    _check("moe_route_select_align", lib().moe_route_select_align(
+        _pp(p), _ptr(logits), _ptr(theta), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+        _ptr(variant), _ptr(t_hat), _ptr(sorted_slots), _ptr(block_expert), _ptr(num_blocks),
+        _ptr(slot_pos), _stream(stream)))
 
 
 def _ws_bytes(workspace, workspace_bytes):

@@ -174,6 +174,26 @@ moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const i
                                       num_blocks, slot_pos, (hipStream_t)stream));
 }
 
+moe_status moe_route_select_align(const moe_problem* p, const float* logits, const float* theta,
+                                  int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  int32_t* variant, float* t_hat, int32_t* sorted_slots,
+                                  int32_t* block_expert, int32_t* num_blocks, int32_t* slot_pos,
+                                  void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_ids || !topk_w || !counts || !variant || !sorted_slots || !block_expert ||
+      !num_blocks || !slot_pos)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(counts, 4))
+    return MOE_ERR_INVALID_ARG;
+  CostTable t;
+  st = fill_cost_table(p, &t);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_route_select_align(*p, logits, theta, t, topk_ids, topk_w, counts,
+                                              variant, t_hat, sorted_slots, block_expert,
+                                              num_blocks, slot_pos, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

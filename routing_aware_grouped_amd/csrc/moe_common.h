@@ -103,6 +103,11 @@ hipError_t launch_select_config(const moe_problem& p, const int32_t* counts, con
 hipError_t launch_align_sort(const moe_problem& p, const int32_t* ids, const int32_t* variant,
                              int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
                              int32_t* slot_pos, hipStream_t s);
+hipError_t launch_route_select_align(const moe_problem& p, const float* logits,
+                                     const float* theta, const CostTable& tab, int32_t* ids,
+                                     float* w, int32_t* counts, int32_t* variant, float* t_hat,
+                                     int32_t* sorted_slots, int32_t* block_expert,
+                                     int32_t* num_blocks, int32_t* slot_pos, hipStream_t s);
 // phases: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both (two launches)
 hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,

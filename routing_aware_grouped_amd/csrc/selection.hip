@@ -1,0 +1,586 @@
+// selection.hip -- steps 1 to 3 of the layer: top-k routing with the per-expert
+// histogram, the on-GPU choice of the tile configuration, and the stable grouping
+// of the routed slots into padded tiles; each as its own kernel (the three C entry
+// points) and fused (moe_route_select_align): one workgroup for batches one
+// workgroup routes, else the routing launch then one select+align workgroup.
+//
+// ---- step 1 ----
+//
+// What is computed (RaMP arXiv 2604.26039, 2.1: the router sends each token to k of
+// E experts; 2.3: the counts n_e of the GPU's experts sum to Bk; 3.2: the selection
+// kernel counts this GPU's tokens per local expert in shared memory and ignores
+// tokens routed elsewhere):
+//   ids[t][0..k)  the k largest logits of token t, descending; equal logits go to
+//                 the lower expert index and -0 equals +0
+//   w[t][j]       softmax over the k chosen logits (renormalize = 1) or those
+//                 experts' entries of the softmax over all E logits (renormalize = 0)
+//   counts[e]     #{(t, j) : ids[t][j] = e0 + e},  e < E_loc
+//
+// Design (gfx950, wave64): a group of L lanes (L = 8..64, a power of two >= E when
+// E <= 64, else 64) owns one token; lane i holds logits e = i, i + L, ... in
+// registers as 64-bit order-preserving keys (float order in the high word, ~index in
+// the low word, so one unsigned max also applies the lower-index tie rule).  Each of
+// the k rounds is a register max plus a log2(L)-step butterfly of cross-lane
+// shuffles; the winner's owner clears its key.  The histogram goes through LDS and
+// then to global memory: with one workgroup the counts are stored directly; with
+// many, a tiny kernel zeroes them first and workgroups add their LDS bins with
+// global atomics (integer, so the result is exact and order-independent).
+//
+// ---- step 2 ----
+//
+// RaMP (arXiv 2604.26039) 2.2 Eq. 1 gives the tiles and waves of configuration c on
+// load n: T_c = q_c * sum_e ceil(n_e / b_c), W_c = ceil(T_c / S_c); 3.1 Eq. 3 predicts
+// t_c = th_c0 + th_c1 W_c + th_c2 T_c + th_c3 A(n); 2.4 Eq. 2 takes the argmin.  The
+// grouped kernel here runs two phases (gate/up, then down), so T and W sum over
+// the phases: T = (q1 + q2) rt, W = ceil(q1 rt / S1) + ceil(q2 rt / S2) with
+// rt = sum_e ceil(n_e / b).  A(n) is read as the number of active experts
+// (n_e > 0), the term the appendix A.1 discussion says sets the floor at small
+// loads.  The prediction is one fp32 FMA chain,
+//   t = fma(th3, A, fma(th2, T, fma(th1, W, th0))),
+// and the first index wins ties.  One workgroup; one wave per configuration
+// (3.2: one warp per menu entry) reduces its row-tile count with cross-lane adds.
+//
+// ---- step 3 ----
+//
+// RaMP (arXiv 2604.26039) 3.2: the selection kernel writes the tokens grouped by
+// expert and padded into the chosen configuration's tiles.  The pages give no
+// layout; the one used here: experts in ascending local index, each expert's slots
+// s = t*k + j in ascending s (a stable counting sort), padded with -1 to a multiple
+// of b = BLOCK_M of the chosen configuration; an expert with no token gets no tile
+// (ceil(0/b) = 0, as in Eq. 1).  Outputs: sorted_slots [R], block_expert[R/b],
+// num_blocks, and the inverse map slot_pos (-1 for slots of other GPUs' experts).
+//
+// Design (one workgroup of 16 waves; the whole step stays in LDS):
+//   * a token's k experts are distinct, so inside one expert ascending s means
+//     ascending token t.  Tokens are cut into 64-token blocks, one lane per token.
+//     For a block, each wave builds a 64-bit lane mask per expert in LDS (bit i set
+//     when token blk*64+i is routed to that expert; LDS atomic OR).  The rank of a
+//     token inside its expert within the block is popcount(mask & lanes-below).
+//   * pass 1 stores popcount(mask) per (block, expert); pass 2 turns those into
+//     each block's first row per expert (exclusive prefix over blocks, plus the
+//     expert's padded offset from a scan over experts); pass 3 writes padding and
+//     the block->expert table; pass 4 rebuilds the block masks and scatters.
+// The permutation is therefore deterministic and equals the stable order exactly.
+#include "moe_common.h"
+
+namespace moe {
+
+size_t align_lds_bytes(int B, int E_loc);
+
+namespace {
+
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0 -> +0: the two compare equal
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_float(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m, kWave);
+  hi = __shfl_xor(hi, m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int L>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum_f32(float v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__global__ void zero_counts_kernel(int32_t* counts, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) counts[i] = 0;
+}
+
+// One workgroup's share of the routing: tokens wg * groups, (wg + nwg) * groups, ...
+// L lanes per token, MMAX >= ceil(E / L) logits per lane; hist [E_loc] in LDS
+// collects this workgroup's local-expert counts.
+template <int L, int MMAX>
+__device__ __forceinline__ void route_block(const float* __restrict__ logits, int32_t* __restrict__ ids,
+                                            float* __restrict__ wout, int32_t* hist, int B, int E,
+                                            int k, int e0, int E_loc, int renormalize, int wg,
+                                            int nwg) {
+  for (int i = threadIdx.x; i < E_loc; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gl = lane & (L - 1);  // lane inside the token group
+  const int groups_per_wg = blockDim.x / L;
+  const int group = threadIdx.x / L;
+  const int M = (E + L - 1) / L;
+
+  for (int t0 = wg * groups_per_wg; t0 < B; t0 += nwg * groups_per_wg) {
+    const int t = t0 + group;
+    const bool active = t < B;  // whole groups are inactive together
+    uint64_t key[MMAX];
+    const float* lrow = logits + (int64_t)(active ? t : 0) * E;
+#pragma unroll
+    for (int i = 0; i < MMAX; ++i) {
+      const int e = gl + i * L;
+      key[i] = 0;
+      if (active && i < M && e < E)
+        key[i] = ((uint64_t)float_order_key(lrow[e]) << 32) | (uint32_t)(~(uint32_t)e);
+    }
+    int my_id = -1;
+    float my_logit = 0.f;
+    float top = 0.f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < MMAX; ++i) best = key[i] > best ? key[i] : best;
+      best = group_max_u64<L>(best);
+      const int e = (int)(~(uint32_t)best);
+      const float lv = order_key_float((uint32_t)(best >> 32));
+      if (j == 0) top = lv;
+      if (gl == j) {
+        my_id = e;
+        my_logit = lv;
+      }
+      if ((e & (L - 1)) == gl) {
+        const int slot = e / L;
+#pragma unroll
+        for (int i = 0; i < MMAX; ++i)
+          if (i == slot) key[i] = 0;
+      }
+    }
+    // weights
+    float ex = (gl < k) ? expf(my_logit - top) : 0.f;
+    float den;
+    if (renormalize) {
+      den = group_sum_f32<L>(ex);
+    } else {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < MMAX; ++i) {
+        const int e = gl + i * L;
+        if (active && i < M && e < E) part += expf(lrow[e] - top);
+      }
+      den = group_sum_f32<L>(part);
+    }
+    if (active && gl < k) {
+      ids[(int64_t)t * k + gl] = my_id;
+      wout[(int64_t)t * k + gl] = ex / den;
+      const int le = my_id - e0;
+      if (le >= 0 && le < E_loc) atomicAdd(&hist[le], 1);
+    }
+  }
+  __syncthreads();
+}
+
+template <int L, int MMAX>
+__global__ void __launch_bounds__(1024) route_topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
+                                  float* __restrict__ wout, int32_t* __restrict__ counts, int B,
+                                  int E, int k, int e0, int E_loc, int renormalize,
+                                  int single_wg) {
+  extern __shared__ int32_t hist[];  // [E_loc]
+  route_block<L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, blockIdx.x,
+                       gridDim.x);
+  if (single_wg) {
+    for (int i = threadIdx.x; i < E_loc; i += blockDim.x) counts[i] = hist[i];
+  } else {
+    for (int i = threadIdx.x; i < E_loc; i += blockDim.x)
+      if (hist[i]) atomicAdd(&counts[i], hist[i]);
+  }
+}
+
+template <int L, int MMAX>
+hipError_t launch_lm(const moe_problem& p, const float* logits, int32_t* ids, float* w,
+                     int32_t* counts, hipStream_t s) {
+  const int B = p.tokens;
+  // one 1024-thread workgroup for small batches (no zeroing launch needed),
+  // otherwise 256-thread workgroups over the token range
+  const int groups_single = 1024 / L;
+  const bool single = B <= 4 * groups_single;
+  const int threads = single ? 1024 : 256;
+  int grid = 1;
+  if (!single) {
+    const int groups = threads / L;
+    grid = (B + groups - 1) / groups;
+    if (grid > 4096) grid = 4096;
+    zero_counts_kernel<<<(p.local_experts + 255) / 256, 256, 0, s>>>(counts, p.local_experts);
+  }
+  route_topk_kernel<L, MMAX><<<grid, threads, p.local_experts * sizeof(int32_t), s>>>(
+      logits, ids, w, counts, B, p.num_experts, p.top_k, p.expert_begin, p.local_experts,
+      p.renormalize, single ? 1 : 0);
+  return hipGetLastError();
+}
+
+
+
+// The selection by one workgroup (one wave per configuration, as many waves as the
+// block has): counts may be in global memory or LDS.  Returns the chosen index to
+// every thread.
+__device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
+                                            const float* __restrict__ theta, const CostTable& tab,
+                                            int32_t* __restrict__ variant,
+                                            float* __restrict__ t_hat) {
+  __shared__ float tv[kNumVariants];
+  __shared__ int active;
+  __shared__ int chosen;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  if (threadIdx.x == 0) active = 0;
+  __syncthreads();
+  if (wave == 0) {
+    int a = 0;
+    for (int e = lane; e < E_loc; e += kWave) a += counts[e] > 0;
+    for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m, kWave);
+    if (lane == 0) active = a;
+  }
+  __syncthreads();
+  for (int v = wave; v < kNumVariants; v += nwaves) {
+    const int b = tab.b[v];
+    int rt = 0;
+    for (int e = lane; e < E_loc; e += kWave) rt += (counts[e] + b - 1) / b;
+    for (int m = 32; m >= 1; m >>= 1) rt += __shfl_xor(rt, m, kWave);
+    if (lane == 0) {
+      const int T1 = tab.q1[v] * rt, T2 = tab.q2[v] * rt;
+      const int W = (T1 + tab.S1[v] - 1) / tab.S1[v] + (T2 + tab.S2[v] - 1) / tab.S2[v];
+      const int T = T1 + T2;
+      const float* th = theta + 4 * v;
+      const float t = __builtin_fmaf(
+          th[3], (float)active, __builtin_fmaf(th[2], (float)T, __builtin_fmaf(th[1], (float)W, th[0])));
+      tv[v] = t;
+      if (t_hat) t_hat[v] = t;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int best = 0;
+    for (int v = 1; v < kNumVariants; ++v)
+      if (tv[v] < tv[best]) best = v;
+    *variant = best;
+    chosen = best;
+  }
+  __syncthreads();
+  return chosen;
+}
+
+__global__ void select_config_kernel(const int32_t* __restrict__ counts, int E_loc,
+                                     const float* __restrict__ theta, CostTable tab,
+                                     int32_t* __restrict__ variant, float* __restrict__ t_hat) {
+  select_block(counts, E_loc, theta, tab, variant, t_hat);
+}
+
+
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+
+__device__ __forceinline__ void build_masks(unsigned long long* masks, const int32_t* ids, int blk,
+                                            int B, int k, int e0, int E_loc, int lane) {
+  for (int e = lane; e < E_loc; e += kWave) masks[e] = 0ull;
+  __builtin_amdgcn_wave_barrier();
+  const int t = blk * kWave + lane;
+  if (t < B) {
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(int64_t)t * k + j] - e0;
+      if (e >= 0 && e < E_loc) atomicOr(&masks[e], 1ull << lane);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The alignment by one workgroup of kAlignThreads threads for tile rows b (b = 0:
+// no valid configuration, so no tiles and no local slots); lds_u64 holds
+// align_lds_bytes(B, E_loc) bytes.
+__device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int b, int B, int k,
+                                            int e0, int E_loc, int32_t* __restrict__ sorted_slots,
+                                            int32_t* __restrict__ block_expert,
+                                            int32_t* __restrict__ num_blocks,
+                                            int32_t* __restrict__ slot_pos,
+                                            unsigned long long* lds_u64) {
+  const int nblk = (B + kWave - 1) / kWave;
+  unsigned long long* masks_all = lds_u64;                              // [16][E_loc]
+  int32_t* base = (int32_t*)(lds_u64 + (size_t)kAlignWaves * E_loc);     // [nblk][E_loc]
+  int32_t* off = base + (size_t)nblk * E_loc;                           // [E_loc + 1]
+  int32_t* tot = off + E_loc + 1;                                       // [E_loc]
+  __shared__ int wave_tot[kAlignWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  unsigned long long* masks = masks_all + (size_t)wave * E_loc;
+
+  if (b == 0) {  // configuration index out of range: no tiles, no local slots
+    for (int64_t s = tid; s < (int64_t)B * k; s += kAlignThreads) slot_pos[s] = -1;
+    if (tid == 0) *num_blocks = 0;
+    return;
+  }
+
+  // pass 1: per-(block, expert) counts
+  for (int blk = wave; blk < nblk; blk += kAlignWaves) {
+    build_masks(masks, ids, blk, B, k, e0, E_loc, lane);
+    for (int e = lane; e < E_loc; e += kWave)
+      base[(size_t)blk * E_loc + e] = __popcll(masks[e]);
+  }
+  __syncthreads();
+
+  // pass 2: per expert (one thread each, E_loc <= 1024): exclusive prefix over
+  // blocks, the padded size, then an exclusive scan of padded sizes over experts
+  {
+    const int e = tid;
+    int padded = 0;
+    if (e < E_loc) {
+      int run = 0;
+      for (int blk = 0; blk < nblk; ++blk) {
+        const int c = base[(size_t)blk * E_loc + e];
+        base[(size_t)blk * E_loc + e] = run;
+        run += c;
+      }
+      tot[e] = run;
+      padded = (run + b - 1) / b * b;
+    }
+    int incl = padded;  // wave-inclusive scan
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int o = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += o;
+    }
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+      int wt = lane < kAlignWaves ? wave_tot[lane] : 0;
+      for (int d = 1; d < kAlignWaves; d <<= 1) {
+        const int o = __shfl_up(wt, d, kWave);
+        if (lane >= d) wt += o;
+      }
+      if (lane < kAlignWaves) wave_tot[lane] = wt;  // inclusive over waves
+    }
+    __syncthreads();
+    const int before = (wave == 0 ? 0 : wave_tot[wave - 1]) + incl - padded;
+    if (e < E_loc) off[e] = before;
+    if (e == E_loc - 1) off[E_loc] = before + padded;
+  }
+  __syncthreads();
+  for (int i = tid; i < nblk * E_loc; i += kAlignThreads) base[i] += off[i % E_loc];
+  const int R = off[E_loc];
+  const int nb = R / b;
+  if (tid == 0) *num_blocks = nb;
+
+  // pass 3: padding rows [off[e] + n_e, off[e + 1]) and the block -> expert table
+  if (tid < E_loc)
+    for (int r = off[tid] + tot[tid]; r < off[tid + 1]; ++r) sorted_slots[r] = -1;
+  for (int i = tid; i < nb; i += kAlignThreads) {
+    const int row = i * b;
+    int lo = 0, hi = E_loc - 1;  // the largest e with off[e] <= row
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    block_expert[i] = lo;
+  }
+  __syncthreads();
+
+  // pass 4: stable scatter
+  for (int blk = wave; blk < nblk; blk += kAlignWaves) {
+    build_masks(masks, ids, blk, B, k, e0, E_loc, lane);
+    const int t = blk * kWave + lane;
+    if (t < B) {
+      const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+      for (int j = 0; j < k; ++j) {
+        const int64_t s = (int64_t)t * k + j;
+        const int e = ids[s] - e0;
+        if (e >= 0 && e < E_loc) {
+          const int pos = base[(size_t)blk * E_loc + e] + __popcll(masks[e] & below);
+          sorted_slots[pos] = (int32_t)s;
+          slot_pos[s] = pos;
+        } else {
+          slot_pos[s] = -1;
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int tile_rows(int v) {
+  return (v >= 0 && v < kNumVariants) ? kVariants[v].bm : 0;
+}
+
+__global__ void __launch_bounds__(kAlignThreads)
+align_sort_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ variant, int B,
+                  int k, int e0, int E_loc, int32_t* __restrict__ sorted_slots,
+                  int32_t* __restrict__ block_expert, int32_t* __restrict__ num_blocks,
+                  int32_t* __restrict__ slot_pos) {
+  extern __shared__ unsigned long long lds_u64[];
+  __shared__ int s_b;
+  if (threadIdx.x == 0) s_b = tile_rows(*variant);
+  __syncthreads();
+  align_block(ids, s_b, B, k, e0, E_loc, sorted_slots, block_expert, num_blocks, slot_pos, lds_u64);
+}
+
+
+// ---- fused steps 1-3 ----
+
+// The configuration in *variant, to every thread (theta == NULL: no selection).
+__device__ __forceinline__ int given_variant(const int32_t* variant) {
+  __shared__ int sv;
+  if (threadIdx.x == 0) sv = *variant;
+  __syncthreads();
+  return sv;
+}
+
+// Steps 1-3 in one workgroup of 1024 threads, for a batch one workgroup routes:
+// the routing with the histogram in LDS, the counts, the choice from the LDS
+// counts (or the given configuration), then the alignment for the chosen tile
+// rows.  The alignment reads the ids this workgroup wrote; the barriers in
+// between order those accesses.
+template <int L, int MMAX>
+__global__ void __launch_bounds__(1024)
+route_select_align_kernel(const float* __restrict__ logits, const float* __restrict__ theta,
+                          CostTable tab, int32_t* __restrict__ ids, float* __restrict__ wout,
+                          int32_t* __restrict__ counts, int32_t* __restrict__ variant,
+                          float* __restrict__ t_hat, int32_t* __restrict__ sorted_slots,
+                          int32_t* __restrict__ block_expert, int32_t* __restrict__ num_blocks,
+                          int32_t* __restrict__ slot_pos, int B, int E, int k, int e0, int E_loc,
+                          int renormalize) {
+  extern __shared__ unsigned long long lds_u64[];
+  int32_t* hist = (int32_t*)lds_u64;  // [E_loc], then the alignment's tables
+  route_block<L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, 0, 1);
+  for (int i = threadIdx.x; i < E_loc; i += blockDim.x) counts[i] = hist[i];
+  const int v = theta ? select_block(hist, E_loc, theta, tab, variant, t_hat) : given_variant(variant);
+  align_block(ids, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
+              slot_pos, lds_u64 + (E_loc + 1) / 2);
+}
+
+// Steps 2-3 in one workgroup, after a multi-workgroup routing launch.
+__global__ void __launch_bounds__(kAlignThreads)
+select_align_kernel(const int32_t* __restrict__ counts, const float* __restrict__ theta,
+                    CostTable tab, const int32_t* __restrict__ ids, int32_t* __restrict__ variant,
+                    float* __restrict__ t_hat, int32_t* __restrict__ sorted_slots,
+                    int32_t* __restrict__ block_expert, int32_t* __restrict__ num_blocks,
+                    int32_t* __restrict__ slot_pos, int B, int k, int e0, int E_loc) {
+  extern __shared__ unsigned long long lds_u64[];
+  const int v = theta ? select_block(counts, E_loc, theta, tab, variant, t_hat) : given_variant(variant);
+  align_block(ids, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
+              slot_pos, lds_u64);
+}
+
+// more than 64 KiB of dynamic LDS needs an opt-in (gfx950 has 160 KiB per CU)
+hipError_t allow_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int L, int MMAX>
+hipError_t launch_rsa(const moe_problem& p, const float* logits, const float* theta,
+                      const CostTable& tab, int32_t* ids, float* w, int32_t* counts,
+                      int32_t* variant, float* t_hat, int32_t* sorted_slots,
+                      int32_t* block_expert, int32_t* num_blocks, int32_t* slot_pos,
+                      hipStream_t s) {
+  const int B = p.tokens;
+  const size_t al_bytes = align_lds_bytes(B, p.local_experts);
+  const size_t fused_bytes = (size_t)(p.local_experts + 1) / 2 * 8 + al_bytes;
+  if (B <= 4 * (1024 / L) && fused_bytes <= 150 * 1024) {
+    const void* fn = (const void*)route_select_align_kernel<L, MMAX>;
+    hipError_t e = allow_lds(fn, fused_bytes);
+    if (e != hipSuccess) return e;
+    route_select_align_kernel<L, MMAX><<<1, 1024, fused_bytes, s>>>(
+        logits, theta, tab, ids, w, counts, variant, t_hat, sorted_slots, block_expert,
+        num_blocks, slot_pos, B, p.num_experts, p.top_k, p.expert_begin, p.local_experts,
+        p.renormalize);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_lm<L, MMAX>(p, logits, ids, w, counts, s);
+  if (e != hipSuccess) return e;
+  e = allow_lds((const void*)select_align_kernel, al_bytes);
+  if (e != hipSuccess) return e;
+  select_align_kernel<<<1, kAlignThreads, al_bytes, s>>>(counts, theta, tab, ids, variant, t_hat,
+                                                         sorted_slots, block_expert, num_blocks,
+                                                         slot_pos, B, p.top_k, p.expert_begin,
+                                                         p.local_experts);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const moe_problem& p, const float* logits, int32_t* ids, float* w,
+                             int32_t* counts, hipStream_t s) {
+  const int E = p.num_experts;
+  if (E <= 8) return launch_lm<8, 1>(p, logits, ids, w, counts, s);
+  if (E <= 16) return launch_lm<16, 1>(p, logits, ids, w, counts, s);
+  if (E <= 32) return launch_lm<32, 1>(p, logits, ids, w, counts, s);
+  if (E <= 64) return launch_lm<64, 1>(p, logits, ids, w, counts, s);
+  if (E <= 128) return launch_lm<64, 2>(p, logits, ids, w, counts, s);
+  if (E <= 256) return launch_lm<64, 4>(p, logits, ids, w, counts, s);
+  if (E <= 512) return launch_lm<64, 8>(p, logits, ids, w, counts, s);
+  if (E <= 1024) return launch_lm<64, 16>(p, logits, ids, w, counts, s);
+  return launch_lm<64, 64>(p, logits, ids, w, counts, s);
+}
+
+
+hipError_t launch_select_config(const moe_problem& p, const int32_t* counts, const float* theta,
+                                const CostTable& tab, int32_t* variant, float* t_hat,
+                                hipStream_t s) {
+  const int threads = kWave * (kNumVariants < 16 ? kNumVariants : 16);
+  select_config_kernel<<<1, threads, 0, s>>>(counts, p.local_experts, theta, tab, variant, t_hat);
+  return hipGetLastError();
+}
+
+
+size_t align_lds_bytes(int B, int E_loc) {
+  const size_t nblk = (size_t)(B + kWave - 1) / kWave;
+  return (size_t)kAlignWaves * E_loc * 8 + nblk * E_loc * 4 + (size_t)(2 * E_loc + 1) * 4;
+}
+
+hipError_t launch_align_sort(const moe_problem& p, const int32_t* ids, const int32_t* variant,
+                             int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
+                             int32_t* slot_pos, hipStream_t s) {
+  const size_t lds = align_lds_bytes(p.tokens, p.local_experts);
+  if (lds > 64 * 1024) {
+    // opt in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
+    static int done[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !done[dev]) {
+      if (hipFuncSetAttribute((const void*)align_sort_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess)
+        done[dev] = 1;
+      else
+        (void)hipGetLastError();
+    }
+  }
+  align_sort_kernel<<<1, kAlignThreads, lds, s>>>(ids, variant, p.tokens, p.top_k, p.expert_begin,
+                                                  p.local_experts, sorted_slots, block_expert,
+                                                  num_blocks, slot_pos);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_route_select_align(const moe_problem& p, const float* logits,
+                                     const float* theta, const CostTable& tab, int32_t* ids,
+                                     float* w, int32_t* counts, int32_t* variant, float* t_hat,
+                                     int32_t* sorted_slots, int32_t* block_expert,
+                                     int32_t* num_blocks, int32_t* slot_pos, hipStream_t s) {
+#define MOE_RSA(L, M) \
+  launch_rsa<L, M>(p, logits, theta, tab, ids, w, counts, variant, t_hat, sorted_slots, \
+                   block_expert, num_blocks, slot_pos, s)
+  const int E = p.num_experts;
+  if (E <= 8) return MOE_RSA(8, 1);
+  if (E <= 16) return MOE_RSA(16, 1);
+  if (E <= 32) return MOE_RSA(32, 1);
+  if (E <= 64) return MOE_RSA(64, 1);
+  if (E <= 128) return MOE_RSA(64, 2);
+  if (E <= 256) return MOE_RSA(64, 4);
+  if (E <= 512) return MOE_RSA(64, 8);
+  if (E <= 1024) return MOE_RSA(64, 16);
+  return MOE_RSA(64, 64);
+#undef MOE_RSA
+}
+
+}  // namespace moe

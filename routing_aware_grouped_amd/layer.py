@@ -1,9 +1,10 @@
 """Device buffers for one fused-MoE problem and the five library calls in order.
 
 Holds no arithmetic of its own: torch allocates device memory, and `forward`
-enqueues moe_route_topk -> moe_select_config -> moe_align_sort ->
-moe_grouped_ffn -> moe_combine on one stream, with no host synchronisation, so a
-caller may capture it in a HIP graph.
+enqueues moe_route_select_align (routing, configuration choice and alignment
+fused) -> moe_grouped_ffn -> moe_combine on one stream, with no host
+synchronisation, so a caller may capture it in a HIP graph.  The separate step
+calls (route, select, align) remain for tests and per-step timing.
 """
 from __future__ import annotations
 
@@ -13,7 +14,7 @@ import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_grouped_down,
                moe_grouped_ffn, moe_grouped_gate_up, moe_num_variants, moe_problem,
-               moe_query_sizes, moe_route_topk, moe_select_config)
+               moe_query_sizes, moe_route_select_align, moe_route_topk, moe_select_config)
 
 _TORCH_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
@@ -90,6 +91,13 @@ def align(b: Buffers, stream=None):
                    b.slot_pos, stream)
 
 
+def route_select_align(b: Buffers, stream=None, forced_variant: bool = False):
+    """Steps 1-3 fused; with forced_variant the configuration in b.variant is kept."""
+    moe_route_select_align(b.p, b.logits, None if forced_variant else b.theta, b.topk_ids,
+                           b.topk_w, b.counts, b.variant, b.t_hat, b.sorted_slots,
+                           b.block_expert, b.num_blocks, b.slot_pos, stream)
+
+
 def ffn(b: Buffers, stream=None):
     moe_grouped_ffn(b.p, b.x, b.w1, b.w3, b.w2, b.s1, b.s3, b.s2, b.sorted_slots, b.block_expert,
                     b.num_blocks, b.variant, b.y_slots, b.workspace, None, stream)
@@ -112,6 +120,13 @@ def combine(b: Buffers, stream=None):
 def forward(b: Buffers, stream=None, forced_variant: bool = False):
     """The whole layer.  With forced_variant the select step is skipped and the
     value already in b.variant is used (exhaustive timing of every configuration)."""
+    route_select_align(b, stream, forced_variant)
+    ffn(b, stream)
+    combine(b, stream)
+
+
+def forward_steps(b: Buffers, stream=None, forced_variant: bool = False):
+    """The whole layer through the five separate step calls."""
     route(b, stream)
     if not forced_variant:
         select(b, stream)

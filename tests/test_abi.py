@@ -103,6 +103,14 @@ def test_compute_calls_validate_before_any_gpu_work():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_align_sort(p, 0x1000, 0x1000, 0, 0x1000, 0x1000, 0x1000, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # the fused steps need slot_pos
+        moe.moe_route_select_align(p, 0x1000, None, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000,
+                                   0x1000, 0x1000, 0, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # logits misaligned
+        moe.moe_route_select_align(p, 0x1002, None, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000,
+                                   0x1000, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_combine(p, 0x1000, 0x1000, 0x1000, 0x1004, stream=0)  # y misaligned
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG

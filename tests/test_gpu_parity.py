@@ -85,6 +85,57 @@ def test_routing_and_permutation_full_batch(shape, B, alpha):
         G.check_align(lay, out, ids)
 
 
+@pytest.mark.parametrize("shape,B,alpha", [
+    ("mixtral", 1, 1.0), ("mixtral", 512, 0.1), ("mixtral", 513, 0.1), ("mixtral", 2048, 1.0),
+    ("qwen3", 64, 0.3), ("qwen3", 65, 0.3), ("qwen3", 4096, 1.0), ("dsv3_share", 96, 0.1),
+    ("kimi_share", 2048, 0.05)])
+def test_fused_selection_matches_steps(shape, B, alpha):
+    """moe_route_select_align (one launch for a batch one workgroup routes, else
+    the routing launches and one select+align workgroup) writes exactly what
+    moe_route_topk, moe_select_config and moe_align_sort write, with a chosen and
+    with a given configuration."""
+    G.say(f"fused selection {shape} B={B} alpha={alpha}")
+    sh = synth.SHAPES[shape]
+    logits, p = synth.routing_logits(sh, B, alpha, np.random.default_rng([B, 9]))
+    e0 = synth.most_loaded_block(p, sh)
+    H, I = 256, 256
+    p_ = L.moe_problem(B, H, I, sh.num_experts, e0, sh.local_experts, sh.top_k, synth.BF16,
+                       synth.BF16, 1)
+    z = torch.zeros
+    w1 = z(sh.local_experts, I, H, dtype=torch.bfloat16)
+    w2 = z(sh.local_experts, H, I, dtype=torch.bfloat16)
+    th = torch.tensor([[50.0 * v, 0.5 * v + 1.0, 0.01, 0.1] for v in range(V)], dtype=torch.float32)
+    names = ["topk_ids", "topk_w", "counts", "variant", "t_hat", "num_blocks", "slot_pos"]
+    for forced in (False, True):
+        bs = []
+        for fused in (False, True):
+            b = L.allocate(p_, torch.from_numpy(logits), z(B, H, dtype=torch.bfloat16), w1, w1, w2,
+                           theta=th)
+            b.variant.fill_(V - 1)
+            b.t_hat.fill_(-1.0)
+            b.sorted_slots.fill_(-7)
+            b.block_expert.fill_(-7)
+            if fused:
+                L.route_select_align(b, forced_variant=forced)
+            else:
+                L.route(b)
+                if not forced:
+                    L.select(b)
+                L.align(b)
+            bs.append(b)
+        torch.cuda.synchronize()
+        a, f = bs
+        for n in names:
+            x, y = getattr(a, n), getattr(f, n)
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (n, forced)
+        nb = int(a.num_blocks.item())
+        R = nb * spec.MENU[int(a.variant.item())][0]
+        assert torch.equal(a.sorted_slots[:R], f.sorted_slots[:R]) and torch.equal(
+            a.block_expert[:nb], f.block_expert[:nb]), forced
+        if forced:
+            assert int(f.variant.item()) == V - 1 and torch.all(f.t_hat == -1.0)
+
+
 def test_routing_ties_and_signed_zeros():
     """Equal logits go to the lower expert index; -0 equals +0."""
     rng = np.random.default_rng(44)
