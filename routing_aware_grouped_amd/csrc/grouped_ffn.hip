@@ -372,8 +372,11 @@ struct Tile {
         const int sl = m[row];
         l_aoff[i] = -1;
         if (l_eok && sl >= 0 && sl < g.slots) {
-          const int64_t arow = PHASE == 1 ? (int64_t)(sl / g.k) : (int64_t)rb * BM + row;
-          l_aoff[i] = (int)(arow * K) + c * EPC_A;
+          // 32-bit: the host rejects problems whose row offsets reach 2^31, so rows
+          // and K are below 2^24 and a 24-bit multiply is exact (a 64-bit
+          // multiply-add would clobber a register of an in-flight load)
+          const int arow = PHASE == 1 ? sl / g.k : rb * BM + row;
+          l_aoff[i] = (int)__umul24((unsigned)arow, (unsigned)K) + c * EPC_A;
         }
       }
     };
