@@ -543,18 +543,8 @@ hipError_t launch_align_sort(const moe_problem& p, const int32_t* ids, const int
                              int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
                              int32_t* slot_pos, hipStream_t s) {
   const size_t lds = align_lds_bytes(p.tokens, p.local_experts);
-  if (lds > 64 * 1024) {
-    // opt in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-    static int done[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !done[dev]) {
-      if (hipFuncSetAttribute((const void*)align_sort_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess)
-        done[dev] = 1;
-      else
-        (void)hipGetLastError();
-    }
-  }
+  hipError_t e = allow_lds((const void*)align_sort_kernel, lds);
+  if (e != hipSuccess) return e;
   align_sort_kernel<<<1, kAlignThreads, lds, s>>>(ids, variant, p.tokens, p.top_k, p.expert_begin,
                                                   p.local_experts, sorted_slots, block_expert,
                                                   num_blocks, slot_pos);
