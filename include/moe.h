@@ -101,6 +101,12 @@ typedef struct moe_sizes {
 /* Version of this ABI (bumped on any incompatible change). */
 int32_t moe_abi_version(void);
 
+/* Shape limits (MOE_ERR_UNSUPPORTED beyond them): B * k < 2^30; the grouped
+ * FFN reads x (B * H), h (rows_max * I) and one expert's weight matrix (I * H)
+ * through 32-bit buffer offsets, so each of these is below 2^31 bytes, and
+ * rows_max * max(H, I) elements of y_slots are below 2^31 bytes too; the
+ * alignment step's tables fit one workgroup's LDS. */
+
 /* Fills *out for problem *p.  Errors: MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED
  * with the same rules as the compute calls. */
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out);

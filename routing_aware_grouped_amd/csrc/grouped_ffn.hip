@@ -20,10 +20,11 @@
 // phase needs every column of h for its row-block, and a dependency between
 // workgroups of one launch would need a wait); each launch is persistent
 // (compute units x kWgPerCu workgroups) and deals its tiles out statically:
-// tile t = rb + nb * nt (row-block fastest, so the row-blocks of one expert that
-// share a weight slab are adjacent) goes to slot t mod G, and slots are numbered
-// so that G / 8 consecutive ones sit on one XCD (the hardware deals workgroup ids
-// round-robin over the 8 XCDs, each with its own L2).  There are no atomics and
+// tiles are numbered in chunks of 16 column tiles, row-block slowest inside a
+// chunk (Tile::tile_rc), tile t goes to slot t mod G, and slots are numbered so
+// that G / 8 consecutive ones sit on one XCD (the hardware deals workgroup ids
+// round-robin over the 8 XCDs, each with its own L2): the tiles that run together
+// on one XCD share a few row-blocks of token rows and many weight slices.  There are no atomics and
 // no waits between workgroups; every loop has a static bound.
 //
 // Data movement.  Each pipeline stage covers BK elements of the reduction for the
@@ -93,6 +94,16 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<true>& a, const Frag<
   for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[c], b.lo[c], acc, 0, 0, 0);
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[c], b.hi[c], acc, 0, 0, 0);
+}
+
+// Buffer resource of `bytes` bytes from `base` for untyped buffer loads (the last
+// descriptor word selects 32-bit data, as gfx9-family untyped loads need).  A load
+// whose offset is at or past `bytes` returns zeros and touches no memory; kOob is
+// past every range the host allows (each operand buffer is below 2^31 bytes).
+constexpr uint32_t kOob = 0x80000000u;
+constexpr int kCacheNt = 2;  // cache-policy operand of a buffer load: non-temporal
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // LDS row swizzle in 16-byte units: lanes reading one 16-byte column of 16
@@ -211,6 +222,7 @@ struct Tile {
   static_assert(KSTEPS % WK == 0, "K-split waves must divide the stage");
   static_assert(!FP8 || GCB * 2 == C, "fp8 chunk pairs");
   static_assert(GA % kThreads == 0 && GB % kThreads == 0, "every thread owns whole chunks");
+  static_assert((BN * GCB) % kThreads == 0, "each weight load instruction reads one matrix");
   static_assert(WM * WN * NFRAG * 256 == PIECE && PIECE <= kPieceMax, "partial tile layout");
 
   struct Regs {
@@ -249,6 +261,29 @@ struct Tile {
       }
   }
 
+  // Tile t of a phase -> row-block rb and column tile nt.  Column tiles come in
+  // chunks of kChunk; a chunk holds every row-block's tiles of its columns, the
+  // row-block changing slowest.  The G / 8 consecutive tiles that run together on
+  // one XCD then cover a few row-blocks (usually of one expert) times many column
+  // tiles, so that XCD's L2 serves each token row and each weight slice to many
+  // workgroups.
+  static constexpr int kChunk = 16;
+  __device__ __forceinline__ static void tile_rc(int t, int nb, int NT, int& rb, int& nt) {
+    const int full = NT / kChunk;
+    const int cs = nb * kChunk;
+    const int c = t / cs;
+    if (c < full) {
+      const int l = t - c * cs;
+      rb = l / kChunk;
+      nt = c * kChunk + l % kChunk;
+    } else {  // the last, narrower chunk (t past the last tile: any finite result)
+      const int w = NT > full * kChunk ? NT - full * kChunk : kChunk;
+      const int l = t - full * cs;
+      rb = l / w;
+      nt = full * kChunk + l % w;
+    }
+  }
+
   // Whether the r tail tiles of a phase are split across all G workgroups.  A
   // last round in which at least half of the workgroups stream weights still runs
   // near the HBM rate, so streaming configurations split only smaller tails; the
@@ -258,9 +293,8 @@ struct Tile {
   }
 
   // Runs the work of workgroup slot `slot` of `G` (hybrid Stream-K).  The phase's
-  // tiles t = rb + nb * nt come in F = total / G full rounds, dealt round-robin
-  // (tiles slot, slot + G, ...), so the row-blocks that share a weight slab run at
-  // the same time on one XCD.  The r = total - F * G tiles left over would leave
+  // tiles (numbered by tile_rc) come in F = total / G full rounds, dealt
+  // round-robin (tiles slot, slot + G, ...).  The r = total - F * G tiles left over would leave
   // most workgroups idle in a last round; when split_tail says so, their r * nst
   // reduction stages are cut into G equal contiguous ranges, one per workgroup, so
   // every workgroup streams the same number of stages to within one (otherwise
@@ -317,8 +351,8 @@ struct Tile {
     // drains the stage loads issued in between.
     int ms0 = -1, ms1 = -1, me = -1;
     auto fetch_meta = [&](int j) __attribute__((always_inline)) {
-      const int t = item_tile(j);
-      const int rb = t % nb;
+      int rb, nt;
+      tile_rc(item_tile(j), nb, N / BN, rb, nt);
       const int64_t row0 = (int64_t)rb * BM;
       if (tid < BM) {
         ms0 = g.sorted_slots[row0 + tid];
@@ -339,44 +373,60 @@ struct Tile {
     };
 
     // ---- one stage: global -> registers, registers -> LDS ----
-    // Both steps are branch-free, so the compiler can count the loads in flight
-    // exactly and each stage waits only for its own data.  A chunk that holds no
-    // operand (a padding row, columns beyond K, a tile past the workgroup's last)
-    // is still loaded, from a valid fallback address, and still written: padding
-    // rows of A only reach output rows that are never stored, reduction steps
-    // beyond K are never computed, and a missing tile is never computed.
+    // Operands are read with buffer loads: a 32-bit per-lane offset that stays
+    // fixed for a tile, plus the stage's reduction offset as a scalar, so a stage
+    // costs no address arithmetic.  A chunk that holds no operand (a padding row,
+    // columns beyond K, a tile past the workgroup's last) gets an offset past the
+    // buffer's range, and the hardware returns zeros for it without a memory
+    // access: padding rows of A only reach output rows that are never stored,
+    // zeros beyond K add nothing, and a missing tile is never computed.  Loads and LDS writes are branch-free, so the compiler can count
+    // the loads in flight exactly and each stage waits only for its own data.
     // The load cursor (l_j, l_s) is the tile and stage of the next load; the
-    // tile's row sources are computed once, when the cursor enters it.
+    // tile's row offsets and weight buffer are set once, when the cursor enters it.
     int l_j = 0, l_s = item_sb(0), l_se = item_se(0);
     bool l_new = true;  // the next load is the first of item l_j
-    int l_aoff[NA];  // element offset of each A chunk's row start (-1: no operand)
-    int64_t l_wrow0 = 0;
+    // A: the whole activation (x) or h buffer; byte offset of each chunk's row start
+    const uint32_t a_bytes = PHASE == 1 ? (uint32_t)(g.slots / g.k) * (uint32_t)K * ASZ
+                                        : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
+    uint32_t l_aoff[NA];
+    // weights: per tile, a buffer from row n0 of the tile's expert matrix to its
+    // end; each chunk's byte offset in it depends on the thread alone
+    __amdgpu_buffer_rsrc_t l_b_rsrc[NMAT];
+    uint32_t b_off[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = i * kThreads + tid;
+      const int row = (q / GCB) % BN;
+      b_off[i] = (uint32_t)(row * K + (q % GCB) * EPC_B) * WSZ;
+    }
     int l_n0 = 0, l_e = 0;
     bool l_eok = false;
     auto enter_load_tile = [&](int j) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
-      const int t = item_tile(j);
-      const int rb = t % nb;
-      l_n0 = (t / nb) * BN;
-      l_e = m[BM + 1];
+      int rb, nt;
+      tile_rc(item_tile(j), nb, N / BN, rb, nt);
+      l_n0 = nt * BN;
+      l_e = __builtin_amdgcn_readfirstlane(m[BM + 1]);
       l_eok = j < nitem && (unsigned)l_e < (unsigned)g.E_loc;
       if (!l_eok) {
         l_e = 0;
         l_n0 = 0;
       }
-      l_wrow0 = (int64_t)l_e * N + l_n0;
+      const int64_t wrow0 = ((int64_t)l_e * N + l_n0) * K;
+      const uint32_t wbytes = l_eok ? (uint32_t)(N - l_n0) * (uint32_t)K * WSZ : 0u;
+      l_b_rsrc[0] = make_rsrc(wmat0 + wrow0, wbytes);
+      if constexpr (NMAT == 2) l_b_rsrc[1] = make_rsrc(wmat1 + wrow0, wbytes);
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int q = i * kThreads + tid;
         const int row = q / GCA, c = q % GCA;
         const int sl = m[row];
-        l_aoff[i] = -1;
+        l_aoff[i] = kOob;
         if (l_eok && sl >= 0 && sl < g.slots) {
-          // 32-bit: the host rejects problems whose row offsets reach 2^31, so rows
-          // and K are below 2^24 and a 24-bit multiply is exact (a 64-bit
-          // multiply-add would clobber a register of an in-flight load)
+          // the host bounds every operand buffer below 2^31 bytes
           const int arow = PHASE == 1 ? sl / g.k : rb * BM + row;
-          l_aoff[i] = (int)__umul24((unsigned)arow, (unsigned)K) + c * EPC_A;
+          l_aoff[i] = (uint32_t)(arow * K + c * EPC_A) * ASZ;
         }
       }
     };
@@ -384,28 +434,26 @@ struct Tile {
       if (l_new) enter_load_tile(l_j);
       l_new = false;
       const int k0 = l_s * BK;
+      const int kl = K - k0;  // reduction elements left from this stage on
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int q = i * kThreads + tid;
-        const int kel = (q % GCA) * EPC_A;
-        const bool ok = l_aoff[i] >= 0 && k0 + kel < K;
-        R.a[i] = *(const u32x4*)(abase + (ok ? (int64_t)l_aoff[i] + k0 : 0));
+        const int kel = ((i * kThreads + tid) % GCA) * EPC_A;
+        R.a[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, kel < kl ? l_aoff[i] : kOob, k0 * ASZ, 0));
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int q = i * kThreads + tid;
-        const int mt = q / (BN * GCB);
-        const int row = (q / GCB) % BN;
+        const int mt = i * kThreads / (BN * GCB);  // one matrix per load instruction (tid < kThreads)
         const int kel = (q % GCB) * EPC_B;
-        const bool ok = l_eok && k0 + kel < K;
-        const Wt* wm_ = mt == 0 ? wmat0 : wmat1;
-        const u32x4* src = (const u32x4*)(wm_ + (ok ? (l_wrow0 + row) * K + k0 + kel : 0));
-        if constexpr (STREAM)
-          R.b[i] = __builtin_nontemporal_load(src);
-        else
-          R.b[i] = *src;
+        // non-temporal loads (cache policy nt) stream weights that no other tile reads
+        R.b[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(l_b_rsrc[mt], kel < kl ? b_off[i] : kOob,
+                                                         k0 * WSZ, STREAM ? kCacheNt : 0));
         if constexpr (FP8) {
+          const int row = (q / GCB) % BN;
           const float* sm = mt == 0 ? smat0 : smat1;
+          const bool ok = l_eok && kel < kl;
           R.s[i] = sm[ok ? ((int64_t)l_e * (N / 128) + (l_n0 + row) / 128) * (K / 128) + (k0 + kel) / 128 : 0];
         }
       }
@@ -457,11 +505,12 @@ struct Tile {
         f.v = __builtin_bit_cast(bf16x8, *(const u32x4*)(rp + ((c0 ^ sw) << 4)));
       }
     };
-    // 16-row groups with no routed slot are skipped (their rows are never stored).
-    // A stage whose rows are all live for this wave and that lies inside K takes a
-    // straight-line path (every fragment read and MFMA unconditional, so reads and
-    // MFMAs interleave freely); only the last row-block of an expert and the last
-    // stage of a ragged K take the guarded path.
+    // 16-row groups with no routed slot are skipped (their rows are never stored),
+    // and a wave with none skips the stage.  A wave whose rows all hold a slot
+    // takes a straight-line path (every fragment read and MFMA unconditional, so
+    // reads and MFMAs interleave freely); only the last row-block of an expert
+    // takes the guarded path.  Reduction steps beyond K need no guard: they were
+    // loaded as zeros and add nothing.
     auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int jj = 0; jj < KSTEPS / WK; ++jj) {
@@ -482,34 +531,32 @@ struct Tile {
             for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa[i], fb[mt][j]);
       }
     };
-    auto compute_stage = [&](const uint8_t* buf, int k0, int nvalid) __attribute__((always_inline)) {
+    auto compute_stage = [&](const uint8_t* buf, int nvalid) __attribute__((always_inline)) {
       if (wm * MW >= nvalid) return;
-      if (wm * MW + MW <= nvalid && k0 + BK <= K) {
+      if (wm * MW + MW <= nvalid) {
         compute_full(buf);
         return;
       }
 #pragma unroll
       for (int jj = 0; jj < KSTEPS / WK; ++jj) {
         const int step = jj * WK + wk;
-        if (k0 + step * 32 < K) {
-          Frag<F32> fa[FM];
-          Frag<F32> fb[NMAT][FN];
+        Frag<F32> fa[FM];
+        Frag<F32> fb[NMAT][FN];
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            if (wm * MW + i * 16 < nvalid) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
+        for (int i = 0; i < FM; ++i)
+          if (wm * MW + i * 16 < nvalid) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
 #pragma unroll
-          for (int mt = 0; mt < NMAT; ++mt)
+        for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
+          for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            if (wm * MW + i * 16 < nvalid) {
+        for (int i = 0; i < FM; ++i)
+          if (wm * MW + i * 16 < nvalid) {
 #pragma unroll
-              for (int mt = 0; mt < NMAT; ++mt)
+            for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa[i], fb[mt][j]);
-            }
-        }
+              for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa[i], fb[mt][j]);
+          }
       }
     };
 
@@ -517,9 +564,10 @@ struct Tile {
     // piece's fp32 sums to its slot of g.part ----
     auto epilogue = [&](int j, uint8_t* red_area, bool whole) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
-      const int t = item_tile(j);
-      const int64_t row0 = (int64_t)(t % nb) * BM;
-      const int n0 = (t / nb) * BN;
+      int rb, nt;
+      tile_rc(item_tile(j), nb, N / BN, rb, nt);
+      const int64_t row0 = (int64_t)rb * BM;
+      const int n0 = nt * BN;
       if ((unsigned)m[BM + 1] >= (unsigned)g.E_loc) return;  // uniform: no such tile
       if constexpr (WK > 1) {
         // waves wk > 0 hand their sums to wave wk = 0 through the LDS buffer just
@@ -591,19 +639,17 @@ struct Tile {
     for (int u = 0; u < RS; ++u)
       if (u < nv) load_stage(R[u]);
     int c_j = 0, c_s = item_sb(0), c_sb = c_s, c_se = item_se(0);  // item and stage being computed
-    for (int v0 = 0; v0 < nv; v0 += RS) {
-#pragma unroll
-      for (int u = 0; u < RS; ++u) {
-        const int v = v0 + u;
-        if (v < nv) {
+    // one pipeline step: stage v from registers Ru to LDS, the load of stage
+    // v + RS into Ru, the MFMAs of stage v
+    auto step = [&](const int v, Regs& Ru) __attribute__((always_inline)) {
           const int* m = meta3 + (c_j % kMetaSlots) * META;
           uint8_t* buf = lds + (v & 1) * STAGE;
-          write_stage(R[u], buf);
+          write_stage(Ru, buf);
           const bool more = v + RS < nv;  // a real load follows this step
           if (more && l_new && v >= 1) store_meta(l_j);
           if (v + RS + 1 < nv && l_s == l_se - 1) fetch_meta(l_j + 1);
           __syncthreads();
-          load_stage(R[u]);  // past the last stage it reads fallback addresses
+          load_stage(Ru);  // past the last stage its offsets are out of range
           if (c_s == c_sb) {
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt)
@@ -612,15 +658,23 @@ struct Tile {
 #pragma unroll
                 for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          if ((unsigned)m[BM + 1] < (unsigned)g.E_loc) compute_stage(buf, c_s * BK, m[BM]);
+          if ((unsigned)m[BM + 1] < (unsigned)g.E_loc) compute_stage(buf, m[BM]);
           if (c_s == c_se - 1) epilogue(c_j, buf, c_sb == 0 && c_se == nst);
           if (++c_s == c_se) {
             ++c_j;
             c_s = c_sb = item_sb(c_j);
             c_se = item_se(c_j);
           }
-        }
-      }
+    };
+    // The compiler's wait before each stage's LDS write also covers the younger
+    // register stage's loads (the steps are conditional), so about one stage of
+    // loads is in flight at that point.  Loops with exact waits (two stages in
+    // flight) measured slower on the cached large-tile configuration, and no
+    // faster elsewhere.
+    for (int v0 = 0; v0 < nv; v0 += RS) {
+#pragma unroll
+      for (int u = 0; u < RS; ++u)
+        if (v0 + u < nv) step(v0 + u, R[u]);
     }
   }
 
@@ -647,9 +701,10 @@ struct Tile {
     const int w1 = (int)(((ub + nst) * G - 1) / Ut);
     if (w0 == w1) return;  // one range holds the whole tile; run_all stored it
     const int t = F * G + tq;
-    const int rb = t % nb;
+    int rb, nt;
+    tile_rc(t, nb, N / BN, rb, nt);
     const int64_t row0 = (int64_t)rb * BM;
-    const int n0 = (t / nb) * BN;
+    const int n0 = nt * BN;
     if ((unsigned)g.block_expert[rb] >= (unsigned)g.E_loc) return;
     const int tid = threadIdx.x;
     if (tid < BM) {

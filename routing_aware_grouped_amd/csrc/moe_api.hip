@@ -40,12 +40,15 @@ moe_status validate(const moe_problem* p) {
   if (slots >= (1ll << 30)) return MOE_ERR_UNSUPPORTED;
   // the alignment step keeps its tables in one workgroup's LDS
   if (align_lds_bytes(p->tokens, p->local_experts) > kMaxLds - 512) return MOE_ERR_UNSUPPORTED;
-  // the grouped FFN addresses activation, h and y_slots rows with 32-bit element
-  // offsets
+  // the grouped FFN addresses x, h, y_slots and one expert's weight matrix with
+  // 32-bit byte offsets below 2^31 (buffer loads; offsets from 2^31 up mark
+  // chunks with no operand)
   {
     const int64_t rmax = slots + (int64_t)(slots < p->local_experts ? slots : p->local_experts) * (kMaxBlockM - 1);
     const int64_t wide = p->hidden > p->inter ? p->hidden : p->inter;
-    if (rmax * wide >= (1ll << 31) || (int64_t)p->tokens * p->hidden >= (1ll << 31))
+    const int64_t ab = elem_bytes(a), wb = elem_bytes(w);
+    if (rmax * wide * ab >= (1ll << 31) || (int64_t)p->tokens * p->hidden * ab >= (1ll << 31) ||
+        (int64_t)p->inter * p->hidden * wb >= (1ll << 31))
       return MOE_ERR_UNSUPPORTED;
   }
   // the cost model converts tile and wave counts to fp32 exactly (< 2^24)

@@ -85,11 +85,24 @@ def test_query_sizes():
     (dict(act_dtype=moe.MOE_FP8_E4M3, weight_dtype=moe.MOE_FP8_E4M3), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=7), moe.MOE_ERR_INVALID_ARG),
     (dict(tokens=1 << 20, num_experts=1024, local_experts=1024, top_k=8), moe.MOE_ERR_UNSUPPORTED),
+    # one expert's bf16 weight matrix of 2^31 bytes: beyond the 32-bit buffer offsets
+    (dict(hidden=32768, inter=32768, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16),
+     moe.MOE_ERR_UNSUPPORTED),
+    # x of 2^31 bytes (B * H bf16)
+    (dict(tokens=1 << 18, hidden=4096, num_experts=8, local_experts=8, top_k=1,
+          act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_problems(kw, status):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_query_sizes(_p(**kw))
     assert ei.value.status == status
+
+
+def test_largest_expert_matrix_is_accepted():
+    """An expert matrix one 128-column block below 2^31 bytes is within the limits."""
+    s = moe.moe_query_sizes(_p(hidden=32768, inter=32768 - 128, act_dtype=moe.MOE_BF16,
+                               weight_dtype=moe.MOE_BF16))
+    assert s.rows_max > 0
 
 
 def test_compute_calls_validate_before_any_gpu_work():
