@@ -285,11 +285,12 @@ struct Tile {
   }
 
   // Whether the r tail tiles of a phase are split across all G workgroups.  A
-  // last round in which at least half of the workgroups stream weights still runs
-  // near the HBM rate, so streaming configurations split only smaller tails; the
-  // cached configuration (compute-bound loads) always splits.
+  // last round in which at least three quarters of the workgroups stream weights
+  // runs near the HBM rate, so streaming configurations split only smaller tails
+  // (a split costs the fix-up launch its work, which a small layer cannot hide);
+  // the cached configuration (compute-bound loads) always splits.
   __device__ __forceinline__ static bool split_tail(int r, int G) {
-    return r > 0 && (!STREAM || 2 * r < G);
+    return r > 0 && (!STREAM || 4 * r < 3 * G);
   }
 
   // Runs the work of workgroup slot `slot` of `G` (hybrid Stream-K).  The phase's

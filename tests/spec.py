@@ -33,5 +33,5 @@ MAX_GRID = 1024
 def splits_tail(r: int, grid: int, stream: int) -> bool:
     """Whether a phase's last r (< grid) tiles are split by reduction stages across
     the whole grid (hybrid Stream-K): always for the cached configuration, and for
-    streaming ones when fewer than half of the workgroups would be busy."""
-    return r > 0 and (not stream or 2 * r < grid)
+    streaming ones when fewer than three quarters of the workgroups would be busy."""
+    return r > 0 and (not stream or 4 * r < 3 * grid)
