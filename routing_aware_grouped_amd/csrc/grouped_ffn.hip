@@ -106,13 +106,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// LDS row swizzle in 16-byte units: chunk c of row r sits at c ^ (r & 7).  A
-// quarter wave's MFMA fragment read (16 consecutive rows, one logical chunk) then
-// hits every bank once per LDS cycle, and a stage write (8 lanes per row) covers
-// each row's 128 bytes.  Measured with rocprofv3 on gfx950: a fragment read costs
-// 4 LDS cycles and no bank-conflict cycles, against 8 cycles (half of them
+// LDS row swizzle in 16-byte units for rows of C chunks: chunk c of row r sits at
+// c ^ (r & 7) for 128-byte rows and c ^ (r & 15) for longer ones.  A quarter
+// wave's MFMA fragment read (16 consecutive rows, one logical chunk) then hits
+// every one of the 64 banks once: 128-byte rows alternate between the two bank
+// halves and take 8 distinct chunks each, longer rows all start on bank 0 and
+// take 16 distinct chunks.  A stage write covers each row's chunks once.
+// Measured with rocprofv3 on gfx950 for 128-byte rows: a fragment read costs 4
+// LDS cycles and no bank-conflict cycles, against 8 cycles (half of them
 // conflicts) for the swizzle c ^ ((r & 7) ^ ((r >> 3) & 1)) and 16 without one.
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+template <int C>
+__device__ __forceinline__ int swz(int row) { return row & (C >= 16 ? 15 : 7); }
 
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
@@ -474,14 +478,14 @@ struct Tile {
       for (int i = 0; i < NA; ++i) {
         const int q = i * kThreads + tid;
         const int row = q / GCA, c = q % GCA;
-        *(u32x4*)(buf + row * ROWB + ((c ^ swz(row)) << 4)) = R.a[i];
+        *(u32x4*)(buf + row * ROWB + ((c ^ swz<C>(row)) << 4)) = R.a[i];
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int q = i * kThreads + tid;
         const int c = q % GCB;
         const int row = BM + q / GCB;  // LDS row: matrices follow each other
-        const int sw = swz(row);
+        const int sw = swz<C>(row);
         uint8_t* rp = buf + row * ROWB;
         if constexpr (FP8) {
           u32x4 o0, o1;
@@ -500,7 +504,7 @@ struct Tile {
     const int lg = lane >> 4;   // k-group of 8 inside a 32-step
     auto read_frag = [&](const uint8_t* buf, int row, int step, Frag<F32>& f) __attribute__((always_inline)) {
       const uint8_t* rp = buf + row * ROWB;
-      const int sw = swz(row);
+      const int sw = swz<C>(row);
       if constexpr (F32) {
         const int c0 = step * 8 + 2 * lg;
         f.lo = *(const f32x4*)(rp + ((c0 ^ sw) << 4));
