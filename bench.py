@@ -27,7 +27,9 @@ alphas:
 - the Kimi-K2 one-GPU expert share.
 
 On every sweep point it times each compiled tile configuration (exhaustive
-search) and reports the gap of the on-GPU choice.
+search) and reports the gap of the on-GPU choice, and next to it the gaps of the
+simpler policies the pages compare with (routing_aware_grouped_amd.choosers),
+fit on the same fit loads as the cost model.
 
 Work accounting follows GC-MoE's conventions:
 - FLOPs = 6 * routed slots * H * I;
@@ -181,6 +183,16 @@ def load_theta(shape_name, V):
     return th, None
 
 
+def fit_loads(shape_name):
+    """The loads the workload's chooser was fit on, with the forced time of every
+    configuration, or None."""
+    path = os.path.join(ROOT, "routing_aware_grouped_amd", "theta", f"{shape_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        return json.load(f).get("loads")
+
+
 # ----------------------------------------------------------------------- points --
 def device_weights(wdev):
     return (wdev["w1"], wdev["w3"], wdev["w2"], wdev["s1"], wdev["s3"], wdev["s2"])
@@ -287,7 +299,19 @@ def sweep_shape(torch, np, synth, L, T, shape, V, reps, log_prefix=""):
                    worst_gap=round(max(gaps), 4),
                    within_5pct=round(sum(g_ <= 0.05 for g_ in gaps) / len(gaps), 3),
                    theta=theta_src or "untuned default (th1 = 1: fewest waves)")
-    return dict(points=out, chooser=chooser)
+    res = dict(points=out, chooser=chooser)
+    loads = fit_loads(shape)
+    if loads:
+        # the pages' simpler policies, fit on the cost model's fit loads and scored
+        # on the same exhaustive labels
+        from routing_aware_grouped_amd import choosers
+        import routing_aware_grouped_amd as moe
+        block_m = [moe.moe_variant_info(v)[0] for v in range(V)]
+        res["alternatives"] = choosers.compare(loads, out, block_m)
+        for name, g in res["alternatives"].items():
+            log(f"[bench] {shape} chooser {name}: gap {g['geomean_gap']:.4f} "
+                f"worst {g['worst_gap']:.4f} (cost model {chooser['geomean_gap']:.4f})")
+    return res
 
 
 # ----------------------------------------------------------------------- main --
