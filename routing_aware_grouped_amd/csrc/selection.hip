@@ -79,28 +79,55 @@ __device__ __forceinline__ float order_key_float(uint32_t o) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  lo = __shfl_xor(lo, m, kWave);
-  hi = __shfl_xor(hi, m, kWave);
-  return ((uint64_t)hi << 32) | lo;
+// Cross-lane reductions over groups of L lanes (L = 8, 16, 32 or 64) with DPP
+// moves, which run in the vector ALU instead of the LDS crossbar that a generic
+// shuffle goes through: quad swaps, the half-row and row mirrors (8 and 16 lanes),
+// then for 32 and 64 lanes the row broadcasts of the scan pattern, after which the
+// group's last lane holds the result and is read back with readlane.  Every lane of
+// the wave must take part; every lane of a group gets the same value.  `id` is the
+// operation's identity, which lanes outside the broadcast's row mask receive.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWMASK, 0xF, false);
 }
 
-template <int L>
-__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
+template <int L, class Op>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v, uint32_t id, Op op) {
+  static_assert(L == 8 || L == 16 || L == 32 || L == 64, "group of 8 to 64 lanes");
+  v = op(v, dpp_mov<0xB1, 0xF>(v, id));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_mov<0x4E, 0xF>(v, id));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_mov<0x141, 0xF>(v, id));  // row_half_mirror: 8 lanes
+  if (L >= 16) v = op(v, dpp_mov<0x140, 0xF>(v, id));  // row_mirror: 16 lanes
+  if (L >= 32) v = op(v, dpp_mov<0x142, 0xA>(v, id));  // row_bcast:15 into rows 1, 3
+  if (L == 64) {
+    v = op(v, dpp_mov<0x143, 0xC>(v, id));  // row_bcast:31 into rows 2, 3
+    v = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  } else if (L == 32) {
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    v = (threadIdx.x & 32) ? b : a;
   }
   return v;
 }
 
+// The largest 64-bit key of the group: the largest high word, then among the lanes
+// holding it the largest low word.
+template <int L>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  const uint32_t hi = group_reduce<L>((uint32_t)(v >> 32), 0u, umax);
+  const uint32_t lo = group_reduce<L>((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u, 0u, umax);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+struct IAdd {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+
 template <int L>
 __device__ __forceinline__ float group_sum_f32(float v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  auto add = [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); };
+  return __uint_as_float(group_reduce<L>(__float_as_uint(v), 0u, add));
 }
 
 __global__ void zero_counts_kernel(int32_t* counts, int n) {
@@ -110,12 +137,13 @@ __global__ void zero_counts_kernel(int32_t* counts, int n) {
 
 // One workgroup's share of the routing: tokens wg * groups, (wg + nwg) * groups, ...
 // L lanes per token, MMAX >= ceil(E / L) logits per lane; hist [E_loc] in LDS
-// collects this workgroup's local-expert counts.
+// collects this workgroup's local-expert counts.  With lds_ids (one workgroup for
+// the whole batch) the ids also go to LDS, [B][k], for the alignment that follows.
 template <int L, int MMAX>
 __device__ __forceinline__ void route_block(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                             float* __restrict__ wout, int32_t* hist, int B, int E,
                                             int k, int e0, int E_loc, int renormalize, int wg,
-                                            int nwg) {
+                                            int nwg, int32_t* lds_ids) {
   for (int i = threadIdx.x; i < E_loc; i += blockDim.x) hist[i] = 0;
   __syncthreads();
 
@@ -175,6 +203,7 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     }
     if (active && gl < k) {
       ids[(int64_t)t * k + gl] = my_id;
+      if (lds_ids) lds_ids[t * k + gl] = my_id;
       wout[(int64_t)t * k + gl] = ex / den;
       const int le = my_id - e0;
       if (le >= 0 && le < E_loc) atomicAdd(&hist[le], 1);
@@ -190,7 +219,7 @@ __global__ void __launch_bounds__(1024) route_topk_kernel(const float* __restric
                                   int single_wg) {
   extern __shared__ int32_t hist[];  // [E_loc]
   route_block<L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, blockIdx.x,
-                       gridDim.x);
+                       gridDim.x, nullptr);
   if (single_wg) {
     for (int i = threadIdx.x; i < E_loc; i += blockDim.x) counts[i] = hist[i];
   } else {
@@ -241,7 +270,7 @@ __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
   if (wave == 0) {
     int a = 0;
     for (int e = lane; e < E_loc; e += kWave) a += counts[e] > 0;
-    for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m, kWave);
+    a = (int)group_reduce<kWave>((uint32_t)a, 0u, IAdd{});
     if (lane == 0) active = a;
   }
   __syncthreads();
@@ -249,7 +278,7 @@ __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
     const int b = tab.b[v];
     int rt = 0;
     for (int e = lane; e < E_loc; e += kWave) rt += (counts[e] + b - 1) / b;
-    for (int m = 32; m >= 1; m >>= 1) rt += __shfl_xor(rt, m, kWave);
+    rt = (int)group_reduce<kWave>((uint32_t)rt, 0u, IAdd{});
     if (lane == 0) {
       const int T1 = tab.q1[v] * rt, T2 = tab.q2[v] * rt;
       const int W = (T1 + tab.S1[v] - 1) / tab.S1[v] + (T2 + tab.S2[v] - 1) / tab.S2[v];
@@ -283,6 +312,13 @@ __global__ void select_config_kernel(const int32_t* __restrict__ counts, int E_l
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
+
+// Bytes of LDS the alignment's tables take: 16 waves' expert masks, the per-block
+// bases [nblk][E_loc], the expert offsets [E_loc + 1] and totals [E_loc].
+__host__ __device__ __forceinline__ size_t align_table_bytes(int B, int E_loc) {
+  const size_t nblk = (size_t)(B + kWave - 1) / kWave;
+  return (size_t)kAlignWaves * E_loc * 8 + nblk * E_loc * 4 + (size_t)(2 * E_loc + 1) * 4;
+}
 
 __device__ __forceinline__ void build_masks(unsigned long long* masks, const int32_t* ids, int blk,
                                             int B, int k, int e0, int E_loc, int lane) {
@@ -374,9 +410,10 @@ __device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int
   const int nb = R / b;
   if (tid == 0) *num_blocks = nb;
 
-  // pass 3: padding rows [off[e] + n_e, off[e + 1]) and the block -> expert table
-  if (tid < E_loc)
-    for (int r = off[tid] + tot[tid]; r < off[tid + 1]; ++r) sorted_slots[r] = -1;
+  // pass 3: padding rows [off[e] + n_e, off[e + 1]), one wave per expert, and the
+  // block -> expert table
+  for (int e = wave; e < E_loc; e += kAlignWaves)
+    for (int r = off[e] + tot[e] + lane; r < off[e + 1]; r += kWave) sorted_slots[r] = -1;
   for (int i = tid; i < nb; i += kAlignThreads) {
     const int row = i * b;
     int lo = 0, hi = E_loc - 1;  // the largest e with off[e] <= row
@@ -451,12 +488,20 @@ route_select_align_kernel(const float* __restrict__ logits, const float* __restr
                           int32_t* __restrict__ slot_pos, int B, int E, int k, int e0, int E_loc,
                           int renormalize) {
   extern __shared__ unsigned long long lds_u64[];
-  int32_t* hist = (int32_t*)lds_u64;  // [E_loc], then the alignment's tables
-  route_block<L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, 0, 1);
+  __shared__ float th_s[4 * kNumVariants];
+  // LDS: hist [E_loc], the alignment's tables, then the ids [B][k]
+  int32_t* hist = (int32_t*)lds_u64;
+  unsigned long long* al = lds_u64 + (E_loc + 1) / 2;
+  int32_t* lds_ids = (int32_t*)((char*)al + align_table_bytes(B, E_loc));
+  // the cost-model coefficients are loaded before the routing and kept in flight
+  const bool pre = theta != nullptr && threadIdx.x < 4 * kNumVariants;
+  const float th = pre ? theta[threadIdx.x] : 0.f;
+  route_block<L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, 0, 1, lds_ids);
+  if (pre) th_s[threadIdx.x] = th;  // read after select_block's first barrier
   for (int i = threadIdx.x; i < E_loc; i += blockDim.x) counts[i] = hist[i];
-  const int v = theta ? select_block(hist, E_loc, theta, tab, variant, t_hat) : given_variant(variant);
-  align_block(ids, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
-              slot_pos, lds_u64 + (E_loc + 1) / 2);
+  const int v = theta ? select_block(hist, E_loc, th_s, tab, variant, t_hat) : given_variant(variant);
+  align_block(lds_ids, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
+              slot_pos, al);
 }
 
 // Steps 2-3 in one workgroup, after a multi-workgroup routing launch.
@@ -486,7 +531,8 @@ hipError_t launch_rsa(const moe_problem& p, const float* logits, const float* th
                       hipStream_t s) {
   const int B = p.tokens;
   const size_t al_bytes = align_lds_bytes(B, p.local_experts);
-  const size_t fused_bytes = (size_t)(p.local_experts + 1) / 2 * 8 + al_bytes;
+  const size_t fused_bytes =
+      (size_t)(p.local_experts + 1) / 2 * 8 + al_bytes + (size_t)B * p.top_k * sizeof(int32_t);
   if (B <= 4 * (1024 / L) && fused_bytes <= 150 * 1024) {
     const void* fn = (const void*)route_select_align_kernel<L, MMAX>;
     hipError_t e = allow_lds(fn, fused_bytes);
@@ -534,10 +580,7 @@ hipError_t launch_select_config(const moe_problem& p, const int32_t* counts, con
 }
 
 
-size_t align_lds_bytes(int B, int E_loc) {
-  const size_t nblk = (size_t)(B + kWave - 1) / kWave;
-  return (size_t)kAlignWaves * E_loc * 8 + nblk * E_loc * 4 + (size_t)(2 * E_loc + 1) * 4;
-}
+size_t align_lds_bytes(int B, int E_loc) { return align_table_bytes(B, E_loc); }
 
 hipError_t launch_align_sort(const moe_problem& p, const int32_t* ids, const int32_t* variant,
                              int32_t* sorted_slots, int32_t* block_expert, int32_t* num_blocks,
