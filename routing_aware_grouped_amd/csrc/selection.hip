@@ -136,20 +136,22 @@ __global__ void zero_counts_kernel(int32_t* counts, int n) {
 }
 
 // One workgroup's share of the routing: tokens wg * groups, (wg + nwg) * groups, ...
-// L lanes per token, MMAX >= ceil(E / L) logits per lane; hist [E_loc] in LDS
-// collects this workgroup's local-expert counts.  With lds_ids (one workgroup for
-// the whole batch) the ids also go to LDS, [B][k], for the alignment that follows.
-template <int L, int MMAX>
+// NT threads, L lanes per token, MMAX >= ceil(E / L) logits per lane; hist [E_loc]
+// in LDS collects this workgroup's local-expert counts.  With lds_ids (one
+// workgroup for the whole batch) the ids also go to LDS, [B][k], for the alignment
+// that follows.  Every logit load is unconditional (out-of-range lanes read
+// element 0 of a valid row and discard it), so one wait covers them all.
+template <int NT, int L, int MMAX>
 __device__ __forceinline__ void route_block(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                             float* __restrict__ wout, int32_t* hist, int B, int E,
                                             int k, int e0, int E_loc, int renormalize, int wg,
                                             int nwg, int32_t* lds_ids) {
-  for (int i = threadIdx.x; i < E_loc; i += blockDim.x) hist[i] = 0;
+  for (int i = threadIdx.x; i < E_loc; i += NT) hist[i] = 0;
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int gl = lane & (L - 1);  // lane inside the token group
-  const int groups_per_wg = blockDim.x / L;
+  constexpr int groups_per_wg = NT / L;
   const int group = threadIdx.x / L;
   const int M = (E + L - 1) / L;
 
@@ -158,12 +160,18 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     const bool active = t < B;  // whole groups are inactive together
     uint64_t key[MMAX];
     const float* lrow = logits + (int64_t)(active ? t : 0) * E;
+    float xl[MMAX];
 #pragma unroll
     for (int i = 0; i < MMAX; ++i) {
       const int e = gl + i * L;
-      key[i] = 0;
-      if (active && i < M && e < E)
-        key[i] = ((uint64_t)float_order_key(lrow[e]) << 32) | (uint32_t)(~(uint32_t)e);
+      xl[i] = lrow[(i < M && e < E) ? e : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < MMAX; ++i) {
+      const int e = gl + i * L;
+      key[i] = (active && i < M && e < E)
+                   ? ((uint64_t)float_order_key(xl[i]) << 32) | (uint32_t)(~(uint32_t)e)
+                   : 0;
     }
     int my_id = -1;
     float my_logit = 0.f;
@@ -193,11 +201,17 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     if (renormalize) {
       den = group_sum_f32<L>(ex);
     } else {
+      float xr[MMAX];
+#pragma unroll
+      for (int i = 0; i < MMAX; ++i) {
+        const int e = gl + i * L;
+        xr[i] = lrow[(i < M && e < E) ? e : 0];
+      }
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < MMAX; ++i) {
         const int e = gl + i * L;
-        if (active && i < M && e < E) part += expf(lrow[e] - top);
+        if (active && i < M && e < E) part += expf(xr[i] - top);
       }
       den = group_sum_f32<L>(part);
     }
@@ -212,18 +226,18 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
   __syncthreads();
 }
 
-template <int L, int MMAX>
-__global__ void __launch_bounds__(1024) route_topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
+template <int NT, int L, int MMAX>
+__global__ void __launch_bounds__(NT) route_topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                   float* __restrict__ wout, int32_t* __restrict__ counts, int B,
                                   int E, int k, int e0, int E_loc, int renormalize,
                                   int single_wg) {
   extern __shared__ int32_t hist[];  // [E_loc]
-  route_block<L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, blockIdx.x,
-                       gridDim.x, nullptr);
+  route_block<NT, L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, blockIdx.x,
+                           gridDim.x, nullptr);
   if (single_wg) {
-    for (int i = threadIdx.x; i < E_loc; i += blockDim.x) counts[i] = hist[i];
+    for (int i = threadIdx.x; i < E_loc; i += NT) counts[i] = hist[i];
   } else {
-    for (int i = threadIdx.x; i < E_loc; i += blockDim.x)
+    for (int i = threadIdx.x; i < E_loc; i += NT)
       if (hist[i]) atomicAdd(&counts[i], hist[i]);
   }
 }
@@ -244,17 +258,22 @@ hipError_t launch_lm(const moe_problem& p, const float* logits, int32_t* ids, fl
     if (grid > 4096) grid = 4096;
     zero_counts_kernel<<<(p.local_experts + 255) / 256, 256, 0, s>>>(counts, p.local_experts);
   }
-  route_topk_kernel<L, MMAX><<<grid, threads, p.local_experts * sizeof(int32_t), s>>>(
-      logits, ids, w, counts, B, p.num_experts, p.top_k, p.expert_begin, p.local_experts,
-      p.renormalize, single ? 1 : 0);
+  if (single)
+    route_topk_kernel<1024, L, MMAX><<<grid, threads, p.local_experts * sizeof(int32_t), s>>>(
+        logits, ids, w, counts, B, p.num_experts, p.top_k, p.expert_begin, p.local_experts,
+        p.renormalize, 1);
+  else
+    route_topk_kernel<256, L, MMAX><<<grid, threads, p.local_experts * sizeof(int32_t), s>>>(
+        logits, ids, w, counts, B, p.num_experts, p.top_k, p.expert_begin, p.local_experts,
+        p.renormalize, 0);
   return hipGetLastError();
 }
 
 
 
-// The selection by one workgroup (one wave per configuration, as many waves as the
-// block has): counts may be in global memory or LDS.  Returns the chosen index to
-// every thread.
+// The selection by one workgroup of NT threads (one wave per configuration):
+// counts may be in global memory or LDS.  Returns the chosen index to every thread.
+template <int NT>
 __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
                                             const float* __restrict__ theta, const CostTable& tab,
                                             int32_t* __restrict__ variant,
@@ -264,7 +283,7 @@ __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
   __shared__ int chosen;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
+  constexpr int nwaves = NT / kWave;
   if (threadIdx.x == 0) active = 0;
   __syncthreads();
   if (wave == 0) {
@@ -305,7 +324,8 @@ __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
 __global__ void select_config_kernel(const int32_t* __restrict__ counts, int E_loc,
                                      const float* __restrict__ theta, CostTable tab,
                                      int32_t* __restrict__ variant, float* __restrict__ t_hat) {
-  select_block(counts, E_loc, theta, tab, variant, t_hat);
+  select_block<kWave * (kNumVariants < 16 ? kNumVariants : 16)>(counts, E_loc, theta, tab, variant,
+                                                              t_hat);
 }
 
 
@@ -325,10 +345,15 @@ __device__ __forceinline__ void build_masks(unsigned long long* masks, const int
   for (int e = lane; e < E_loc; e += kWave) masks[e] = 0ull;
   __builtin_amdgcn_wave_barrier();
   const int t = blk * kWave + lane;
-  if (t < B) {
-    for (int j = 0; j < k; ++j) {
-      const int e = ids[(int64_t)t * k + j] - e0;
-      if (e >= 0 && e < E_loc) atomicOr(&masks[e], 1ull << lane);
+  const int tc = t < B ? t : B - 1;  // loads stay in bounds; results of t >= B are dropped
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ids[(int64_t)tc * k + (j0 + u < k ? j0 + u : k - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = v[u] - e0;
+      if (t < B && j0 + u < k && e >= 0 && e < E_loc) atomicOr(&masks[e], 1ull << lane);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -429,11 +454,17 @@ __device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int
   for (int blk = wave; blk < nblk; blk += kAlignWaves) {
     build_masks(masks, ids, blk, B, k, e0, E_loc, lane);
     const int t = blk * kWave + lane;
-    if (t < B) {
-      const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-      for (int j = 0; j < k; ++j) {
-        const int64_t s = (int64_t)t * k + j;
-        const int e = ids[s] - e0;
+    const int tc = t < B ? t : B - 1;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = ids[(int64_t)tc * k + (j0 + u < k ? j0 + u : k - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t >= B || j0 + u >= k) continue;
+        const int64_t s = (int64_t)t * k + j0 + u;
+        const int e = v[u] - e0;
         if (e >= 0 && e < E_loc) {
           const int pos = base[(size_t)blk * E_loc + e] + __popcll(masks[e] & below);
           sorted_slots[pos] = (int32_t)s;
@@ -496,10 +527,11 @@ route_select_align_kernel(const float* __restrict__ logits, const float* __restr
   // the cost-model coefficients are loaded before the routing and kept in flight
   const bool pre = theta != nullptr && threadIdx.x < 4 * kNumVariants;
   const float th = pre ? theta[threadIdx.x] : 0.f;
-  route_block<L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, 0, 1, lds_ids);
+  route_block<1024, L, MMAX>(logits, ids, wout, hist, B, E, k, e0, E_loc, renormalize, 0, 1,
+                             lds_ids);
   if (pre) th_s[threadIdx.x] = th;  // read after select_block's first barrier
-  for (int i = threadIdx.x; i < E_loc; i += blockDim.x) counts[i] = hist[i];
-  const int v = theta ? select_block(hist, E_loc, th_s, tab, variant, t_hat) : given_variant(variant);
+  for (int i = threadIdx.x; i < E_loc; i += 1024) counts[i] = hist[i];
+  const int v = theta ? select_block<1024>(hist, E_loc, th_s, tab, variant, t_hat) : given_variant(variant);
   align_block(lds_ids, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
               slot_pos, al);
 }
@@ -512,7 +544,8 @@ select_align_kernel(const int32_t* __restrict__ counts, const float* __restrict_
                     int32_t* __restrict__ block_expert, int32_t* __restrict__ num_blocks,
                     int32_t* __restrict__ slot_pos, int B, int k, int e0, int E_loc) {
   extern __shared__ unsigned long long lds_u64[];
-  const int v = theta ? select_block(counts, E_loc, theta, tab, variant, t_hat) : given_variant(variant);
+  const int v = theta ? select_block<kAlignThreads>(counts, E_loc, theta, tab, variant, t_hat)
+                      : given_variant(variant);
   align_block(ids, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
               slot_pos, lds_u64);
 }
