@@ -211,7 +211,9 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
     g_chosen = T.graph(lambda: L.forward(b))
     t_chosen = stats(T.time_graph(g_chosen, reps, warmup))
     res = dict(tokens=tokens, alpha=alpha, expert_begin=layer.expert_begin, S=w["S"], A=w["A"],
-               eff_exp=round(w["eff_exp"], 3), variant=chosen, us=round(t_chosen["median"], 3),
+               eff_exp=round(w["eff_exp"], 3),
+               ddist_x=round(layer.shape.local_experts / w["eff_exp"], 2) if w["eff_exp"] > 0 else None,
+               variant=chosen, us=round(t_chosen["median"], 3),
                us_p10=round(t_chosen["p10"], 3), us_p90=round(t_chosen["p90"], 3),
                roof_us=round(roof_us(w), 3),
                hbm_frac=round(w["layer_bytes"] / (t_chosen["median"] * 1e-6) / HBM_PEAK, 4),

@@ -119,6 +119,29 @@ def eff_exp(counts) -> float:
     return float(t.sum() ** 2 / s2) if s2 > 0 else 0.0
 
 
+def ddist_alpha(x: float, n: int, samples: int = 64, iters: int = 40, seed: int = 0) -> float:
+    """ddist:X ("Decoding the Skew", section III-A): the concentration of a
+    symmetric Dirichlet over n experts whose shares have mean effective experts
+    n / x.  Effective experts grow with alpha, so the search bisects [1e-6, 1e6]
+    with the arithmetic midpoint as the page gives it, each step averaging
+    eff_exp over `samples` draws of the shares.  x = 1 asks for n, which no draw
+    reaches, so the search runs to the top of the range (near-uniform routing)."""
+    if not (1.0 <= x <= n):
+        raise ValueError("ddist:X needs 1 <= X <= n")
+    target = n / x
+    rng = np.random.default_rng(seed)
+    lo, hi = 1e-6, 1e6
+    mid = 0.5 * (lo + hi)
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        v = float(np.mean([eff_exp(dirichlet_shares(rng, mid, n)) for _ in range(samples)]))
+        if v < target:
+            lo = mid
+        else:
+            hi = mid
+    return mid
+
+
 # ----------------------------------------------------------------------------------
 # Tensors and dtype encodings
 # ----------------------------------------------------------------------------------

@@ -1,6 +1,7 @@
 """The seeded input generator: Dirichlet skew model ("Decoding the Skew" II-D,
 III-A) and the fp8 block quantiser.  CPU only."""
 import numpy as np
+import pytest
 import scipy.stats
 
 import synth
@@ -82,3 +83,31 @@ def test_layer_seeds_are_deterministic():
     np.testing.assert_array_equal(a.w2, b.w2)
     c = synth.make_layer("tiny", 64, None, 1)
     assert not np.array_equal(a.logits, c.logits)
+
+
+def test_ddist_alpha_hits_its_target():
+    """The searched alpha gives mean effective experts n / X on fresh draws."""
+    rng = np.random.default_rng(11)
+    for n, x in ((8, 2.0), (128, 4.0), (256, 16.0)):
+        a = synth.ddist_alpha(x, n, samples=64, iters=40, seed=1)
+        v = np.mean([synth.eff_exp(synth.dirichlet_shares(rng, a, n)) for _ in range(400)])
+        assert abs(v / (n / x) - 1) < 0.05, (n, x, a, v)
+
+
+def test_ddist_alpha_against_the_second_moment():
+    """For Dir(a 1_n), E[sum p_i^2] = (a + 1) / (n a + 1); with many experts the
+    mean of 1 / sum p^2 is close to its reciprocal, so the alpha found for ddist:X
+    is close to the closed-form root of (n a + 1) / (a + 1) = n / X."""
+    n, x = 256, 4.0
+    t = n / x
+    a_closed = (t - 1) / (n - t)
+    a = synth.ddist_alpha(x, n, samples=64, iters=40, seed=2)
+    assert abs(a / a_closed - 1) < 0.08, (a, a_closed)
+
+
+def test_ddist_alpha_is_monotone_and_bounded():
+    a = [synth.ddist_alpha(x, 64, samples=32, iters=40, seed=3) for x in (1.0, 2.0, 8.0, 32.0)]
+    assert a[0] > 1e5  # X = 1: no draw reaches n, the search runs to the top of the range
+    assert a[0] > a[1] > a[2] > a[3] > 1e-6
+    with pytest.raises(ValueError):
+        synth.ddist_alpha(0.5, 64)
