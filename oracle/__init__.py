@@ -27,6 +27,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, FP8 = 0, 1, 2
+F64 = 3  # fp64 activations: the dequantized x of the FP8 activation path
 
 
 def build(force: bool = True) -> str:
@@ -65,6 +66,8 @@ def lib():
         L.oracle_decode_fp8.restype = None
         L.oracle_decode_bf16.argtypes = [P, i64, P]
         L.oracle_decode_bf16.restype = None
+        L.oracle_quant_act_e4m3.argtypes = [i32, i32, P, P, P]
+        L.oracle_e4m3_round.argtypes = [P, i64, P]
         L.oracle_max_threads.argtypes = []
         _lib = L
     return _lib
@@ -135,6 +138,46 @@ def align(ids: np.ndarray, e0: int, E_loc: int, b: int):
     return ss[:R].copy(), be[: nb[0]].copy(), int(nb[0]), sp
 
 
+# ------------------------------------------------------------------------ Q ----
+def quant_act_e4m3(x_bits: np.ndarray):
+    """Q: bf16 activations (uint16 bits [B][H]) -> (E4M3FN codes uint8 [B][H],
+    fp32 scales [B][H/128]), one scale per token and 128-column group."""
+    x = _c(x_bits, np.uint16)
+    B, H = x.shape
+    q = np.empty((B, H), np.uint8)
+    s = np.empty((B, H // 128), np.float32)
+    if lib().oracle_quant_act_e4m3(B, H, _p(x), _p(q), _p(s)) != 0:
+        raise ValueError("oracle_quant_act_e4m3: H must be a multiple of 128")
+    return q, s
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """The rounding step of Q alone: nearest E4M3FN codes of fp32 values, |v| <= 448."""
+    a = _c(v, np.float32).ravel()
+    q = np.empty(a.size, np.uint8)
+    if lib().oracle_e4m3_round(_p(a), a.size, _p(q)) != 0:
+        raise ValueError("e4m3_round: |v| must be <= 448")
+    return q.reshape(np.shape(v))
+
+
+def dequant_act(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """x = q * s in fp64 (exact), per 128-column group."""
+    B, H = q.shape
+    return decode_fp8(q) * np.repeat(np.asarray(s, np.float64), 128, axis=1)[:, :H]
+
+
+def _act_args(layer, tokens: np.ndarray):
+    """The activation rows the FFN uses for `tokens`: (buffer, dtype, token
+    indices into it).  With the FP8 activation path these are the dequantized
+    rows of Q, computed for the listed tokens only (Q is per token)."""
+    xdt = layer.shape.act_dtype
+    if getattr(layer.shape, "act_quant", 0):
+        toks = np.asarray(tokens, np.int64)
+        q, s = quant_act_e4m3(np.asarray(layer.x)[toks])
+        return _c(dequant_act(q, s), np.float64), F64, np.arange(len(toks), dtype=np.int32)
+    return _c(layer.x, np.float32 if xdt == F32 else np.uint16), xdt, _c(tokens, np.int32)
+
+
 # ------------------------------------------------------------------ O5 - O6 ----
 def _weights_args(layer):
     wd = layer.shape.weight_dtype
@@ -147,10 +190,8 @@ def _weights_args(layer):
 def ffn_slots(layer, tok: np.ndarray, exp_local: np.ndarray, nthreads: int | None = None):
     """O5: fp64 expert outputs [n][H] for (token, local expert) pairs."""
     H, I = layer.shape.hidden, layer.shape.inter
-    xdt = layer.shape.act_dtype
-    x = _c(layer.x, np.float32 if xdt == F32 else np.uint16)
+    x, xdt, tok = _act_args(layer, tok)
     wd, w1, w3, w2, s1, s3, s2 = _weights_args(layer)
-    tok = _c(tok, np.int32)
     el = _c(exp_local, np.int32)
     y = np.empty((len(tok), H), np.float64)
     rc = lib().oracle_ffn_slots(H, I, _p(x), xdt, _p(w1), _p(w3), _p(w2), wd, _p(s1), _p(s3),
@@ -165,12 +206,17 @@ def layer_tokens(layer, ids: np.ndarray, w: np.ndarray, tokens: np.ndarray,
                  nthreads: int | None = None):
     """O5 + O6 for the listed tokens: fp64 Y rows [len(tokens)][H]."""
     H, I, k = layer.shape.hidden, layer.shape.inter, layer.shape.top_k
-    xdt = layer.shape.act_dtype
-    x = _c(layer.x, np.float32 if xdt == F32 else np.uint16)
+    if getattr(layer.shape, "act_quant", 0):
+        # the FFN sees the listed tokens' dequantized rows; ids/w follow them
+        sel = np.asarray(tokens, np.int64)
+        x, xdt, toks = _act_args(layer, sel)
+        ids = _c(np.asarray(ids)[sel], np.int32)
+        w = _c(np.asarray(w)[sel], np.float64)
+    else:
+        x, xdt, toks = _act_args(layer, tokens)
+        ids = _c(ids, np.int32)
+        w = _c(w, np.float64)
     wd, w1, w3, w2, s1, s3, s2 = _weights_args(layer)
-    ids = _c(ids, np.int32)
-    w = _c(w, np.float64)
-    toks = _c(tokens, np.int32)
     Y = np.empty((len(toks), H), np.float64)
     rc = lib().oracle_layer_tokens(H, I, k, layer.expert_begin, layer.shape.local_experts,
                                    _p(x), xdt, _p(w1), _p(w3), _p(w2), wd, _p(s1), _p(s3),

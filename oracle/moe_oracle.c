@@ -25,6 +25,11 @@
  *  O5 ffn      - per routed slot, W2 * SwiGLU(W1 x) with SwiGLU = silu(gate)*up
  *                (GC-MoE 2.1 Eq. 1; RaMP 2.1 gated MLP).
  *  O6 combine  - y_t = sum_j g_{t,j} * y_{t,j}, in j order (GC-MoE 2.1 Eq. 1).
+ *  Q  act quant - the optional FP8 activation path: x quantized to E4M3FN per
+ *                token and per group of 128 hidden columns with an fp32 scale
+ *                (RaMP 3.3 and A.8: FP8 with 128 x 128 block scaling as used by
+ *                DeepSeek-V3, whose activations are scaled per 1 x 128 group);
+ *                the expert FFN then runs on the dequantized x = q * s.
  *
  * Readings of points the pages leave open (each stated where it is used):
  *  - top-k compares raw fp32 logits; equal logits go to the lower expert index
@@ -43,7 +48,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_F64 = 3 };
 
 /* ---------------------------------------------------------------- decoders -- */
 
@@ -93,7 +98,83 @@ static double orc_weight(const void* w, int dt, const float* scale, int e, int r
 
 static double orc_act(const void* x, int dt, int64_t idx) {
   if (dt == ORC_F32) return (double)((const float*)x)[idx];
+  if (dt == ORC_F64) return ((const double*)x)[idx];
   return orc_bf16_to_f64(((const uint16_t*)x)[idx]);
+}
+
+/* ------------------------------------------------- Q: activation quantizer -- */
+
+/* The E4M3FN code nearest to v, for |v| <= 448.  vals[c] is the value of code c
+ * for c = 0..126 (the finite non-negative codes, increasing with c).  A value
+ * halfway between two neighbouring codes takes the one whose code is even (the
+ * round-to-nearest-even rule of IEEE conversions).  The sign bit is v's sign bit,
+ * so a negative value that rounds to zero gives 0x80 (as an IEEE conversion keeps
+ * the sign of a result that underflows to zero). */
+static uint8_t orc_e4m3_nearest(float v, const double* vals) {
+  const double a = fabs((double)v);
+  int lo = 0, hi = 126;  /* invariant: vals[lo] <= a, answer in [lo, hi] */
+  if (a >= vals[126]) {
+    lo = 126;
+  } else {
+    while (hi - lo > 1) {  /* bisection for the largest lo with vals[lo] <= a */
+      int mid = (lo + hi) / 2;
+      if (vals[mid] <= a) lo = mid; else hi = mid;
+    }
+    {
+      double dlo = a - vals[lo], dhi = vals[lo + 1] - a;
+      if (dhi < dlo || (dhi == dlo && ((lo + 1) & 1) == 0)) lo = lo + 1;
+    }
+  }
+  return (uint8_t)((signbit(v) ? 0x80 : 0x00) | lo);
+}
+
+/* Q: per token t and per group g of 128 hidden columns of bf16 x [B][H]:
+ *   amax = max |x[t][128g + i]| (fp32, exact), s[t][g] = amax / 448 (fp32 division),
+ *   q[t][128g + i] = the nearest E4M3FN code of min(max(x / s, -448), 448), with
+ *   x / s an fp32 division, so that x is approximately q * s with the group's
+ *   largest magnitude mapped onto 448, the largest E4M3FN value.  A group whose
+ *   values are all zero gets s = 0 and codes 0x00.  Returns 0, or -1 for H not a
+ *   multiple of 128. */
+int oracle_quant_act_e4m3(int B, int H, const uint16_t* x, uint8_t* q, float* s) {
+  double vals[127];
+  if (B < 0 || H % 128) return -1;
+  for (int c = 0; c <= 126; ++c) vals[c] = oracle_fp8_e4m3fn_to_f64((uint8_t)c);
+  const int G = H / 128;
+  for (int t = 0; t < B; ++t)
+    for (int g = 0; g < G; ++g) {
+      const uint16_t* xr = x + (int64_t)t * H + (int64_t)g * 128;
+      uint8_t* qr = q + (int64_t)t * H + (int64_t)g * 128;
+      float amax = 0.0f;
+      for (int i = 0; i < 128; ++i) {
+        float a = fabsf((float)orc_bf16_to_f64(xr[i]));
+        if (a > amax) amax = a;
+      }
+      const float sc = amax / 448.0f;
+      s[(int64_t)t * G + g] = sc;
+      for (int i = 0; i < 128; ++i) {
+        if (amax == 0.0f) {
+          qr[i] = 0;
+          continue;
+        }
+        float v = (float)orc_bf16_to_f64(xr[i]) / sc;
+        if (v > 448.0f) v = 448.0f;
+        if (v < -448.0f) v = -448.0f;
+        qr[i] = orc_e4m3_nearest(v, vals);
+      }
+    }
+  return 0;
+}
+
+/* Finite float inputs only: the nearest E4M3FN codes of n fp32 values |v| <= 448
+ * (the rounding step of Q alone, for the pins). */
+int oracle_e4m3_round(const float* v, int64_t n, uint8_t* q) {
+  double vals[127];
+  for (int c = 0; c <= 126; ++c) vals[c] = oracle_fp8_e4m3fn_to_f64((uint8_t)c);
+  for (int64_t i = 0; i < n; ++i) {
+    if (!(fabsf(v[i]) <= 448.0f)) return -1;
+    q[i] = orc_e4m3_nearest(v[i], vals);
+  }
+  return 0;
 }
 
 /* -------------------------------------------------------------- O1: route -- */

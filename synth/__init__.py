@@ -45,6 +45,7 @@ class Shape:
     weight_dtype: int
     out_dtype: int
     logits: str  # "normal" (tiny) or "dirichlet"
+    act_quant: int = 0  # 1: the layer runs its gate/up GEMM on FP8 E4M3 activations
 
 
 SHAPES = {
@@ -53,9 +54,19 @@ SHAPES = {
     "qwen3": Shape("qwen3", 2048, 768, 128, 128, 8, BF16, BF16, BF16, "dirichlet"),
     "dsv3_share": Shape("dsv3_share", 7168, 2048, 256, 32, 8, BF16, FP8, BF16, "dirichlet"),
     "kimi_share": Shape("kimi_share", 7168, 2048, 384, 48, 8, BF16, FP8, BF16, "dirichlet"),
+    # the same two expert shares with FP8 activations in the gate/up GEMM (same
+    # seeds, so the loads are identical to the bf16-activation ones)
+    "dsv3_share_fp8a": Shape("dsv3_share_fp8a", 7168, 2048, 256, 32, 8, BF16, FP8, BF16,
+                             "dirichlet", 1),
+    "kimi_share_fp8a": Shape("kimi_share_fp8a", 7168, 2048, 384, 48, 8, BF16, FP8, BF16,
+                             "dirichlet", 1),
+    # a small fp8 layer for parity at sizes the oracle runs in seconds: a ragged
+    # number of 128-column groups, so that stages of 256 and 512 are partly empty
+    "small_fp8a": Shape("small_fp8a", 384, 256, 8, 8, 2, BF16, FP8, BF16, "dirichlet", 1),
 }
 
-CFG_INDEX = {"tiny": 1, "mixtral": 2, "qwen3": 3, "dsv3_share": 4, "kimi_share": 5}
+CFG_INDEX = {"tiny": 1, "mixtral": 2, "qwen3": 3, "dsv3_share": 4, "kimi_share": 5,
+             "dsv3_share_fp8a": 4, "kimi_share_fp8a": 5, "small_fp8a": 6}
 
 
 def seed_seq(shape: str, tokens: int, alpha: float | None, rep: int) -> np.random.SeedSequence:
