@@ -46,6 +46,13 @@
  *   - Supported dtype combinations (act/out, weights): (f32, f32), (bf16, bf16),
  *     (bf16, fp8_e4m3).  The intermediate h and the per-slot outputs y_slots use
  *     the activation dtype; accumulation is always fp32.
+ *   - FP8 activation path (act_quant = 1, bf16 x with fp8 weights only): the
+ *     library quantizes x to E4M3FN per token and per 128-column group
+ *     (moe_quant_act) and runs the gate/up GEMM with fp8 x fp8 matrix
+ *     instructions, applying the activation and weight block scales to each
+ *     128-deep partial sum (RaMP section 3.3 and appendix A.8: FP8 GEMMs with
+ *     128 x 128 block scaling as used by DeepSeek-V3).  h stays bf16 and the down
+ *     GEMM is unchanged.
  *   - Concurrent calls must not share one workspace or output buffer.
  */
 #ifndef MOE_MI355X_H
@@ -85,6 +92,8 @@ typedef struct moe_problem {
   int32_t weight_dtype;  /* moe_dtype of W1, W3, W2                             */
   int32_t renormalize;   /* 1: softmax over the k chosen logits (default);
                             0: those experts' values of the softmax over all E  */
+  int32_t act_quant;     /* 0: none (default); 1: FP8 activation path (see above;
+                            needs act_dtype MOE_BF16, weight_dtype MOE_FP8_E4M3) */
 } moe_problem;
 
 /* Buffer sizes a caller must provide for one problem. */
@@ -92,7 +101,8 @@ typedef struct moe_sizes {
   int64_t rows_max;        /* capacity (elements) of sorted_slots; rows of y_slots */
   int64_t blocks_max;      /* capacity (elements) of block_expert                  */
   int64_t y_slots_bytes;   /* rows_max * H * sizeof(act)                           */
-  int64_t workspace_bytes; /* grouped_ffn workspace: header, h, partial tiles       */
+  int64_t workspace_bytes; /* grouped_ffn workspace: header, h, (act_quant: x codes
+                              and scales), partial tiles                            */
   int64_t align_ws_bytes;  /* reserved, 0 in this version                          */
 } moe_sizes;
 
@@ -187,6 +197,19 @@ moe_status moe_route_select_align(const moe_problem* p, const float* logits, con
                                   int32_t* block_expert, int32_t* num_blocks, int32_t* slot_pos,
                                   void* stream);
 
+/* FP8 activation quantization (the first launch of the gate/up phase when
+ * act_quant = 1; callable alone for tests).  For every token t and group g of 128
+ * hidden columns of bf16 x [B][H]:
+ *   amax = max_i |x[t][128g + i]|,  xs[t][g] = amax / 448 (fp32 division),
+ *   xq[t][128g + i] = E4M3FN code nearest to clamp(x / xs, -448, 448) (fp32
+ *                     division; ties to the even code; a negative value that
+ *                     rounds to zero gives 0x80),
+ * and a group of zeros gets xs = 0 and codes 0x00.  x = q * s then holds to
+ * within half a code step.  xq uint8 [B][H], xs f32 [B][H/128], device memory.
+ * Requires act_quant = 1; errors as the other calls. */
+moe_status moe_quant_act(const moe_problem* p, const void* x, uint8_t* xq, float* xs,
+                         void* stream);
+
 /* Step 4: grouped expert FFN (RaMP 3.3 and A.8; GC-MoE 2.1 Eq. 1).  For every
  * row r < R that holds a slot (sorted_slots[r] >= 0):
  *   h[r]       = silu(x[t] W1_e^T) * (x[t] W3_e^T)   (t = sorted_slots[r] / k)
@@ -207,7 +230,8 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 4a alone: the grouped gate/up GEMM with the fused SwiGLU, writing h into
- * workspace (as moe_grouped_ffn's first launch).  Arguments and errors as for
+ * workspace (as moe_grouped_ffn's first launch; with act_quant = 1 it is preceded
+ * by moe_quant_act of x into the workspace).  Arguments and errors as for
  * moe_grouped_ffn; w2, s2 and y_slots are not used. */
 moe_status moe_grouped_gate_up(const moe_problem* p, const void* x, const void* w1,
                                const void* w3, const float* s1, const float* s3,

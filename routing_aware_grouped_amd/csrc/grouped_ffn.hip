@@ -38,7 +38,12 @@
 // block scale in fp32, rounded to bf16 (RaMP section 3.3's block-scaled FP8).
 //
 // Math.  v_mfma_f32_16x16x32_bf16 for bf16 operands (fp8 weights decoded to
-// bf16), v_mfma_f32_16x16x4_f32 for the fp32 problem; fp32 accumulation.  Waves
+// bf16), v_mfma_f32_16x16x4_f32 for the fp32 problem; fp32 accumulation.  On the
+// FP8 activation path the gate/up phase stages fp8 x and fp8 weights unchanged and
+// multiplies them with v_mfma_f32_16x16x128_f8f6f4: each instruction covers one
+// 128-deep block, whose activation scale (per row) and weight scale (per tile)
+// multiply its sums before they are added (the block-scaled FP8 GEMM of RaMP
+// section 3.3 and appendix A.8).  Waves
 // are arranged WM x WN x WK over the tile; waves that split K inside a tile add
 // their partial sums through LDS in a fixed order, so results are deterministic.
 #include "moe_common.h"
@@ -49,45 +54,71 @@ namespace {
 // ---------------------------------------------------------------------------
 // element types
 // ---------------------------------------------------------------------------
-enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP8A = 3 };
 
 template <int WK_>
 struct Types;
+// Act: the A operand (x or h) as read; Out: the phase's output (h or y_slots)
 template <>
 struct Types<W_F32> {
   using Act = float;
   using Wt = float;
+  using Out = float;
   static constexpr int asz = 4, wsz = 4;
 };
 template <>
 struct Types<W_BF16> {
   using Act = uint16_t;
   using Wt = uint16_t;
+  using Out = uint16_t;
   static constexpr int asz = 2, wsz = 2;
 };
 template <>
 struct Types<W_FP8> {
   using Act = uint16_t;
   using Wt = uint8_t;
+  using Out = uint16_t;
   static constexpr int asz = 2, wsz = 1;
+};
+// FP8 activation path, gate/up phase: fp8 x (one fp32 scale per token and 128
+// columns), fp8 weights, bf16 h
+template <>
+struct Types<W_FP8A> {
+  using Act = uint8_t;
+  using Wt = uint8_t;
+  using Out = uint16_t;
+  static constexpr int asz = 1, wsz = 1;
 };
 
 // MFMA operand fragment: 8 consecutive k of one row per lane
-template <bool F32>
-struct Frag;
-template <>
-struct Frag<false> {
+template <int KIND>
+struct Frag {  // bf16 operands (also fp8 weights decoded to bf16)
   bf16x8 v;
 };
 template <>
-struct Frag<true> {
+struct Frag<W_F32> {
   f32x4 lo, hi;
 };
+template <>
+struct Frag<W_FP8A> {  // 32 fp8 values of one row: a 128-deep block over 4 lanes
+  u32x4 lo, hi;
+};
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
-__device__ __forceinline__ void mma(f32x4& acc, const Frag<false>& a, const Frag<false>& b) {
+template <int KIND>
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<KIND>& a, const Frag<KIND>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mma(f32x4& acc, const Frag<true>& a, const Frag<true>& b) {
+// fp8 x fp8 over one 128-deep block, from zero: both operands E4M3 (format 0) and
+// unit block exponents (127 = 2^0), so the instruction is a plain fp8 product
+__device__ __forceinline__ f32x4 mma_fp8_block(const Frag<W_FP8A>& a, const Frag<W_FP8A>& b) {
+  const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a.lo, a.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 bv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b.lo, b.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                          0, 127, 0, 127);
+}
+template <>
+__device__ __forceinline__ void mma<W_F32>(f32x4& acc, const Frag<W_F32>& a, const Frag<W_F32>& b) {
   // lane l holds k = 8*(l/16) + c in element c; the c-th 16x16x4 product sums
   // k = {c, 8+c, 16+c, 24+c}, so the eight products cover k = 0..31 once.
 #pragma unroll
@@ -159,7 +190,8 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
 // kernel arguments and the tile queue
 // ---------------------------------------------------------------------------
 struct FfnArgs {
-  const void* x;   // [B][H] act
+  const void* x;   // [B][H] act (the fp8 codes on the FP8 activation path)
+  const float* xs; // [B][H/128] activation scales of the FP8 activation path
   const void* w1;  // [E_loc][I][H]
   const void* w3;  // [E_loc][I][H]
   const void* w2;  // [E_loc][H][I]
@@ -200,14 +232,23 @@ struct Tile {
   using T = Types<WKIND>;
   using Act = typename T::Act;
   using Wt = typename T::Wt;
+  using Out = typename T::Out;
   static constexpr bool F32 = WKIND == W_F32;
-  static constexpr bool FP8 = WKIND == W_FP8;
+  static constexpr bool FP8 = WKIND == W_FP8;    // fp8 weights decoded to bf16
+  static constexpr bool FP8A = WKIND == W_FP8A;  // fp8 x fp8 (gate/up phase only)
+  static_assert(!FP8A || PHASE == 1, "the FP8 activation path covers the gate/up GEMM");
+  using FragT = Frag<F32 ? W_F32 : (FP8A ? W_FP8A : W_BF16)>;
   static constexpr int ASZ = T::asz, WSZ = T::wsz;
   static constexpr int NMAT = PHASE == 1 ? 2 : 1;
   static constexpr int BK = ROWB / ASZ;  // reduction elements per stage
   static constexpr int C = ROWB / 16;    // 16-byte LDS chunks per row
   static constexpr int ROWS = BM + NMAT * BN;
-  static constexpr int STAGE = ROWS * ROWB;  // LDS bytes per stage
+  // FP8 activation path: 128-deep scale blocks per stage, and the stage's scales
+  // in LDS after its rows: x scales [KB][BM], weight scales [NMAT][KB], 1 spare
+  static constexpr int KB = FP8A ? ROWB / 128 : 0;
+  static constexpr int SC_FLOATS = FP8A ? BM * KB + NMAT * KB + 1 : 0;
+  static constexpr int SC_BYTES = (SC_FLOATS * 4 + 15) / 16 * 16;
+  static constexpr int STAGE = ROWS * ROWB + SC_BYTES;  // LDS bytes per stage
   static constexpr int EPC_A = 16 / ASZ;     // elements per global A chunk
   static constexpr int EPC_B = 16 / WSZ;     // elements per global weight chunk
   static constexpr int GCA = BK / EPC_A;     // global chunks per A row per stage
@@ -218,7 +259,7 @@ struct Tile {
   static constexpr int NB = (GB + kThreads - 1) / kThreads;
   static constexpr int MW = BM / WM, NW = BN / WN;
   static constexpr int FM = MW / 16, FN = NW / 16;
-  static constexpr int KSTEPS = BK / 32;
+  static constexpr int KSTEPS = BK / (FP8A ? 128 : 32);  // MFMA steps per stage
   static constexpr int RED_FLOATS = (WK > 1) ? (WK - 1) * WM * WN * NMAT * FM * FN * 4 * 64 : 0;
   static constexpr int NFRAG = NMAT * FM * FN;   // 16x16 accumulator blocks per wave
   static constexpr int PIECE = NMAT * BM * BN;   // floats of one partial tile
@@ -231,12 +272,15 @@ struct Tile {
   static_assert(!FP8 || GCB * 2 == C, "fp8 chunk pairs");
   static_assert(GA % kThreads == 0 && GB % kThreads == 0, "every thread owns whole chunks");
   static_assert((BN * GCB) % kThreads == 0, "each weight load instruction reads one matrix");
+  static_assert(!FP8A || (BM * KB <= kThreads && NMAT * KB <= kThreads && BN <= 128 && 128 % BN == 0),
+                "one scale load per thread; a tile's columns share one 128-row weight block");
   static_assert(WM * WN * NFRAG * 256 == PIECE && PIECE <= kPieceMax, "partial tile layout");
 
   struct Regs {
     u32x4 a[NA];
     u32x4 b[NB];
     float s[FP8 ? NB : 1];
+    float xs, ws;  // FP8 activation path: one x scale and one weight scale
   };
 
   // Tile metadata kept in LDS, in a ring of kMetaSlots slots: the BM slot ids of
@@ -251,7 +295,7 @@ struct Tile {
                                                   const int* m, int64_t row0, int n0, int wm,
                                                   int wn, int lane) {
     const int N = PHASE == 1 ? g.I : g.H;
-    Act* out = (Act*)(PHASE == 1 ? g.h : g.y_slots);
+    Out* out = (Out*)(PHASE == 1 ? g.h : g.y_slots);
     const int lr = lane & 15;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -259,12 +303,12 @@ struct Tile {
       for (int c = 0; c < 4; ++c) {
         const int r = wm * MW + i * 16 + (lane >> 4) * 4 + c;
         if (m[r] < 0) continue;
-        Act* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
+        Out* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn) {
           const float v = PHASE == 1 ? silu_mul(acc[0][i][jn][c], acc[NMAT - 1][i][jn][c])
                                      : acc[0][i][jn][c];
-          store_out<Act>(orow + jn * 16, v);
+          store_out<Out>(orow + jn * 16, v);
         }
       }
   }
@@ -399,6 +443,14 @@ struct Tile {
                                         : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
     uint32_t l_aoff[NA];
+    // FP8 activation path: thread tid < BM * KB loads the x scale of tile row
+    // tid % BM, block tid / BM of each stage (l_xsoff: that row's scale row, or
+    // kOob); threads tid < NMAT * KB load the weight scale of matrix tid / KB,
+    // block tid % KB (l_wsbase: the tile's first scale of its 128-row block)
+    const __amdgpu_buffer_rsrc_t xs_rsrc =
+        make_rsrc(g.xs, FP8A ? (uint32_t)(g.slots / g.k) * (uint32_t)(K / 128) * 4u : 0u);
+    uint32_t l_xsoff = kOob;
+    int64_t l_wsbase = 0;
     // weights: per tile, a buffer from row n0 of the tile's expert matrix to its
     // end; each chunk's byte offset in it depends on the thread alone
     __amdgpu_buffer_rsrc_t l_b_rsrc[NMAT];
@@ -438,6 +490,13 @@ struct Tile {
           l_aoff[i] = (uint32_t)(arow * K + c * EPC_A) * ASZ;
         }
       }
+      if constexpr (FP8A) {
+        const int sl = m[tid % BM];
+        l_xsoff = (l_eok && tid < BM * KB && sl >= 0 && sl < g.slots)
+                      ? (uint32_t)(sl / g.k) * (uint32_t)(K / 128) * 4u + (uint32_t)(tid / BM) * 4u
+                      : kOob;
+        l_wsbase = l_eok ? ((int64_t)l_e * (N / 128) + l_n0 / 128) * (K / 128) : 0;
+      }
     };
     auto load_stage = [&](Regs& R) __attribute__((always_inline)) {
       if (l_new) enter_load_tile(l_j);
@@ -465,6 +524,17 @@ struct Tile {
           const bool ok = l_eok && kel < kl;
           R.s[i] = sm[ok ? ((int64_t)l_e * (N / 128) + (l_n0 + row) / 128) * (K / 128) + (k0 + kel) / 128 : 0];
         }
+      }
+      if constexpr (FP8A) {
+        // scale blocks past K read as zero (x) or as a real scale (weights): the
+        // operands there are zeros, so their products add nothing either way
+        const int kb0 = k0 / 128;
+        const bool xin = kb0 + tid / BM < K / 128;
+        R.xs = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, xin ? l_xsoff : kOob, kb0 * 4, 0));
+        const float* sm = tid / KB == 0 ? smat0 : smat1;
+        const bool wok = l_eok && tid < NMAT * KB && kb0 + tid % KB < K / 128;
+        R.ws = sm[wok ? l_wsbase + kb0 + tid % KB : 0];
       }
       if (++l_s == l_se) {  // past the last item the cursor runs on harmlessly
         ++l_j;
@@ -496,16 +566,25 @@ struct Tile {
           *(u32x4*)(rp + ((c ^ sw) << 4)) = R.b[i];
         }
       }
+      if constexpr (FP8A) {  // the stage's scales; threads without one write the spare
+        float* sc = (float*)(buf + ROWS * ROWB);
+        sc[tid < BM * KB ? tid : SC_FLOATS - 1] = R.xs;
+        sc[tid < NMAT * KB ? BM * KB + tid : SC_FLOATS - 1] = R.ws;
+      }
     };
 
     // ---- MFMA over one stage ----
     f32x4 acc[NMAT][FM][FN];
     const int lr = lane & 15;   // row of the fragment
     const int lg = lane >> 4;   // k-group of 8 inside a 32-step
-    auto read_frag = [&](const uint8_t* buf, int row, int step, Frag<F32>& f) __attribute__((always_inline)) {
+    auto read_frag = [&](const uint8_t* buf, int row, int step, FragT& f) __attribute__((always_inline)) {
       const uint8_t* rp = buf + row * ROWB;
       const int sw = swz<C>(row);
-      if constexpr (F32) {
+      if constexpr (FP8A) {  // 32 consecutive bytes of the step's 128-byte block
+        const int c0 = step * 8 + 2 * lg;
+        f.lo = *(const u32x4*)(rp + ((c0 ^ sw) << 4));
+        f.hi = *(const u32x4*)(rp + (((c0 + 1) ^ sw) << 4));
+      } else if constexpr (F32) {
         const int c0 = step * 8 + 2 * lg;
         f.lo = *(const f32x4*)(rp + ((c0 ^ sw) << 4));
         f.hi = *(const f32x4*)(rp + (((c0 + 1) ^ sw) << 4));
@@ -521,11 +600,12 @@ struct Tile {
     // takes the guarded path.  Reduction steps beyond K need no guard: they were
     // loaded as zeros and add nothing.
     auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
+     if constexpr (!FP8A) {
 #pragma unroll
       for (int jj = 0; jj < KSTEPS / WK; ++jj) {
         const int step = jj * WK + wk;
-        Frag<F32> fa[FM];
-        Frag<F32> fb[NMAT][FN];
+        FragT fa[FM];
+        FragT fb[NMAT][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
 #pragma unroll
@@ -539,8 +619,53 @@ struct Tile {
 #pragma unroll
             for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa[i], fb[mt][j]);
       }
+     }
+    };
+    // FP8 activation path: each step is one 128-deep block; its sums are scaled by
+    // the row's x scale times the tile's weight scale and added in fp32
+    auto compute_f8 = [&](const uint8_t* buf, int nvalid) __attribute__((always_inline)) {
+     if constexpr (FP8A) {
+      if (wm * MW >= nvalid) return;
+      const bool full = wm * MW + MW <= nvalid;
+      const float* sc = (const float*)(buf + ROWS * ROWB);
+#pragma unroll
+      for (int jj = 0; jj < KSTEPS / WK; ++jj) {
+        const int step = jj * WK + wk;
+        FragT fb[NMAT][FN];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
+        float wsv[NMAT];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) wsv[mt] = sc[BM * KB + mt * KB + step];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (!full && wm * MW + i * 16 >= nvalid) continue;
+          FragT fa;
+          read_frag(buf, wm * MW + i * 16 + lr, step, fa);
+          // x scales of this lane's output rows 4 * (lane / 16) + c
+          const f32x4 xsv = *(const f32x4*)(sc + step * BM + wm * MW + i * 16 + 4 * lg);
+#pragma unroll
+          for (int mt = 0; mt < NMAT; ++mt) {
+            f32x4 s4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s4[c] = xsv[c] * wsv[mt];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const f32x4 t = mma_fp8_block(fa, fb[mt][j]);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) acc[mt][i][j][c] = __builtin_fmaf(t[c], s4[c], acc[mt][i][j][c]);
+            }
+          }
+        }
+      }
+     }
     };
     auto compute_stage = [&](const uint8_t* buf, int nvalid) __attribute__((always_inline)) {
+     if constexpr (FP8A) {
+      compute_f8(buf, nvalid);
+     } else {
       if (wm * MW >= nvalid) return;
       if (wm * MW + MW <= nvalid) {
         compute_full(buf);
@@ -549,8 +674,8 @@ struct Tile {
 #pragma unroll
       for (int jj = 0; jj < KSTEPS / WK; ++jj) {
         const int step = jj * WK + wk;
-        Frag<F32> fa[FM];
-        Frag<F32> fb[NMAT][FN];
+        FragT fa[FM];
+        FragT fb[NMAT][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           if (wm * MW + i * 16 < nvalid) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
@@ -567,6 +692,7 @@ struct Tile {
               for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa[i], fb[mt][j]);
           }
       }
+     }
     };
 
     // ---- epilogue of item j: K-split reduction, then the tile's stores, or the
@@ -786,12 +912,11 @@ MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2, 1)
 MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2, 0)
 #undef MOE_CFG
 
-template <int WKIND>
+template <int PHASE, int WKIND>
 constexpr int lds_bytes() {
   int m = 0;
 #define MOE_LDS(V)                                                                            \
-  m = Cfg<V, 1, WKIND>::R::LDS_BYTES > m ? Cfg<V, 1, WKIND>::R::LDS_BYTES : m;                \
-  m = Cfg<V, 2, WKIND>::R::LDS_BYTES > m ? Cfg<V, 2, WKIND>::R::LDS_BYTES : m;
+  m = Cfg<V, PHASE, WKIND>::R::LDS_BYTES > m ? Cfg<V, PHASE, WKIND>::R::LDS_BYTES : m;
   MOE_LDS(0) MOE_LDS(1) MOE_LDS(2) MOE_LDS(3)
 #undef MOE_LDS
   return m;
@@ -845,7 +970,7 @@ __global__ void __launch_bounds__(kThreads) ffn_fixup_kernel(FfnArgs g) {
 
 template <int PHASE, int WKIND>
 hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
-  constexpr int lds = lds_bytes<WKIND>();
+  constexpr int lds = lds_bytes<PHASE, WKIND>();
   static_assert((lds + 4096) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
   static int done[64] = {0};
   int dev = 0;
@@ -876,20 +1001,32 @@ hipError_t launch_w(const FfnArgs& g, int phases, int grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const void* w1,
+hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const uint8_t* xq,
+                              const float* xs, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,
                               const int32_t* variant, void* y_slots, void* h, float* part,
                               int num_cus, int64_t rows_max, hipStream_t s) {
-  FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
+  FfnArgs g{x, nullptr, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
             h, y_slots, part, p.hidden, p.inter, p.top_k, p.local_experts,
             p.tokens * p.top_k, rows_max};
   const int grid = num_cus * kWgPerCu < kMaxGrid ? num_cus * kWgPerCu : kMaxGrid;
   switch (p.weight_dtype) {
     case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);
     case MOE_BF16: return launch_w<W_BF16>(g, phases, grid, s);
-    case MOE_FP8_E4M3: return launch_w<W_FP8>(g, phases, grid, s);
+    case MOE_FP8_E4M3:
+      if (p.act_quant) {  // gate/up on fp8 x fp8; the down phase as for fp8 weights
+        if (phases & 1) {
+          FfnArgs gq = g;
+          gq.x = xq;
+          gq.xs = xs;
+          const hipError_t e = launch_phase<1, W_FP8A>(gq, grid, s);
+          if (e != hipSuccess) return e;
+        }
+        return (phases & 2) ? launch_phase<2, W_FP8>(g, grid, s) : hipSuccess;
+      }
+      return launch_w<W_FP8>(g, phases, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -30,11 +30,14 @@ moe_status validate(const moe_problem* p) {
   if ((int64_t)p->expert_begin + p->local_experts > p->num_experts) return MOE_ERR_INVALID_ARG;
   if (p->top_k < 1 || p->top_k > 32 || p->top_k > p->num_experts) return MOE_ERR_INVALID_ARG;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (p->act_quant != 0 && p->act_quant != 1) return MOE_ERR_INVALID_ARG;
   const int a = p->act_dtype, w = p->weight_dtype;
   if (a < MOE_F32 || a > MOE_FP8_E4M3 || w < MOE_F32 || w > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && w == MOE_BF16) ||
                   (a == MOE_BF16 && w == MOE_FP8_E4M3);
   if (!ok) return MOE_ERR_UNSUPPORTED;
+  // the FP8 activation path: bf16 activations quantized for fp8-weight GEMMs
+  if (p->act_quant && !(a == MOE_BF16 && w == MOE_FP8_E4M3)) return MOE_ERR_UNSUPPORTED;
   // 32-bit slot and row indices
   const int64_t slots = (int64_t)p->tokens * p->top_k;
   if (slots >= (1ll << 30)) return MOE_ERR_UNSUPPORTED;
@@ -61,6 +64,13 @@ moe_status validate(const moe_problem* p) {
   return MOE_OK;
 }
 
+int64_t quant_bytes(const moe_problem* p) {
+  if (!p->act_quant) return 0;
+  const int64_t q = ((int64_t)p->tokens * p->hidden + 255) / 256 * 256;
+  const int64_t sc = ((int64_t)p->tokens * (p->hidden / 128) * 4 + 255) / 256 * 256;
+  return q + sc;
+}
+
 void sizes_of(const moe_problem* p, moe_sizes* s) {
   const int64_t slots = (int64_t)p->tokens * p->top_k;
   const int64_t active_max = slots < p->local_experts ? slots : p->local_experts;
@@ -70,8 +80,17 @@ void sizes_of(const moe_problem* p, moe_sizes* s) {
   s->y_slots_bytes = s->rows_max * p->hidden * eb;
   int64_t hb = s->rows_max * p->inter * eb;
   hb = (hb + 255) / 256 * 256;
-  s->workspace_bytes = kWsHeader + hb + kPartBytes;
+  s->workspace_bytes = kWsHeader + hb + quant_bytes(p) + kPartBytes;
   s->align_ws_bytes = 0;
+}
+
+// workspace layout: header | h | (act_quant) xq [B][H] u8, xs [B][H/128] f32 | parts
+int64_t h_bytes(const moe_problem* p, int64_t rows_max) {
+  const int64_t hb = rows_max * p->inter * elem_bytes(p->act_dtype);
+  return (hb + 255) / 256 * 256;
+}
+int64_t xq_bytes(const moe_problem* p) {
+  return ((int64_t)p->tokens * p->hidden + 255) / 256 * 256;
 }
 
 int num_cus_current(hipError_t* err) {
@@ -107,7 +126,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
@@ -231,7 +250,17 @@ moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, c
   if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
   void* h = (char*)workspace + kWsHeader;
   float* part = (float*)((char*)workspace + (sz.workspace_bytes - kPartBytes));
-  return hip_status(launch_grouped_ffn(*p, phases, x, w1, w3, w2, fp8 ? s1 : nullptr,
+  uint8_t* xq = nullptr;
+  float* xs = nullptr;
+  if (p->act_quant) {
+    xq = (uint8_t*)workspace + kWsHeader + h_bytes(p, sz.rows_max);
+    xs = (float*)(xq + xq_bytes(p));
+    if (up) {
+      const hipError_t e = launch_quant_act(*p, x, xq, xs, (hipStream_t)stream);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+  }
+  return hip_status(launch_grouped_ffn(*p, phases, x, xq, xs, w1, w3, w2, fp8 ? s1 : nullptr,
                                        fp8 ? s3 : nullptr, fp8 ? s2 : nullptr, sorted_slots,
                                        block_expert, num_blocks, variant, y_slots, h, part, cus,
                                        sz.rows_max, (hipStream_t)stream));
@@ -267,6 +296,16 @@ moe_status moe_grouped_down(const moe_problem* p, const void* w2, const float* s
   return grouped_ffn_phases(2, p, nullptr, nullptr, nullptr, w2, nullptr, nullptr, s2,
                             sorted_slots, block_expert, num_blocks, variant, y_slots, workspace,
                             workspace_bytes, stream);
+}
+
+moe_status moe_quant_act(const moe_problem* p, const void* x, uint8_t* xq, float* xs,
+                         void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!p->act_quant) return MOE_ERR_INVALID_ARG;
+  if (!x || !xq || !xs) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(xq, 8) || !aligned(xs, 4)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quant_act(*p, x, xq, xs, (hipStream_t)stream));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,

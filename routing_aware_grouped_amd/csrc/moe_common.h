@@ -108,8 +108,13 @@ hipError_t launch_route_select_align(const moe_problem& p, const float* logits,
                                      float* w, int32_t* counts, int32_t* variant, float* t_hat,
                                      int32_t* sorted_slots, int32_t* block_expert,
                                      int32_t* num_blocks, int32_t* slot_pos, hipStream_t s);
-// phases: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both (two launches)
-hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const void* w1,
+// FP8 activation quantization: xq [B][H] E4M3FN codes, xs [B][H/128] scales
+hipError_t launch_quant_act(const moe_problem& p, const void* x, uint8_t* xq, float* xs,
+                            hipStream_t s);
+// phases: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both (two launches).
+// With p.act_quant the gate/up phase reads the quantized x (xq, xs) instead of x.
+hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const uint8_t* xq,
+                              const float* xs, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,

@@ -1,0 +1,74 @@
+// quant.hip -- FP8 E4M3FN quantization of the activations, per token and per
+// group of 128 hidden columns (the 1 x 128 activation scaling that goes with the
+// 128 x 128 weight blocks of DeepSeek-V3's FP8 recipe, which RaMP (arXiv
+// 2604.26039) section 3.3 and appendix A.8 use for both expert GEMMs):
+//   s = amax / 448,  q = E4M3FN(clamp(x / s, -448, 448)),  x ~ q * s.
+//
+// Design: one group (128 bf16 = 256 bytes) per 16 lanes, each lane holding one
+// 16-byte chunk of 8 values; the group maximum is a 16-lane xor-shuffle
+// reduction; a 256-thread workgroup covers 16 groups.  fp32 division is the
+// correctly rounded one (HIP's default), and the hardware conversion rounds to
+// nearest even, so the codes match a plain CPU implementation bit for bit.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kGroupsPerWg = kQuantThreads / 16;
+
+__global__ void __launch_bounds__(kQuantThreads)
+quant_act_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s,
+                 int64_t ngroups, int G) {
+  const int l16 = threadIdx.x & 15;
+  // 16 consecutive lanes share a group, so a group's lanes are always all
+  // active together (the shuffles below stay inside the 16 lanes)
+  for (int64_t grp = (int64_t)blockIdx.x * kGroupsPerWg + (threadIdx.x >> 4); grp < ngroups;
+       grp += (int64_t)gridDim.x * kGroupsPerWg) {
+    const int64_t t = grp / G;
+    const int g = (int)(grp - t * G);
+    const int64_t off = (t * G + g) * 128 + l16 * 8;  // = t * H + 128 g + 8 l16
+    const u32x4 v = *(const u32x4*)(x + off);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+    const float sc = amax / 448.0f;
+    u32x2 o;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float r = amax > 0.f ? f[4 * w + i] / sc : 0.f;
+        c[i] = fminf(fmaxf(r, -448.0f), 448.0f);
+      }
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], p, true);
+      o[w] = (uint32_t)p;
+    }
+    *(u32x2*)(q + off) = o;
+    if (l16 == 0) s[grp] = sc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const moe_problem& p, const void* x, uint8_t* xq, float* xs,
+                            hipStream_t s) {
+  const int G = p.hidden / 128;
+  const int64_t ngroups = (int64_t)p.tokens * G;
+  int64_t grid = (ngroups + kGroupsPerWg - 1) / kGroupsPerWg;
+  if (grid > 4096) grid = 4096;
+  quant_act_kernel<<<(int)grid, kQuantThreads, 0, s>>>((const uint16_t*)x, xq, xs, ngroups, G);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -162,7 +162,8 @@ def act_tensor(layer, a):
 def problem_of(layer, renormalize: int = 1) -> moe_problem:
     sh = layer.shape
     return moe_problem(layer.tokens, sh.hidden, sh.inter, sh.num_experts, layer.expert_begin,
-                       sh.local_experts, sh.top_k, sh.act_dtype, sh.weight_dtype, renormalize)
+                       sh.local_experts, sh.top_k, sh.act_dtype, sh.weight_dtype, renormalize,
+                       getattr(sh, "act_quant", 0))
 
 
 def from_layer(layer, theta=None, device="cuda", weights=None, renormalize: int = 1) -> Buffers:

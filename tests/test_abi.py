@@ -34,7 +34,7 @@ def test_binding_mirrors_names():
 
 
 def test_variant_menu_matches_spec():
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
     assert moe.moe_num_variants() == len(spec.MENU)
     for v, m in enumerate(spec.MENU):
         assert tuple(moe.moe_variant_info(v)) == m
@@ -48,7 +48,8 @@ def _p(**kw):
     base = dict(tokens=64, hidden=128, inter=256, num_experts=8, top_k=2, act_dtype=moe.MOE_F32,
                 weight_dtype=moe.MOE_F32)
     base.update(kw)
-    extra = {k: base.pop(k) for k in ("expert_begin", "local_experts", "renormalize") if k in base}
+    extra = {k: base.pop(k) for k in ("expert_begin", "local_experts", "renormalize", "act_quant")
+             if k in base}
     return moe.problem(base.pop("tokens"), base.pop("hidden"), base.pop("inter"),
                        base.pop("num_experts"), base.pop("top_k"), **base, **extra)
 
@@ -84,6 +85,11 @@ def test_query_sizes():
     (dict(act_dtype=moe.MOE_F32, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=moe.MOE_FP8_E4M3, weight_dtype=moe.MOE_FP8_E4M3), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(act_quant=2, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3),
+     moe.MOE_ERR_INVALID_ARG),
+    # the FP8 activation path needs bf16 activations and fp8 weights
+    (dict(act_quant=1, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_quant=1), moe.MOE_ERR_UNSUPPORTED),
     (dict(tokens=1 << 20, num_experts=1024, local_experts=1024, top_k=8), moe.MOE_ERR_UNSUPPORTED),
     # one expert's bf16 weight matrix of 2^31 bytes: beyond the 32-bit buffer offsets
     (dict(hidden=32768, inter=32768, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16),
@@ -96,6 +102,24 @@ def test_invalid_problems(kw, status):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_query_sizes(_p(**kw))
     assert ei.value.status == status
+
+
+def test_act_quant_workspace_holds_codes_and_scales():
+    """With the FP8 activation path the workspace grows by the x codes (B * H bytes)
+    and scales (B * H / 128 floats), each rounded up to 256 bytes."""
+    kw = dict(tokens=37, hidden=7168, inter=2048, num_experts=256, top_k=8, expert_begin=32,
+              local_experts=32, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3)
+    s0 = moe.moe_query_sizes(_p(**kw))
+    s1 = moe.moe_query_sizes(_p(act_quant=1, **kw))
+    up = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    assert s1.workspace_bytes - s0.workspace_bytes == up(37 * 7168) + up(37 * 56 * 4)
+    assert (s1.rows_max, s1.y_slots_bytes) == (s0.rows_max, s0.y_slots_bytes)
+    with pytest.raises(moe.MoeError) as ei:  # quantization without the path
+        moe.moe_quant_act(_p(**kw), 0x1000, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # x misaligned
+        moe.moe_quant_act(_p(act_quant=1, **kw), 0x1008, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
 
 
 def test_largest_expert_matrix_is_accepted():
