@@ -51,6 +51,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5166e15  # flop/s, dense bf16 MFMA (256 CU x 2.4 GHz x 4096)
+MFMA_FP8_PEAK = 2 * MFMA_BF16_PEAK  # flop/s, dense fp8 MFMA (the FP8 activation path's gate/up)
 METRIC = "fused-MoE layer µs + % of HBM/MFMA roofline vs tokens × Dirichlet α skew"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -59,6 +60,9 @@ SWEEPS = {
     "qwen3": dict(tokens=[1, 16, 128, 512, 2048, 4096], alphas=[0.05, 0.3, 1.0, 10.0]),
     "dsv3_share": dict(tokens=[1, 16, 64, 256], alphas=[0.1, 1.0, 10.0]),  # per GPU; B = 8T
     "kimi_share": dict(tokens=[8, 64, 512, 2048, 4096], alphas=[0.05]),
+    # the expert shares again with FP8 activations in the gate/up GEMM
+    "dsv3_share_fp8a": dict(tokens=[1, 16, 64, 256], alphas=[0.1, 1.0, 10.0]),  # B = 8T
+    "kimi_share_fp8a": dict(tokens=[8, 64, 512, 2048, 4096], alphas=[0.05]),
 }
 
 
@@ -86,13 +90,17 @@ def work(layer, ids_np):
     wbytes = A * (3 * H * I * wb + 3 * mat_scale)
     layer_bytes = wbytes + U * H * ab + B * H * ab + B * sh.num_experts * 4 + B * k * 8
     gate_up_bytes = A * (2 * H * I * wb + 2 * mat_scale) + U * H * ab
+    # time the MFMA pipes need at peak: bf16 rate, except the gate/up GEMM of the
+    # FP8 activation path, which runs at the fp8 rate
+    gu_peak = MFMA_FP8_PEAK if getattr(sh, "act_quant", 0) else MFMA_BF16_PEAK
+    mfma_s = 4 * S * H * I / gu_peak + 2 * S * H * I / MFMA_BF16_PEAK
     return dict(S=S, A=A, U=U, flops=6 * S * H * I, layer_bytes=layer_bytes,
-                gate_up_bytes=gate_up_bytes, gate_up_flops=4 * S * H * I,
-                eff_exp=synth.eff_exp(cnt), counts=cnt)
+                gate_up_bytes=gate_up_bytes, gate_up_flops=4 * S * H * I, gate_up_peak=gu_peak,
+                mfma_s=mfma_s, eff_exp=synth.eff_exp(cnt), counts=cnt)
 
 
 def roof_us(w):
-    return max(w["layer_bytes"] / HBM_PEAK, w["flops"] / MFMA_BF16_PEAK) * 1e6
+    return max(w["layer_bytes"] / HBM_PEAK, w["mfma_s"]) * 1e6
 
 
 def kernel_source_hash():
@@ -217,9 +225,9 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
                us_p10=round(t_chosen["p10"], 3), us_p90=round(t_chosen["p90"], 3),
                roof_us=round(roof_us(w), 3),
                hbm_frac=round(w["layer_bytes"] / (t_chosen["median"] * 1e-6) / HBM_PEAK, 4),
-               mfma_frac=round(w["flops"] / (t_chosen["median"] * 1e-6) / MFMA_BF16_PEAK, 4),
+               mfma_frac=round(w["mfma_s"] / (t_chosen["median"] * 1e-6), 4),
                counts=[int(c) for c in w["counts"]], t_hat=[round(x, 4) for x in t_hat])
-    res["binding"] = "hbm" if w["layer_bytes"] / HBM_PEAK >= w["flops"] / MFMA_BF16_PEAK else "mfma"
+    res["binding"] = "hbm" if w["layer_bytes"] / HBM_PEAK >= w["mfma_s"] else "mfma"
     res["roof_frac"] = round(res["roof_us"] / res["us"], 4)
     if exhaustive:
         g_forced = T.graph(lambda: L.forward(b, forced_variant=True))
@@ -285,10 +293,10 @@ def sweep_shape(torch, np, synth, L, T, shape, V, reps, log_prefix=""):
     out = []
     for tok in sw["tokens"]:
         for a in sw["alphas"]:
-            tb = 8 * tok if shape == "dsv3_share" else tok
+            tb = 8 * tok if shape.startswith("dsv3_share") else tok
             r, *_ = run_point(torch, np, synth, L, T, shape, tb, a, wdev, nowts, theta, V, reps, 3,
                               exhaustive=True)
-            if shape == "dsv3_share":
+            if shape.startswith("dsv3_share"):
                 r["tokens_per_gpu"] = tok
             log(f"[bench] {shape} B={tb} alpha={a}: {r['us']:.1f} us, v={r['variant']} "
                 f"best={r['best_variant']} gap={r['gap_to_exhaustive']:.3f} "
@@ -325,7 +333,8 @@ def main():
     ap.add_argument("--shape", default="mixtral", choices=sorted(SWEEPS))
     ap.add_argument("--tokens", type=int, default=128)
     ap.add_argument("--alpha", type=float, default=1.0)
-    ap.add_argument("--sweep", default="mixtral,qwen3,dsv3_share,kimi_share",
+    ap.add_argument("--sweep", default="mixtral,qwen3,dsv3_share,kimi_share,dsv3_share_fp8a,"
+                                       "kimi_share_fp8a",
                     help="comma-separated workloads to sweep ('' for none)")
     ap.add_argument("--sweep-reps", type=int, default=15)
     ap.add_argument("--cpu", type=int, default=1, help="1: time the CPU oracle baseline")
@@ -394,11 +403,12 @@ def main():
 
     # dominant kernel: the grouped gate/up launch (2/3 of the weight bytes and FLOPs)
     t_gu = seg["grouped_gate_up"] * 1e-6
-    bound = "hbm" if w["gate_up_bytes"] / HBM_PEAK >= w["gate_up_flops"] / MFMA_BF16_PEAK else "mfma"
+    gu_peak = w["gate_up_peak"]  # the gate/up GEMM's own dtype: bf16, or fp8 x fp8
+    bound = "hbm" if w["gate_up_bytes"] / HBM_PEAK >= w["gate_up_flops"] / gu_peak else "mfma"
     if bound == "hbm":
         achieved, peak, unit = w["gate_up_bytes"] / t_gu / 1e9, HBM_PEAK / 1e9, "GB/s"
     else:
-        achieved, peak, unit = w["gate_up_flops"] / t_gu / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
+        achieved, peak, unit = w["gate_up_flops"] / t_gu / 1e12, gu_peak / 1e12, "TFLOP/s"
     wl_key = f"{args.shape}:B{args.tokens}:a{args.alpha:g}:v{head['variant']}"
     roofline = dict(bound=bound, achieved=round(achieved, 2), peak=round(peak, 1), unit=unit,
                     frac=round(achieved / peak, 4), traffic=measured_traffic(wl_key),
@@ -452,7 +462,7 @@ def main():
                       us_per_variant=head.get("us_per_variant"), roof_us=head["roof_us"],
                       roof_frac=round(head["roof_us"] / st["median"], 4), binding=head["binding"],
                       hbm_frac=round(w["layer_bytes"] / (st["median"] * 1e-6) / HBM_PEAK, 4),
-                      mfma_frac=round(w["flops"] / (st["median"] * 1e-6) / MFMA_BF16_PEAK, 4),
+                      mfma_frac=round(w["mfma_s"] / (st["median"] * 1e-6), 4),
                       segments_us={k: round(v, 3) for k, v in seg.items()},
                       theta=theta_src or "untuned default (th1 = 1: fewest waves)",
                       timed_wall_s=round(t_wall, 3), p10=round(st["p10"], 3), p90=round(st["p90"], 3)),

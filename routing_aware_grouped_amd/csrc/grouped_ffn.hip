@@ -191,7 +191,6 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
 // ---------------------------------------------------------------------------
 struct FfnArgs {
   const void* x;   // [B][H] act (the fp8 codes on the FP8 activation path)
-  const float* xs; // [B][H/128] activation scales of the FP8 activation path
   const void* w1;  // [E_loc][I][H]
   const void* w3;  // [E_loc][I][H]
   const void* w2;  // [E_loc][H][I]
@@ -209,6 +208,7 @@ struct FfnArgs {
   int E_loc;
   int slots;  // B * k
   int64_t rows_max;
+  const float* xs;  // [B][H/128] activation scales of the FP8 activation path
 };
 
 // ring slots of per-tile metadata (see Tile::run_all)
@@ -1008,9 +1008,9 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               const int32_t* block_expert, const int32_t* num_blocks,
                               const int32_t* variant, void* y_slots, void* h, float* part,
                               int num_cus, int64_t rows_max, hipStream_t s) {
-  FfnArgs g{x, nullptr, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
+  FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
             h, y_slots, part, p.hidden, p.inter, p.top_k, p.local_experts,
-            p.tokens * p.top_k, rows_max};
+            p.tokens * p.top_k, rows_max, nullptr};
   const int grid = num_cus * kWgPerCu < kMaxGrid ? num_cus * kWgPerCu : kMaxGrid;
   switch (p.weight_dtype) {
     case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);

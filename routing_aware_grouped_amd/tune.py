@@ -46,6 +46,8 @@ FIT_TOKENS = {
     "qwen3": [1, 4, 16, 64, 128, 256, 512, 1024, 2048, 4096],
     "dsv3_share": [8, 32, 128, 512, 1024, 2048],      # B = 8 x tokens per GPU
     "kimi_share": [8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096],
+    "dsv3_share_fp8a": [8, 32, 128, 512, 1024, 2048],
+    "kimi_share_fp8a": [8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096],
 }
 FIT_ALPHAS = [0.03, 0.5, 3.0, 30.0]
 FIT_REP0 = 100
