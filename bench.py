@@ -63,6 +63,9 @@ SWEEPS = {
     # the expert shares again with FP8 activations in the gate/up GEMM
     "dsv3_share_fp8a": dict(tokens=[1, 16, 64, 256], alphas=[0.1, 1.0, 10.0]),  # B = 8T
     "kimi_share_fp8a": dict(tokens=[8, 64, 512, 2048, 4096], alphas=[0.05]),
+    # and with FP8 activations in both GEMMs
+    "dsv3_share_fp8ah": dict(tokens=[1, 16, 64, 256], alphas=[0.1, 1.0, 10.0]),  # B = 8T
+    "kimi_share_fp8ah": dict(tokens=[8, 64, 512, 2048, 4096], alphas=[0.05]),
 }
 
 
@@ -90,10 +93,12 @@ def work(layer, ids_np):
     wbytes = A * (3 * H * I * wb + 3 * mat_scale)
     layer_bytes = wbytes + U * H * ab + B * H * ab + B * sh.num_experts * 4 + B * k * 8
     gate_up_bytes = A * (2 * H * I * wb + 2 * mat_scale) + U * H * ab
-    # time the MFMA pipes need at peak: bf16 rate, except the gate/up GEMM of the
-    # FP8 activation path, which runs at the fp8 rate
-    gu_peak = MFMA_FP8_PEAK if getattr(sh, "act_quant", 0) else MFMA_BF16_PEAK
-    mfma_s = 4 * S * H * I / gu_peak + 2 * S * H * I / MFMA_BF16_PEAK
+    # time the MFMA pipes need at peak: bf16 rate, except the GEMMs that the FP8
+    # activation path runs at the fp8 rate (gate/up; with act_quant 2 down too)
+    aq = getattr(sh, "act_quant", 0)
+    gu_peak = MFMA_FP8_PEAK if aq >= 1 else MFMA_BF16_PEAK
+    dn_peak = MFMA_FP8_PEAK if aq == 2 else MFMA_BF16_PEAK
+    mfma_s = 4 * S * H * I / gu_peak + 2 * S * H * I / dn_peak
     return dict(S=S, A=A, U=U, flops=6 * S * H * I, layer_bytes=layer_bytes,
                 gate_up_bytes=gate_up_bytes, gate_up_flops=4 * S * H * I, gate_up_peak=gu_peak,
                 mfma_s=mfma_s, eff_exp=synth.eff_exp(cnt), counts=cnt)
@@ -334,7 +339,7 @@ def main():
     ap.add_argument("--tokens", type=int, default=128)
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--sweep", default="mixtral,qwen3,dsv3_share,kimi_share,dsv3_share_fp8a,"
-                                       "kimi_share_fp8a",
+                                       "kimi_share_fp8a,dsv3_share_fp8ah,kimi_share_fp8ah",
                     help="comma-separated workloads to sweep ('' for none)")
     ap.add_argument("--sweep-reps", type=int, default=15)
     ap.add_argument("--cpu", type=int, default=1, help="1: time the CPU oracle baseline")

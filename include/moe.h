@@ -52,7 +52,11 @@
  *     instructions, applying the activation and weight block scales to each
  *     128-deep partial sum (RaMP section 3.3 and appendix A.8: FP8 GEMMs with
  *     128 x 128 block scaling as used by DeepSeek-V3).  h stays bf16 and the down
- *     GEMM is unchanged.
+ *     GEMM is unchanged.  act_quant = 2 also quantizes h (bf16, as the gate/up
+ *     GEMM stores it) the same way, per slot row and 128-column group, at the
+ *     start of the down phase, and runs the down GEMM on fp8 x fp8 too (RaMP
+ *     appendix A.8 quantizes the gated activation to FP8 before the down
+ *     projection).
  *   - Concurrent calls must not share one workspace or output buffer.
  */
 #ifndef MOE_MI355X_H
@@ -92,8 +96,9 @@ typedef struct moe_problem {
   int32_t weight_dtype;  /* moe_dtype of W1, W3, W2                             */
   int32_t renormalize;   /* 1: softmax over the k chosen logits (default);
                             0: those experts' values of the softmax over all E  */
-  int32_t act_quant;     /* 0: none (default); 1: FP8 activation path (see above;
-                            needs act_dtype MOE_BF16, weight_dtype MOE_FP8_E4M3) */
+  int32_t act_quant;     /* 0: none (default); 1: x in FP8 for the gate/up GEMM;
+                            2: x and h in FP8 for both GEMMs (see above; needs
+                            act_dtype MOE_BF16, weight_dtype MOE_FP8_E4M3)      */
 } moe_problem;
 
 /* Buffer sizes a caller must provide for one problem. */
@@ -102,7 +107,7 @@ typedef struct moe_sizes {
   int64_t blocks_max;      /* capacity (elements) of block_expert                  */
   int64_t y_slots_bytes;   /* rows_max * H * sizeof(act)                           */
   int64_t workspace_bytes; /* grouped_ffn workspace: header, h, (act_quant: x codes
-                              and scales), partial tiles                            */
+                              and scales; 2: h codes and scales), partial tiles     */
   int64_t align_ws_bytes;  /* reserved, 0 in this version                          */
 } moe_sizes;
 
@@ -206,7 +211,7 @@ moe_status moe_route_select_align(const moe_problem* p, const float* logits, con
  *                     rounds to zero gives 0x80),
  * and a group of zeros gets xs = 0 and codes 0x00.  x = q * s then holds to
  * within half a code step.  xq uint8 [B][H], xs f32 [B][H/128], device memory.
- * Requires act_quant = 1; errors as the other calls. */
+ * Requires act_quant = 1 or 2; errors as the other calls. */
 moe_status moe_quant_act(const moe_problem* p, const void* x, uint8_t* xq, float* xs,
                          void* stream);
 
@@ -240,7 +245,9 @@ moe_status moe_grouped_gate_up(const moe_problem* p, const void* x, const void* 
                                size_t workspace_bytes, void* stream);
 
 /* Step 4b alone: the grouped down GEMM, y_slots[r] = h[r] W2_e^T with h read from
- * workspace (written by moe_grouped_gate_up for the same grouping and variant).
+ * workspace (written by moe_grouped_gate_up for the same grouping and variant;
+ * with act_quant = 2 the rows of h that hold a slot are first quantized in the
+ * workspace, as moe_quant_act does for x).
  * Arguments and errors as for moe_grouped_ffn; x, w1, w3, s1 and s3 are not
  * used. */
 moe_status moe_grouped_down(const moe_problem* p, const void* w2, const float* s2,

@@ -59,9 +59,10 @@ def lib():
         L.oracle_select.argtypes = [i32, P, i32, P, P, P, P, P, P, P, P]
         L.oracle_align.argtypes = [i32, i32, i32, i32, P, i32, P, i64, P, P, P]
         L.oracle_align.restype = i64
-        L.oracle_ffn_slots.argtypes = [i32, i32, P, i32, P, P, P, i32, P, P, P, i32, P, P, P, i32]
+        L.oracle_ffn_slots.argtypes = [i32, i32, P, i32, P, P, P, i32, P, P, P, i32, P, P, P, i32,
+                                       i32]
         L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, P, i32, P, P, P, i32, P, P, P,
-                                          P, P, i32, P, P, i32]
+                                          P, P, i32, P, P, i32, i32]
         L.oracle_decode_fp8.argtypes = [P, i64, P]
         L.oracle_decode_fp8.restype = None
         L.oracle_decode_bf16.argtypes = [P, i64, P]
@@ -166,6 +167,11 @@ def dequant_act(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return decode_fp8(q) * np.repeat(np.asarray(s, np.float64), 128, axis=1)[:, :H]
 
 
+def _h_quant(layer) -> int:
+    """1 when the layer also quantizes h before the down projection (act_quant 2)."""
+    return int(getattr(layer.shape, "act_quant", 0) == 2)
+
+
 def _act_args(layer, tokens: np.ndarray):
     """The activation rows the FFN uses for `tokens`: (buffer, dtype, token
     indices into it).  With the FP8 activation path these are the dequantized
@@ -196,7 +202,7 @@ def ffn_slots(layer, tok: np.ndarray, exp_local: np.ndarray, nthreads: int | Non
     y = np.empty((len(tok), H), np.float64)
     rc = lib().oracle_ffn_slots(H, I, _p(x), xdt, _p(w1), _p(w3), _p(w2), wd, _p(s1), _p(s3),
                                 _p(s2), len(tok), _p(tok), _p(el), _p(y),
-                                nthreads or max_threads())
+                                nthreads or max_threads(), _h_quant(layer))
     if rc != 0:
         raise RuntimeError(f"oracle_ffn_slots rc={rc}")
     return y
@@ -221,7 +227,7 @@ def layer_tokens(layer, ids: np.ndarray, w: np.ndarray, tokens: np.ndarray,
     rc = lib().oracle_layer_tokens(H, I, k, layer.expert_begin, layer.shape.local_experts,
                                    _p(x), xdt, _p(w1), _p(w3), _p(w2), wd, _p(s1), _p(s3),
                                    _p(s2), _p(ids), _p(w), len(toks), _p(toks), _p(Y),
-                                   nthreads or max_threads())
+                                   nthreads or max_threads(), _h_quant(layer))
     if rc != 0:
         raise RuntimeError(f"oracle_layer_tokens rc={rc}")
     return Y

@@ -29,7 +29,11 @@
  *                token and per group of 128 hidden columns with an fp32 scale
  *                (RaMP 3.3 and A.8: FP8 with 128 x 128 block scaling as used by
  *                DeepSeek-V3, whose activations are scaled per 1 x 128 group);
- *                the expert FFN then runs on the dequantized x = q * s.
+ *                the expert FFN then runs on the dequantized x = q * s.  With h
+ *                quantization as well (RaMP A.8 quantizes the gated activation to
+ *                FP8 before the down projection), h is rounded to bf16 (the
+ *                intermediate precision) and quantized the same way, per slot row
+ *                and 128-column group, and the down projection uses q * s.
  *
  * Readings of points the pages leave open (each stated where it is used):
  *  - top-k compares raw fp32 logits; equal logits go to the lower expert index
@@ -163,6 +167,29 @@ int oracle_quant_act_e4m3(int B, int H, const uint16_t* x, uint8_t* q, float* s)
       }
     }
   return 0;
+}
+
+/* h quantization of one row of n (a multiple of 128) values, in place: each value
+ * rounded to bf16 (fp64 -> fp32 -> bf16, each to nearest even: the row is held in
+ * fp32 and stored as bf16 before it is quantized), then Q on the bf16 row, and the
+ * row replaced by the dequantized q * s. */
+static void orc_quant_row(int n, double* a) {
+  uint16_t* bits = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n);
+  uint8_t* q = (uint8_t*)malloc((size_t)n);
+  float* s = (float*)malloc(sizeof(float) * (size_t)(n / 128));
+  if (!bits || !q || !s) abort();
+  for (int i = 0; i < n; ++i) {
+    float f = (float)a[i];
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u); /* round to nearest even on the upper half */
+    bits[i] = (uint16_t)(u >> 16);
+  }
+  oracle_quant_act_e4m3(1, n, bits, q, s);
+  for (int i = 0; i < n; ++i) a[i] = oracle_fp8_e4m3fn_to_f64(q[i]) * (double)s[i / 128];
+  free(bits);
+  free(q);
+  free(s);
 }
 
 /* Finite float inputs only: the nearest E4M3FN codes of n fp32 values |v| <= 448
@@ -310,7 +337,7 @@ int64_t oracle_align(int B, int k, int e0, int E_loc, const int32_t* ids, int b,
  *   y_d = sum_i a_i W2[e][d][i]                                               */
 static void orc_expert_ffn(int H, int I, const double* x, const void* w1, const void* w3,
                            const void* w2, int wdt, const float* s1, const float* s3,
-                           const float* s2, int e, double* a, double* y) {
+                           const float* s2, int e, double* a, double* y, int hq) {
   for (int i = 0; i < I; ++i) {
     double g = 0.0, u = 0.0;
     for (int h = 0; h < H; ++h) {
@@ -319,6 +346,7 @@ static void orc_expert_ffn(int H, int I, const double* x, const void* w1, const 
     }
     a[i] = g / (1.0 + exp(-g)) * u;
   }
+  if (hq) orc_quant_row(I, a);
   for (int d = 0; d < H; ++d) {
     double acc = 0.0;
     for (int i = 0; i < I; ++i) acc += a[i] * orc_weight(w2, wdt, s2, e, H, I, d, i);
@@ -330,7 +358,7 @@ static void orc_expert_ffn(int H, int I, const double* x, const void* w1, const 
 int oracle_ffn_slots(int H, int I, const void* x, int xdt, const void* w1, const void* w3,
                      const void* w2, int wdt, const float* s1, const float* s3, const float* s2,
                      int n, const int32_t* tok, const int32_t* exp_local, double* y,
-                     int nthreads) {
+                     int nthreads, int hq) {
   int err = 0;
   if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1) reduction(| : err)
@@ -341,7 +369,7 @@ int oracle_ffn_slots(int H, int I, const void* x, int xdt, const void* w1, const
       err |= 1;
     } else {
       for (int h = 0; h < H; ++h) xr[h] = orc_act(x, xdt, (int64_t)tok[i] * H + h);
-      orc_expert_ffn(H, I, xr, w1, w3, w2, wdt, s1, s3, s2, exp_local[i], a, y + (int64_t)i * H);
+      orc_expert_ffn(H, I, xr, w1, w3, w2, wdt, s1, s3, s2, exp_local[i], a, y + (int64_t)i * H, hq);
     }
     free(xr);
     free(a);
@@ -357,7 +385,7 @@ int oracle_ffn_slots(int H, int I, const void* x, int xdt, const void* w1, const
 int oracle_layer_tokens(int H, int I, int k, int e0, int E_loc, const void* x, int xdt,
                         const void* w1, const void* w3, const void* w2, int wdt, const float* s1,
                         const float* s3, const float* s2, const int32_t* ids, const double* w,
-                        int n_tok, const int32_t* tokens, double* Y, int nthreads) {
+                        int n_tok, const int32_t* tokens, double* Y, int nthreads, int hq) {
   int err = 0;
   if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1) reduction(| : err)
@@ -375,7 +403,7 @@ int oracle_layer_tokens(int H, int I, int k, int e0, int E_loc, const void* x, i
       for (int j = 0; j < k; ++j) {
         int e = ids[(int64_t)t * k + j] - e0;
         if (e < 0 || e >= E_loc) continue;
-        orc_expert_ffn(H, I, xr, w1, w3, w2, wdt, s1, s3, s2, e, a, ys);
+        orc_expert_ffn(H, I, xr, w1, w3, w2, wdt, s1, s3, s2, e, a, ys, hq);
         double g = w[(int64_t)t * k + j];
         for (int d = 0; d < H; ++d) out[d] += g * ys[d];
       }

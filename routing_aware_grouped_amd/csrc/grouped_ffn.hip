@@ -80,8 +80,8 @@ struct Types<W_FP8> {
   using Out = uint16_t;
   static constexpr int asz = 2, wsz = 1;
 };
-// FP8 activation path, gate/up phase: fp8 x (one fp32 scale per token and 128
-// columns), fp8 weights, bf16 h
+// FP8 activation path: fp8 x or h (one fp32 scale per row and 128 columns), fp8
+// weights, bf16 output (h or y_slots)
 template <>
 struct Types<W_FP8A> {
   using Act = uint8_t;
@@ -235,8 +235,7 @@ struct Tile {
   using Out = typename T::Out;
   static constexpr bool F32 = WKIND == W_F32;
   static constexpr bool FP8 = WKIND == W_FP8;    // fp8 weights decoded to bf16
-  static constexpr bool FP8A = WKIND == W_FP8A;  // fp8 x fp8 (gate/up phase only)
-  static_assert(!FP8A || PHASE == 1, "the FP8 activation path covers the gate/up GEMM");
+  static constexpr bool FP8A = WKIND == W_FP8A;  // fp8 x fp8
   using FragT = Frag<F32 ? W_F32 : (FP8A ? W_FP8A : W_BF16)>;
   static constexpr int ASZ = T::asz, WSZ = T::wsz;
   static constexpr int NMAT = PHASE == 1 ? 2 : 1;
@@ -443,12 +442,14 @@ struct Tile {
                                         : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
     uint32_t l_aoff[NA];
-    // FP8 activation path: thread tid < BM * KB loads the x scale of tile row
-    // tid % BM, block tid / BM of each stage (l_xsoff: that row's scale row, or
-    // kOob); threads tid < NMAT * KB load the weight scale of matrix tid / KB,
-    // block tid % KB (l_wsbase: the tile's first scale of its 128-row block)
+    // FP8 activation path: thread tid < BM * KB loads the A scale (x: per token;
+    // h: per padded row) of tile row tid % BM, block tid / BM of each stage
+    // (l_xsoff: that row's scale row, or kOob); threads tid < NMAT * KB load the
+    // weight scale of matrix tid / KB, block tid % KB (l_wsbase: the tile's first
+    // scale of its 128-row block)
+    const uint32_t a_rows = PHASE == 1 ? (uint32_t)(g.slots / g.k) : (uint32_t)g.rows_max;
     const __amdgpu_buffer_rsrc_t xs_rsrc =
-        make_rsrc(g.xs, FP8A ? (uint32_t)(g.slots / g.k) * (uint32_t)(K / 128) * 4u : 0u);
+        make_rsrc(g.xs, FP8A ? a_rows * (uint32_t)(K / 128) * 4u : 0u);
     uint32_t l_xsoff = kOob;
     int64_t l_wsbase = 0;
     // weights: per tile, a buffer from row n0 of the tile's expert matrix to its
@@ -492,8 +493,9 @@ struct Tile {
       }
       if constexpr (FP8A) {
         const int sl = m[tid % BM];
+        const int srow = PHASE == 1 ? sl / g.k : rb * BM + tid % BM;
         l_xsoff = (l_eok && tid < BM * KB && sl >= 0 && sl < g.slots)
-                      ? (uint32_t)(sl / g.k) * (uint32_t)(K / 128) * 4u + (uint32_t)(tid / BM) * 4u
+                      ? (uint32_t)srow * (uint32_t)(K / 128) * 4u + (uint32_t)(tid / BM) * 4u
                       : kOob;
         l_wsbase = l_eok ? ((int64_t)l_e * (N / 128) + l_n0 / 128) * (K / 128) : 0;
       }
@@ -1002,7 +1004,7 @@ hipError_t launch_w(const FfnArgs& g, int phases, int grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const uint8_t* xq,
-                              const float* xs, const void* w1,
+                              const float* xs, const uint8_t* hq, const float* hs, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,
@@ -1024,7 +1026,14 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
           const hipError_t e = launch_phase<1, W_FP8A>(gq, grid, s);
           if (e != hipSuccess) return e;
         }
-        return (phases & 2) ? launch_phase<2, W_FP8>(g, grid, s) : hipSuccess;
+        if (!(phases & 2)) return hipSuccess;
+        if (p.act_quant == 2) {  // down on fp8 h x fp8 weights; output y_slots
+          FfnArgs gh = g;
+          gh.h = const_cast<uint8_t*>(hq);  // read only in the down phase
+          gh.xs = hs;
+          return launch_phase<2, W_FP8A>(gh, grid, s);
+        }
+        return launch_phase<2, W_FP8>(g, grid, s);
       }
       return launch_w<W_FP8>(g, phases, grid, s);
     default: return hipErrorInvalidValue;

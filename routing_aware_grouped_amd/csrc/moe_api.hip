@@ -30,7 +30,7 @@ moe_status validate(const moe_problem* p) {
   if ((int64_t)p->expert_begin + p->local_experts > p->num_experts) return MOE_ERR_INVALID_ARG;
   if (p->top_k < 1 || p->top_k > 32 || p->top_k > p->num_experts) return MOE_ERR_INVALID_ARG;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID_ARG;
-  if (p->act_quant != 0 && p->act_quant != 1) return MOE_ERR_INVALID_ARG;
+  if (p->act_quant < 0 || p->act_quant > 2) return MOE_ERR_INVALID_ARG;
   const int a = p->act_dtype, w = p->weight_dtype;
   if (a < MOE_F32 || a > MOE_FP8_E4M3 || w < MOE_F32 || w > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && w == MOE_BF16) ||
@@ -64,11 +64,25 @@ moe_status validate(const moe_problem* p) {
   return MOE_OK;
 }
 
+// codes and scales of n rows of m columns, each rounded up to 256 bytes
+int64_t codes_bytes(int64_t n, int64_t m) { return (n * m + 255) / 256 * 256; }
+int64_t scales_bytes(int64_t n, int64_t m) { return (n * (m / 128) * 4 + 255) / 256 * 256; }
+
+int64_t rows_max_of(const moe_problem* p) {
+  const int64_t slots = (int64_t)p->tokens * p->top_k;
+  const int64_t active_max = slots < p->local_experts ? slots : p->local_experts;
+  return slots + active_max * (kMaxBlockM - 1);
+}
+
+// x codes and scales (act_quant >= 1), then h codes and scales (act_quant == 2)
 int64_t quant_bytes(const moe_problem* p) {
-  if (!p->act_quant) return 0;
-  const int64_t q = ((int64_t)p->tokens * p->hidden + 255) / 256 * 256;
-  const int64_t sc = ((int64_t)p->tokens * (p->hidden / 128) * 4 + 255) / 256 * 256;
-  return q + sc;
+  int64_t b = 0;
+  if (p->act_quant >= 1) b += codes_bytes(p->tokens, p->hidden) + scales_bytes(p->tokens, p->hidden);
+  if (p->act_quant == 2) {
+    const int64_t r = rows_max_of(p);
+    b += codes_bytes(r, p->inter) + scales_bytes(r, p->inter);
+  }
+  return b;
 }
 
 void sizes_of(const moe_problem* p, moe_sizes* s) {
@@ -89,9 +103,7 @@ int64_t h_bytes(const moe_problem* p, int64_t rows_max) {
   const int64_t hb = rows_max * p->inter * elem_bytes(p->act_dtype);
   return (hb + 255) / 256 * 256;
 }
-int64_t xq_bytes(const moe_problem* p) {
-  return ((int64_t)p->tokens * p->hidden + 255) / 256 * 256;
-}
+
 
 int num_cus_current(hipError_t* err) {
   static int cache[64] = {0};
@@ -252,15 +264,34 @@ moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, c
   float* part = (float*)((char*)workspace + (sz.workspace_bytes - kPartBytes));
   uint8_t* xq = nullptr;
   float* xs = nullptr;
+  uint8_t* hq = nullptr;
+  float* hs = nullptr;
   if (p->act_quant) {
     xq = (uint8_t*)workspace + kWsHeader + h_bytes(p, sz.rows_max);
-    xs = (float*)(xq + xq_bytes(p));
+    xs = (float*)(xq + codes_bytes(p->tokens, p->hidden));
+    if (p->act_quant == 2) {
+      hq = (uint8_t*)xs + scales_bytes(p->tokens, p->hidden);
+      hs = (float*)(hq + codes_bytes(sz.rows_max, p->inter));
+    }
     if (up) {
       const hipError_t e = launch_quant_act(*p, x, xq, xs, (hipStream_t)stream);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
   }
-  return hip_status(launch_grouped_ffn(*p, phases, x, xq, xs, w1, w3, w2, fp8 ? s1 : nullptr,
+  if (up && down) {  // two calls, so that h is quantized between the phases
+    const moe_status st1 = hip_status(launch_grouped_ffn(
+        *p, 1, x, xq, xs, nullptr, nullptr, w1, w3, w2, fp8 ? s1 : nullptr, fp8 ? s3 : nullptr,
+        fp8 ? s2 : nullptr, sorted_slots, block_expert, num_blocks, variant, y_slots, h, part, cus,
+        sz.rows_max, (hipStream_t)stream));
+    if (st1 != MOE_OK) return st1;
+  }
+  if (down && p->act_quant == 2) {
+    const hipError_t e = launch_quant_h(*p, h, hq, hs, sorted_slots, num_blocks, variant,
+                                        sz.rows_max, (hipStream_t)stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (up && down) phases = 2;
+  return hip_status(launch_grouped_ffn(*p, phases, x, xq, xs, hq, hs, w1, w3, w2, fp8 ? s1 : nullptr,
                                        fp8 ? s3 : nullptr, fp8 ? s2 : nullptr, sorted_slots,
                                        block_expert, num_blocks, variant, y_slots, h, part, cus,
                                        sz.rows_max, (hipStream_t)stream));

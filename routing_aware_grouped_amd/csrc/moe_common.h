@@ -111,10 +111,16 @@ hipError_t launch_route_select_align(const moe_problem& p, const float* logits,
 // FP8 activation quantization: xq [B][H] E4M3FN codes, xs [B][H/128] scales
 hipError_t launch_quant_act(const moe_problem& p, const void* x, uint8_t* xq, float* xs,
                             hipStream_t s);
+// the same for the rows of h [rows_max][I] that hold a slot, among the rows the
+// chosen configuration's row-blocks cover (read from device memory)
+hipError_t launch_quant_h(const moe_problem& p, const void* h, uint8_t* hq, float* hs,
+                          const int32_t* sorted_slots, const int32_t* num_blocks,
+                          const int32_t* variant, int64_t rows_max, hipStream_t s);
 // phases: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both (two launches).
-// With p.act_quant the gate/up phase reads the quantized x (xq, xs) instead of x.
+// With p.act_quant the gate/up phase reads the quantized x (xq, xs) instead of x,
+// and with act_quant 2 the down phase reads the quantized h (hq, hs).
 hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const uint8_t* xq,
-                              const float* xs, const void* w1,
+                              const float* xs, const uint8_t* hq, const float* hs, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,

@@ -4,6 +4,11 @@
 // 2604.26039) section 3.3 and appendix A.8 use for both expert GEMMs):
 //   s = amax / 448,  q = E4M3FN(clamp(x / s, -448, 448)),  x ~ q * s.
 //
+// The same quantization serves h before the down GEMM (RaMP appendix A.8
+// quantizes the gated activation to FP8): there the rows are the padded slot rows
+// of the expert grouping, their count comes from device memory (the chosen
+// configuration's BLOCK_M times the row-block count) and padding rows are skipped.
+//
 // Design: one group (128 bf16 = 256 bytes) per 16 lanes, each lane holding one
 // 16-byte chunk of 8 values; the group maximum is a 16-lane xor-shuffle
 // reduction; a 256-thread workgroup covers 16 groups.  fp32 division is the
@@ -17,16 +22,29 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kGroupsPerWg = kQuantThreads / 16;
 
+// PADDED: rows are slot rows of h; only rows r < num_blocks * BLOCK_M of the chosen
+// configuration with sorted_slots[r] >= 0 are quantized
+template <bool PADDED>
 __global__ void __launch_bounds__(kQuantThreads)
 quant_act_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s,
-                 int64_t ngroups, int G) {
+                 int64_t ngroups, int G, const int32_t* __restrict__ sorted_slots,
+                 const int32_t* __restrict__ num_blocks, const int32_t* __restrict__ variant) {
   const int l16 = threadIdx.x & 15;
+  if constexpr (PADDED) {
+    const int v = *variant;
+    const int64_t nb = *num_blocks;
+    const int64_t rows = (v >= 0 && v < kNumVariants && nb > 0) ? nb * kVariants[v].bm : 0;
+    ngroups = rows * G < ngroups ? rows * G : ngroups;
+  }
   // 16 consecutive lanes share a group, so a group's lanes are always all
   // active together (the shuffles below stay inside the 16 lanes)
   for (int64_t grp = (int64_t)blockIdx.x * kGroupsPerWg + (threadIdx.x >> 4); grp < ngroups;
        grp += (int64_t)gridDim.x * kGroupsPerWg) {
     const int64_t t = grp / G;
     const int g = (int)(grp - t * G);
+    if constexpr (PADDED) {
+      if (sorted_slots[t] < 0) continue;  // a padding row (uniform over the 16 lanes)
+    }
     const int64_t off = (t * G + g) * 128 + l16 * 8;  // = t * H + 128 g + 8 l16
     const u32x4 v = *(const u32x4*)(x + off);
     float f[8];
@@ -67,7 +85,20 @@ hipError_t launch_quant_act(const moe_problem& p, const void* x, uint8_t* xq, fl
   const int64_t ngroups = (int64_t)p.tokens * G;
   int64_t grid = (ngroups + kGroupsPerWg - 1) / kGroupsPerWg;
   if (grid > 4096) grid = 4096;
-  quant_act_kernel<<<(int)grid, kQuantThreads, 0, s>>>((const uint16_t*)x, xq, xs, ngroups, G);
+  quant_act_kernel<false><<<(int)grid, kQuantThreads, 0, s>>>((const uint16_t*)x, xq, xs, ngroups,
+                                                               G, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_h(const moe_problem& p, const void* h, uint8_t* hq, float* hs,
+                          const int32_t* sorted_slots, const int32_t* num_blocks,
+                          const int32_t* variant, int64_t rows_max, hipStream_t s) {
+  const int G = p.inter / 128;
+  const int64_t ngroups = rows_max * G;  // the device count bounds it further
+  int64_t grid = (ngroups + kGroupsPerWg - 1) / kGroupsPerWg;
+  if (grid > 4096) grid = 4096;
+  quant_act_kernel<true><<<(int)grid, kQuantThreads, 0, s>>>((const uint16_t*)h, hq, hs, ngroups,
+                                                              G, sorted_slots, num_blocks, variant);
   return hipGetLastError();
 }
 

@@ -48,6 +48,8 @@ FIT_TOKENS = {
     "kimi_share": [8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096],
     "dsv3_share_fp8a": [8, 32, 128, 512, 1024, 2048],
     "kimi_share_fp8a": [8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096],
+    "dsv3_share_fp8ah": [8, 32, 128, 512, 1024, 2048],
+    "kimi_share_fp8ah": [8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096],
 }
 FIT_ALPHAS = [0.03, 0.5, 3.0, 30.0]
 FIT_REP0 = 100

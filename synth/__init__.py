@@ -45,7 +45,7 @@ class Shape:
     weight_dtype: int
     out_dtype: int
     logits: str  # "normal" (tiny) or "dirichlet"
-    act_quant: int = 0  # 1: the layer runs its gate/up GEMM on FP8 E4M3 activations
+    act_quant: int = 0  # FP8 E4M3 activations: 1 in the gate/up GEMM, 2 in both GEMMs
 
 
 SHAPES = {
@@ -63,10 +63,17 @@ SHAPES = {
     # a small fp8 layer for parity at sizes the oracle runs in seconds: a ragged
     # number of 128-column groups, so that stages of 256 and 512 are partly empty
     "small_fp8a": Shape("small_fp8a", 384, 256, 8, 8, 2, BF16, FP8, BF16, "dirichlet", 1),
+    # FP8 activations in both GEMMs (h quantized before the down projection)
+    "dsv3_share_fp8ah": Shape("dsv3_share_fp8ah", 7168, 2048, 256, 32, 8, BF16, FP8, BF16,
+                              "dirichlet", 2),
+    "kimi_share_fp8ah": Shape("kimi_share_fp8ah", 7168, 2048, 384, 48, 8, BF16, FP8, BF16,
+                              "dirichlet", 2),
+    "small_fp8ah": Shape("small_fp8ah", 384, 256, 8, 8, 2, BF16, FP8, BF16, "dirichlet", 2),
 }
 
 CFG_INDEX = {"tiny": 1, "mixtral": 2, "qwen3": 3, "dsv3_share": 4, "kimi_share": 5,
-             "dsv3_share_fp8a": 4, "kimi_share_fp8a": 5, "small_fp8a": 6}
+             "dsv3_share_fp8a": 4, "kimi_share_fp8a": 5, "small_fp8a": 6,
+             "dsv3_share_fp8ah": 4, "kimi_share_fp8ah": 5, "small_fp8ah": 6}
 
 
 def seed_seq(shape: str, tokens: int, alpha: float | None, rep: int) -> np.random.SeedSequence:

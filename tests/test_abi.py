@@ -85,8 +85,9 @@ def test_query_sizes():
     (dict(act_dtype=moe.MOE_F32, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=moe.MOE_FP8_E4M3, weight_dtype=moe.MOE_FP8_E4M3), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=7), moe.MOE_ERR_INVALID_ARG),
-    (dict(act_quant=2, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3),
+    (dict(act_quant=3, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3),
      moe.MOE_ERR_INVALID_ARG),
+    (dict(act_quant=2, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
     # the FP8 activation path needs bf16 activations and fp8 weights
     (dict(act_quant=1, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_quant=1), moe.MOE_ERR_UNSUPPORTED),
@@ -114,6 +115,10 @@ def test_act_quant_workspace_holds_codes_and_scales():
     up = lambda n: (n + 255) // 256 * 256  # noqa: E731
     assert s1.workspace_bytes - s0.workspace_bytes == up(37 * 7168) + up(37 * 56 * 4)
     assert (s1.rows_max, s1.y_slots_bytes) == (s0.rows_max, s0.y_slots_bytes)
+    # act_quant 2 adds h codes and scales for every slot row
+    s2 = moe.moe_query_sizes(_p(act_quant=2, **kw))
+    R = s0.rows_max
+    assert s2.workspace_bytes - s1.workspace_bytes == up(R * 2048) + up(R * 16 * 4)
     with pytest.raises(moe.MoeError) as ei:  # quantization without the path
         moe.moe_quant_act(_p(**kw), 0x1000, 0x1000, 0x1000, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG

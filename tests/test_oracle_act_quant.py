@@ -116,3 +116,41 @@ def test_lossless_grid_makes_fp8a_layer_equal_plain_layer(oracle_lib):
     y_p = oracle_lib.layer_tokens(plain, ids, w, toks)
     np.testing.assert_array_equal(y_q, y_p)
     assert np.abs(y_p).max() > 0
+
+
+def _torch_quant_rows(a: np.ndarray) -> np.ndarray:
+    """Q written with torch ops on bf16 rows: per 128-column group s = amax / 448,
+    q = float8_e4m3fn(clamp(x / s)); returns q * s in fp64."""
+    xf = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).float()
+    n, m = xf.shape
+    g = xf.reshape(n, m // 128, 128)
+    s = g.abs().amax(dim=2) / 448.0
+    q = (g / torch.where(s > 0, s, torch.ones_like(s))[..., None]).clamp(-448.0, 448.0)
+    q = q.to(torch.float8_e4m3fn).to(torch.float64)
+    q[(s == 0)[..., None].expand_as(q)] = 0.0
+    return (q * s.double()[..., None]).reshape(n, m).numpy()
+
+
+def test_one_hot_router_with_fp8_x_and_h_is_quantized_dense_ffn(oracle_lib):
+    """All tokens on one expert ("Decoding the Skew" III-C3) with x and h both
+    quantized: the dense FFN with torch's quantization of x, h rounded through fp32
+    to bf16 and quantized the same way, and fp64 matrix products."""
+    rng = np.random.default_rng(21)
+    T, E, H, I = 9, 4, 256, 384
+    shape = synth.Shape("t", H, I, E, E, 1, synth.BF16, synth.F32, synth.BF16, "normal", 2)
+    x = synth.to_bf16_bits((rng.standard_normal((T, H)) * 0.5).astype(np.float32))
+    w = {n: (rng.standard_normal((E,) + s) * 0.1).astype(np.float32)
+         for n, s in (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I)))}
+    lg = np.full((T, E), -5.0, np.float32)
+    lg[:, 1] = 3.0
+    lay = synth.Layer(shape, T, None, 0, lg, x, w["w1"], w["w3"], w["w2"])
+    out = oracle_lib.full_layer(lay, b=16)
+    xq = _torch_quant_rows(synth.bf16_bits_to_f32(x))
+    g = xq @ w["w1"][1].astype(np.float64).T
+    u = xq @ w["w3"][1].astype(np.float64).T
+    hq = _torch_quant_rows((g / (1.0 + np.exp(-g)) * u).astype(np.float32))
+    ref = hq @ w["w2"][1].astype(np.float64).T
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-10, atol=1e-12)
+    # and h quantization does change the result (the flag reaches the oracle)
+    plain = oracle_lib.full_layer(dataclasses.replace(lay, shape=dataclasses.replace(shape, act_quant=1)), b=16)
+    assert np.abs(plain["Y"] - out["Y"]).max() > 1e-6 * np.abs(ref).max()
