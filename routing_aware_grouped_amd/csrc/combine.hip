@@ -8,50 +8,76 @@
 // all on other GPUs get zeros.  Gather form (each token reads its own k rows), so
 // the result is deterministic without atomics.
 //
-// Design: one workgroup per token (grid-stride), 16-byte vector loads and stores
-// along H; the token's slot rows and weights are workgroup-uniform (scalar loads).
+// Design: a workgroup takes one token and a chunk of 256 16-byte vectors along H
+// (grid-stride over tokens x chunks, so a small batch still spreads over many
+// workgroups).  The token's slot rows and weights are read once into LDS; each
+// thread then issues the loads of up to 8 slot rows before it adds them, so the
+// k row reads overlap instead of waiting one after another.
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
+constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 8;  // slot rows loaded before they are added
+
 template <bool F32>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slot_pos,
                const float* __restrict__ w, void* __restrict__ y, int B, int H, int k,
-               int64_t rows_max) {
+               int64_t rows_max, int chunks) {
   constexpr int VEC = F32 ? 4 : 8;  // elements per 16-byte vector
-  for (int t = blockIdx.x; t < B; t += gridDim.x) {
-    for (int h0 = threadIdx.x * VEC; h0 < H; h0 += blockDim.x * VEC) {
-      float acc[VEC];
+  __shared__ int s_pos[32];
+  __shared__ float s_w[32];
+  const int64_t items = (int64_t)B * chunks;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int t = (int)(item / chunks);
+    const int c = (int)(item - (int64_t)t * chunks);
+    __syncthreads();  // the previous item's readers are done with s_pos / s_w
+    if (threadIdx.x < k) {
+      const int pos = slot_pos[(int64_t)t * k + threadIdx.x];
+      s_pos[threadIdx.x] = (pos < 0 || pos >= rows_max) ? -1 : pos;
+      s_w[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    const int h0 = (c * kCombineThreads + (int)threadIdx.x) * VEC;
+    if (h0 >= H) continue;
+    float acc[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int pos = slot_pos[(int64_t)t * k + j];
-        if (pos < 0 || pos >= rows_max) continue;
-        const float g = w[(int64_t)t * k + j];
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+      u32x4 v[kCombineBatch];
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        const int pos = j0 + u < k ? s_pos[j0 + u] : -1;
+        v[u] = pos >= 0 ? *(const u32x4*)((const char*)y_slots + ((int64_t)pos * H + h0) * (F32 ? 4 : 2))
+                        : u32x4{0u, 0u, 0u, 0u};
+      }
+      // accumulated in ascending j, in fp32
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        if (j0 + u >= k || s_pos[j0 + u] < 0) continue;
+        const float g = s_w[j0 + u];
         if (F32) {
-          const f32x4 v = *(const f32x4*)((const float*)y_slots + (int64_t)pos * H + h0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(g, v[i], acc[i]);
+          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(g, __uint_as_float(v[u][i]), acc[i]);
         } else {
-          const u32x4 v = *(const u32x4*)((const uint16_t*)y_slots + (int64_t)pos * H + h0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = __builtin_fmaf(g, __uint_as_float(v[i] << 16), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(g, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+            acc[2 * i] = __builtin_fmaf(g, __uint_as_float(v[u][i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = __builtin_fmaf(g, __uint_as_float(v[u][i] & 0xFFFF0000u), acc[2 * i + 1]);
           }
         }
       }
-      if (F32) {
-        f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
-        *(f32x4*)((float*)y + (int64_t)t * H + h0) = o;
-      } else {
-        u32x4 o;
+    }
+    if (F32) {
+      f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)((float*)y + (int64_t)t * H + h0) = o;
+    } else {
+      u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-        *(u32x4*)((uint16_t*)y + (int64_t)t * H + h0) = o;
-      }
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+      *(u32x4*)((uint16_t*)y + (int64_t)t * H + h0) = o;
     }
   }
 }
@@ -60,11 +86,16 @@ combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slo
 
 hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
                           const float* w, void* y, int64_t rows_max, hipStream_t s) {
-  int grid = p.tokens < 4096 ? p.tokens : 4096;
+  const int vec = p.act_dtype == MOE_F32 ? 4 : 8;
+  const int chunks = (p.hidden / vec + kCombineThreads - 1) / kCombineThreads;
+  const int64_t items = (int64_t)p.tokens * chunks;
+  const int grid = items < 4096 ? (int)items : 4096;
   if (p.act_dtype == MOE_F32)
-    combine_kernel<true><<<grid, 256, 0, s>>>(y_slots, slot_pos, w, y, p.tokens, p.hidden, p.top_k, rows_max);
+    combine_kernel<true><<<grid, kCombineThreads, 0, s>>>(y_slots, slot_pos, w, y, p.tokens,
+                                                          p.hidden, p.top_k, rows_max, chunks);
   else
-    combine_kernel<false><<<grid, 256, 0, s>>>(y_slots, slot_pos, w, y, p.tokens, p.hidden, p.top_k, rows_max);
+    combine_kernel<false><<<grid, kCombineThreads, 0, s>>>(y_slots, slot_pos, w, y, p.tokens,
+                                                           p.hidden, p.top_k, rows_max, chunks);
   return hipGetLastError();
 }
 
