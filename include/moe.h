@@ -58,6 +58,12 @@
  *     appendix A.8 quantizes the gated activation to FP8 before the down
  *     projection).
  *   - Concurrent calls must not share one workspace or output buffer.
+ *   - Shared experts (shared_experts > 0): after the routed row-blocks of the
+ *     chosen configuration come, for each shared expert i, ceil(B / BLOCK_M)
+ *     row-blocks holding tokens 0..B-1 in order; their rows of h and y_slots
+ *     follow the routed rows.  The configuration choice counts them (each shared
+ *     expert adds ceil(B / b) row-tiles and one active expert); the sort and the
+ *     inverse map cover the routed slots only; moe_combine_shared adds lane k.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -99,6 +105,13 @@ typedef struct moe_problem {
   int32_t act_quant;     /* 0: none (default); 1: x in FP8 for the gate/up GEMM;
                             2: x and h in FP8 for both GEMMs (see above; needs
                             act_dtype MOE_BF16, weight_dtype MOE_FP8_E4M3)      */
+  int32_t shared_experts; /* S_sh, 0..8: experts every token goes through with
+                            weight 1, fused into the same grouped FFN launches
+                            (GC-MoE section 4: shared experts see every local
+                            token, need no dispatch, and their output is one more
+                            lane of the combine).  Their weights follow the local
+                            experts' in W1, W3, W2 (and s1, s3, s2): those arrays
+                            hold E_loc + S_sh experts.                          */
 } moe_problem;
 
 /* Buffer sizes a caller must provide for one problem. */
@@ -255,8 +268,18 @@ moe_status moe_grouped_down(const moe_problem* p, const void* w2, const float* s
                             const int32_t* num_blocks, const int32_t* variant, void* y_slots,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Step 5 with shared experts: as moe_combine, then, after the k routed lanes,
+ * y_t += y_slots[(num_blocks + i * ceil(B / b)) * b + t] for i = 0..S_sh-1, with
+ * weight 1 (b = BLOCK_M of *variant): the shared experts' lanes of the combine
+ * (GC-MoE section 4).  num_blocks and variant are the device values the sort
+ * wrote.  Errors: as moe_combine; MOE_ERR_INVALID_ARG for shared_experts = 0. */
+moe_status moe_combine_shared(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,
+                              const float* topk_w, const int32_t* num_blocks,
+                              const int32_t* variant, void* y, void* stream);
+
 /* Step 5: combine (GC-MoE 2.1 Eq. 1; the slot-order reduction of its combine
- * role).  y [B][H] (act dtype) = sum over j = 0..k-1 with slot_pos[t*k+j] >= 0 of
+ * role).  Problems with shared experts use moe_combine_shared instead
+ * (MOE_ERR_INVALID_ARG here).  y [B][H] (act dtype) = sum over j = 0..k-1 with slot_pos[t*k+j] >= 0 of
  * topk_w[t][j] * y_slots[slot_pos[t*k+j]], in fp32, rounded to nearest even once;
  * tokens with no local slot get zeros. */
 moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,

@@ -62,7 +62,7 @@ def lib():
         L.oracle_ffn_slots.argtypes = [i32, i32, P, i32, P, P, P, i32, P, P, P, i32, P, P, P, i32,
                                        i32]
         L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, P, i32, P, P, P, i32, P, P, P,
-                                          P, P, i32, P, P, i32, i32]
+                                          P, P, i32, P, P, i32, i32, i32]
         L.oracle_decode_fp8.argtypes = [P, i64, P]
         L.oracle_decode_fp8.restype = None
         L.oracle_decode_bf16.argtypes = [P, i64, P]
@@ -210,7 +210,8 @@ def ffn_slots(layer, tok: np.ndarray, exp_local: np.ndarray, nthreads: int | Non
 
 def layer_tokens(layer, ids: np.ndarray, w: np.ndarray, tokens: np.ndarray,
                  nthreads: int | None = None):
-    """O5 + O6 for the listed tokens: fp64 Y rows [len(tokens)][H]."""
+    """O5 + O6 for the listed tokens: fp64 Y rows [len(tokens)][H] (with the shared
+    experts' lanes when the shape has them)."""
     H, I, k = layer.shape.hidden, layer.shape.inter, layer.shape.top_k
     if getattr(layer.shape, "act_quant", 0):
         # the FFN sees the listed tokens' dequantized rows; ids/w follow them
@@ -227,7 +228,8 @@ def layer_tokens(layer, ids: np.ndarray, w: np.ndarray, tokens: np.ndarray,
     rc = lib().oracle_layer_tokens(H, I, k, layer.expert_begin, layer.shape.local_experts,
                                    _p(x), xdt, _p(w1), _p(w3), _p(w2), wd, _p(s1), _p(s3),
                                    _p(s2), _p(ids), _p(w), len(toks), _p(toks), _p(Y),
-                                   nthreads or max_threads(), _h_quant(layer))
+                                   nthreads or max_threads(), _h_quant(layer),
+                                   int(getattr(layer.shape, "shared", 0)))
     if rc != 0:
         raise RuntimeError(f"oracle_layer_tokens rc={rc}")
     return Y

@@ -25,6 +25,10 @@
  *  O5 ffn      - per routed slot, W2 * SwiGLU(W1 x) with SwiGLU = silu(gate)*up
  *                (GC-MoE 2.1 Eq. 1; RaMP 2.1 gated MLP).
  *  O6 combine  - y_t = sum_j g_{t,j} * y_{t,j}, in j order (GC-MoE 2.1 Eq. 1).
+ *                With shared experts (GC-MoE 4: every token goes through them and
+ *                their output is one more lane of the combine), after the k routed
+ *                lanes y_t += FFN_{E_loc + i}(x_t) for each shared expert i, with
+ *                weight 1; their weights follow the local experts' in W1, W3, W2.
  *  Q  act quant - the optional FP8 activation path: x quantized to E4M3FN per
  *                token and per group of 128 hidden columns with an fp32 scale
  *                (RaMP 3.3 and A.8: FP8 with 128 x 128 block scaling as used by
@@ -385,7 +389,8 @@ int oracle_ffn_slots(int H, int I, const void* x, int xdt, const void* w1, const
 int oracle_layer_tokens(int H, int I, int k, int e0, int E_loc, const void* x, int xdt,
                         const void* w1, const void* w3, const void* w2, int wdt, const float* s1,
                         const float* s3, const float* s2, const int32_t* ids, const double* w,
-                        int n_tok, const int32_t* tokens, double* Y, int nthreads, int hq) {
+                        int n_tok, const int32_t* tokens, double* Y, int nthreads, int hq,
+                        int n_shared) {
   int err = 0;
   if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1) reduction(| : err)
@@ -406,6 +411,10 @@ int oracle_layer_tokens(int H, int I, int k, int e0, int E_loc, const void* x, i
         orc_expert_ffn(H, I, xr, w1, w3, w2, wdt, s1, s3, s2, e, a, ys, hq);
         double g = w[(int64_t)t * k + j];
         for (int d = 0; d < H; ++d) out[d] += g * ys[d];
+      }
+      for (int i = 0; i < n_shared; ++i) {  /* the shared lanes, weight 1 */
+        orc_expert_ffn(H, I, xr, w1, w3, w2, wdt, s1, s3, s2, E_loc + i, a, ys, hq);
+        for (int d = 0; d < H; ++d) out[d] += ys[d];
       }
     }
     free(xr);

@@ -32,7 +32,8 @@ class moe_problem(ctypes.Structure):  # noqa: N801  (C struct name)
                 ("num_experts", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
                 ("local_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("renormalize", ctypes.c_int32), ("act_quant", ctypes.c_int32)]
+                ("renormalize", ctypes.c_int32), ("act_quant", ctypes.c_int32),
+                ("shared_experts", ctypes.c_int32)]
 
 
 class moe_sizes(ctypes.Structure):  # noqa: N801
@@ -42,10 +43,11 @@ class moe_sizes(ctypes.Structure):  # noqa: N801
 
 
 def problem(tokens, hidden, inter, num_experts, top_k, *, expert_begin=0, local_experts=None,
-            act_dtype=MOE_BF16, weight_dtype=MOE_BF16, renormalize=1, act_quant=0) -> moe_problem:
+            act_dtype=MOE_BF16, weight_dtype=MOE_BF16, renormalize=1, act_quant=0,
+            shared_experts=0) -> moe_problem:
     return moe_problem(tokens, hidden, inter, num_experts, expert_begin,
                        num_experts if local_experts is None else local_experts, top_k,
-                       act_dtype, weight_dtype, renormalize, act_quant)
+                       act_dtype, weight_dtype, renormalize, act_quant, shared_experts)
 
 
 _lib = None
@@ -69,6 +71,7 @@ _SIGS = {
                          ctypes.c_int),
     "moe_combine": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
     "moe_quant_act": ([ctypes.POINTER(moe_problem), P, P, P, P], ctypes.c_int),
+    "moe_combine_shared": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P], ctypes.c_int),
 }
 
 
@@ -201,6 +204,12 @@ def moe_grouped_down(p, w2, s2, sorted_slots, block_expert, num_blocks, variant,
 def moe_quant_act(p, x, xq, xs, stream=None):
     _check("moe_quant_act", lib().moe_quant_act(_pp(p), _ptr(x), _ptr(xq), _ptr(xs),
                                                 _stream(stream)))
+
+
+def moe_combine_shared(p, y_slots, slot_pos, topk_w, num_blocks, variant, y, stream=None):
+    _check("moe_combine_shared", lib().moe_combine_shared(
+        _pp(p), _ptr(y_slots), _ptr(slot_pos), _ptr(topk_w), _ptr(num_blocks), _ptr(variant),
+        _ptr(y), _stream(stream)))
 
 
 def moe_combine(p, y_slots, slot_pos, topk_w, y, stream=None):

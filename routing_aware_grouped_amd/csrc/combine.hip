@@ -8,6 +8,13 @@
 // all on other GPUs get zeros.  Gather form (each token reads its own k rows), so
 // the result is deterministic without atomics.
 //
+// Shared experts (GC-MoE section 4: their output is one more lane of the combine):
+// after the k routed lanes, lane k + i adds shared expert i's row of y_slots with
+// weight 1; those rows follow the routed ones, in token order, ceil(B / b) row-
+// blocks per shared expert (b = BLOCK_M of the chosen configuration, read with the
+// routed row-block count from device memory).  A configuration outside the menu
+// means the grouped FFN ran no tile, and the shared lanes then add nothing.
+//
 // Design: a workgroup takes one token and a chunk of 256 16-byte vectors along H
 // (grid-stride over tokens x chunks, so a small batch still spreads over many
 // workgroups).  The token's slot rows and weights are read once into LDS; each
@@ -25,10 +32,25 @@ template <bool F32>
 __global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slot_pos,
                const float* __restrict__ w, void* __restrict__ y, int B, int H, int k,
-               int64_t rows_max, int chunks) {
+               int64_t rows_max, int chunks, int n_shared, const int32_t* __restrict__ num_blocks,
+               const int32_t* __restrict__ variant) {
   constexpr int VEC = F32 ? 4 : 8;  // elements per 16-byte vector
-  __shared__ int s_pos[32];
-  __shared__ float s_w[32];
+  __shared__ int s_pos[32 + kMaxShared];
+  __shared__ float s_w[32 + kMaxShared];
+  // first row of the shared experts' rows and the rows per shared expert
+  int64_t sh0 = 0, shn = 0;
+  if (n_shared > 0) {
+    const int v = *variant;
+    const int nb = *num_blocks;
+    if (v >= 0 && v < kNumVariants && nb >= 0) {
+      const int bm = kVariants[v].bm;
+      sh0 = (int64_t)nb * bm;
+      shn = (int64_t)((B + bm - 1) / bm) * bm;
+    } else {
+      n_shared = 0;
+    }
+  }
+  const int lanes = k + n_shared;
   const int64_t items = (int64_t)B * chunks;
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int t = (int)(item / chunks);
@@ -38,6 +60,10 @@ combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slo
       const int pos = slot_pos[(int64_t)t * k + threadIdx.x];
       s_pos[threadIdx.x] = (pos < 0 || pos >= rows_max) ? -1 : pos;
       s_w[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
+    } else if (threadIdx.x < lanes) {  // shared expert lanes, weight 1
+      const int64_t row = sh0 + (threadIdx.x - k) * shn + t;
+      s_pos[threadIdx.x] = row < rows_max ? (int)row : -1;
+      s_w[threadIdx.x] = 1.0f;
     }
     __syncthreads();
     const int h0 = (c * kCombineThreads + (int)threadIdx.x) * VEC;
@@ -45,18 +71,18 @@ combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slo
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    for (int j0 = 0; j0 < lanes; j0 += kCombineBatch) {
       u32x4 v[kCombineBatch];
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
-        const int pos = j0 + u < k ? s_pos[j0 + u] : -1;
+        const int pos = j0 + u < lanes ? s_pos[j0 + u] : -1;
         v[u] = pos >= 0 ? *(const u32x4*)((const char*)y_slots + ((int64_t)pos * H + h0) * (F32 ? 4 : 2))
                         : u32x4{0u, 0u, 0u, 0u};
       }
       // accumulated in ascending j, in fp32
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
-        if (j0 + u >= k || s_pos[j0 + u] < 0) continue;
+        if (j0 + u >= lanes || s_pos[j0 + u] < 0) continue;
         const float g = s_w[j0 + u];
         if (F32) {
 #pragma unroll
@@ -85,17 +111,21 @@ combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slo
 }  // namespace
 
 hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
-                          const float* w, void* y, int64_t rows_max, hipStream_t s) {
+                          const float* w, const int32_t* num_blocks, const int32_t* variant,
+                          void* y, int64_t rows_max, hipStream_t s) {
+  const int n_shared = num_blocks && variant ? p.shared_experts : 0;
   const int vec = p.act_dtype == MOE_F32 ? 4 : 8;
   const int chunks = (p.hidden / vec + kCombineThreads - 1) / kCombineThreads;
   const int64_t items = (int64_t)p.tokens * chunks;
   const int grid = items < 4096 ? (int)items : 4096;
   if (p.act_dtype == MOE_F32)
     combine_kernel<true><<<grid, kCombineThreads, 0, s>>>(y_slots, slot_pos, w, y, p.tokens,
-                                                          p.hidden, p.top_k, rows_max, chunks);
+                                                          p.hidden, p.top_k, rows_max, chunks,
+                                                          n_shared, num_blocks, variant);
   else
     combine_kernel<false><<<grid, kCombineThreads, 0, s>>>(y_slots, slot_pos, w, y, p.tokens,
-                                                           p.hidden, p.top_k, rows_max, chunks);
+                                                           p.hidden, p.top_k, rows_max, chunks,
+                                                           n_shared, num_blocks, variant);
   return hipGetLastError();
 }
 

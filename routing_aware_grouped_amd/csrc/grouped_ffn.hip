@@ -209,6 +209,7 @@ struct FfnArgs {
   int slots;  // B * k
   int64_t rows_max;
   const float* xs;  // [B][H/128] activation scales of the FP8 activation path
+  int n_shared;     // shared experts (row-blocks after the routed ones)
 };
 
 // ring slots of per-tile metadata (see Tile::run_all)
@@ -357,10 +358,19 @@ struct Tile {
   // (No workgroup ever waits for another, and no atomics are used.)
   // All the work items (whole tiles, then pieces) form one continuous pipeline, so
   // the next item's first loads are in flight while the current one finishes.
+  //
+  // SH (shared experts): nb counts the routed row-blocks nbr and then, for each
+  // shared expert i, ceil(B / BM) row-blocks of tokens 0..B-1 in order, with
+  // local expert index E_loc + i.  Their slot ids are encoded as g.slots + token.
+  template <bool SH>
   __device__ __forceinline__ static void run_all(const FfnArgs& g, uint8_t* lds, int* meta3,
-                                                int nb, int slot, int G) {
+                                                int nb, int nbr, int slot, int G) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
+    const int Btok = g.slots / g.k;
+    const int nbs = SH ? (Btok + BM - 1) / BM : 1;  // row-blocks per shared expert
+    const int slot_end = SH ? g.slots + Btok : g.slots;
+    const int e_end = SH ? g.E_loc + g.n_shared : g.E_loc;
     const int total = nb * (N / BN);
     const int nst = (K + BK - 1) / BK;
     const int F = total / G;                        // full rounds
@@ -406,17 +416,26 @@ struct Tile {
       int rb, nt;
       tile_rc(item_tile(j), nb, N / BN, rb, nt);
       const int64_t row0 = (int64_t)rb * BM;
-      if (tid < BM) {
-        ms0 = g.sorted_slots[row0 + tid];
-        ms1 = tid + 1 < BM ? g.sorted_slots[row0 + tid + 1] : -1;
+      if (SH && rb >= nbr) {  // a shared expert's row-block: tokens in order
+        const int t0 = ((rb - nbr) % nbs) * BM + tid;
+        if (tid < BM) {
+          ms0 = t0 < Btok ? g.slots + t0 : -1;
+          ms1 = tid + 1 < BM && t0 + 1 < Btok ? g.slots + t0 + 1 : -1;
+        }
+        if (tid == 0) me = g.E_loc + (rb - nbr) / nbs;
+      } else {
+        if (tid < BM) {
+          ms0 = g.sorted_slots[row0 + tid];
+          ms1 = tid + 1 < BM ? g.sorted_slots[row0 + tid + 1] : -1;
+        }
+        if (tid == 0) me = g.block_expert[rb];
       }
-      if (tid == 0) me = g.block_expert[rb];
     };
     auto store_meta = [&](int j) __attribute__((always_inline)) {  // all threads; the caller's next barrier publishes it
       int* m = meta3 + (j % kMetaSlots) * META;
       if (tid < BM) {
-        const bool v0 = ms0 >= 0 && ms0 < g.slots;
-        const bool v1 = ms1 >= 0 && ms1 < g.slots;
+        const bool v0 = ms0 >= 0 && ms0 < slot_end;
+        const bool v1 = ms1 >= 0 && ms1 < slot_end;
         m[tid] = v0 ? ms0 : -1;
         if (v0 && !v1) m[BM] = tid + 1;    // last row of the leading run
         if (tid == 0 && !v0) m[BM] = 0;    // no row holds a slot
@@ -470,7 +489,7 @@ struct Tile {
       tile_rc(item_tile(j), nb, N / BN, rb, nt);
       l_n0 = nt * BN;
       l_e = __builtin_amdgcn_readfirstlane(m[BM + 1]);
-      l_eok = j < nitem && (unsigned)l_e < (unsigned)g.E_loc;
+      l_eok = j < nitem && (unsigned)l_e < (unsigned)e_end;
       if (!l_eok) {
         l_e = 0;
         l_n0 = 0;
@@ -485,16 +504,16 @@ struct Tile {
         const int row = q / GCA, c = q % GCA;
         const int sl = m[row];
         l_aoff[i] = kOob;
-        if (l_eok && sl >= 0 && sl < g.slots) {
+        if (l_eok && sl >= 0 && sl < slot_end) {
           // the host bounds every operand buffer below 2^31 bytes
-          const int arow = PHASE == 1 ? sl / g.k : rb * BM + row;
+          const int arow = PHASE == 1 ? (SH && sl >= g.slots ? sl - g.slots : sl / g.k) : rb * BM + row;
           l_aoff[i] = (uint32_t)(arow * K + c * EPC_A) * ASZ;
         }
       }
       if constexpr (FP8A) {
         const int sl = m[tid % BM];
-        const int srow = PHASE == 1 ? sl / g.k : rb * BM + tid % BM;
-        l_xsoff = (l_eok && tid < BM * KB && sl >= 0 && sl < g.slots)
+        const int srow = PHASE == 1 ? (SH && sl >= g.slots ? sl - g.slots : sl / g.k) : rb * BM + tid % BM;
+        l_xsoff = (l_eok && tid < BM * KB && sl >= 0 && sl < slot_end)
                       ? (uint32_t)srow * (uint32_t)(K / 128) * 4u + (uint32_t)(tid / BM) * 4u
                       : kOob;
         l_wsbase = l_eok ? ((int64_t)l_e * (N / 128) + l_n0 / 128) * (K / 128) : 0;
@@ -705,7 +724,7 @@ struct Tile {
       tile_rc(item_tile(j), nb, N / BN, rb, nt);
       const int64_t row0 = (int64_t)rb * BM;
       const int n0 = nt * BN;
-      if ((unsigned)m[BM + 1] >= (unsigned)g.E_loc) return;  // uniform: no such tile
+      if ((unsigned)m[BM + 1] >= (unsigned)e_end) return;  // uniform: no such tile
       if constexpr (WK > 1) {
         // waves wk > 0 hand their sums to wave wk = 0 through the LDS buffer just
         // computed on (the barrier first lets every wave finish reading it)
@@ -795,7 +814,7 @@ struct Tile {
 #pragma unroll
                 for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          if ((unsigned)m[BM + 1] < (unsigned)g.E_loc) compute_stage(buf, m[BM]);
+          if ((unsigned)m[BM + 1] < (unsigned)e_end) compute_stage(buf, m[BM]);
           if (c_s == c_se - 1) epilogue(c_j, buf, c_sb == 0 && c_se == nst);
           if (++c_s == c_se) {
             ++c_j;
@@ -824,7 +843,9 @@ struct Tile {
   // before the tile (its piece is then in its slot 1).  With Ut < G every range
   // holds at most one stage, so each of the tile's nst stages is its own piece,
   // in slot 0 of its owner.
-  __device__ __forceinline__ static void fixup(const FfnArgs& g, int* meta, int nb, int G, int tq) {
+  template <bool SH>
+  __device__ __forceinline__ static void fixup(const FfnArgs& g, int* meta, int nb, int nbr, int G,
+                                               int tq) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
     const int total = nb * (N / BN);
@@ -842,11 +863,21 @@ struct Tile {
     tile_rc(t, nb, N / BN, rb, nt);
     const int64_t row0 = (int64_t)rb * BM;
     const int n0 = nt * BN;
-    if ((unsigned)g.block_expert[rb] >= (unsigned)g.E_loc) return;
     const int tid = threadIdx.x;
-    if (tid < BM) {
-      const int sl = g.sorted_slots[row0 + tid];
-      meta[tid] = (sl >= 0 && sl < g.slots) ? sl : -1;
+    if (SH && rb >= nbr) {  // a shared expert's row-block (see run_all)
+      const int Btok = g.slots / g.k;
+      const int nbs = (Btok + BM - 1) / BM;
+      if ((rb - nbr) / nbs >= g.n_shared) return;
+      if (tid < BM) {
+        const int t = ((rb - nbr) % nbs) * BM + tid;
+        meta[tid] = t < Btok ? g.slots + t : -1;
+      }
+    } else {
+      if ((unsigned)g.block_expert[rb] >= (unsigned)g.E_loc) return;
+      if (tid < BM) {
+        const int sl = g.sorted_slots[row0 + tid];
+        meta[tid] = (sl >= 0 && sl < g.slots) ? sl : -1;
+      }
     }
     __syncthreads();
     const int wave = tid >> 6;
@@ -925,53 +956,80 @@ constexpr int lds_bytes() {
 }
 
 // The tiles of configuration V in phase PHASE, dealt out statically.
-template <int V, int PHASE, int WKIND>
-__device__ __forceinline__ void run_phase(const FfnArgs& g, uint8_t* lds, int* meta3, int nb) {
+template <int V, int PHASE, int WKIND, bool SH>
+__device__ __forceinline__ void run_phase(const FfnArgs& g, uint8_t* lds, int* meta3, int nb,
+                                          int nbr) {
   using R = typename Cfg<V, PHASE, WKIND>::R;
-  R::run_all(g, lds, meta3, nb, xcd_slot(blockIdx.x, gridDim.x), gridDim.x);
+  R::template run_all<SH>(g, lds, meta3, nb, nbr, xcd_slot(blockIdx.x, gridDim.x), gridDim.x);
 }
 
-template <int PHASE, int WKIND>
+// Row-blocks of the launch: the routed ones the sort wrote (nbr), then with
+// shared experts ceil(B / BM) per shared expert; none beyond the buffers.
+template <bool SH>
+__device__ __forceinline__ bool block_counts(const FfnArgs& g, int v, int& nb, int& nbr) {
+  nbr = *g.num_blocks;
+  if (v < 0 || v >= kNumVariants || nbr < 0 || (!SH && nbr == 0)) return false;
+  const int bm = kVariants[v].bm;
+  nb = nbr;
+  if (SH) nb += g.n_shared * ((g.slots / g.k + bm - 1) / bm);
+  // never address rows beyond the buffers, whatever the device state says
+  const int nb_cap = (int)(g.rows_max / bm);
+  nb = nb < nb_cap ? nb : nb_cap;
+  nbr = nbr < nb ? nbr : nb;
+  return nb > 0;
+}
+
+template <int PHASE, int WKIND, bool SH>
 __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int meta3[kMetaSlots * (kMaxBlockM + 2)];
   const int v = *g.variant;
   int nb = *g.num_blocks;
-  if (v < 0 || v >= kNumVariants || nb <= 0) return;  // no tiles (align_sort wrote none)
-  // never address rows beyond the buffers, whatever the device state says
-  const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
-  nb = nb < nb_cap ? nb : nb_cap;
+  int nbr = nb;
+  if constexpr (!SH) {
+    if (v < 0 || v >= kNumVariants || nb <= 0) return;  // no tiles (align_sort wrote none)
+    // never address rows beyond the buffers, whatever the device state says
+    const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
+    nb = nb < nb_cap ? nb : nb_cap;
+  } else {
+    if (!block_counts<SH>(g, v, nb, nbr)) return;
+  }
   switch (v) {
-    case 0: run_phase<0, PHASE, WKIND>(g, lds, meta3, nb); break;
-    case 1: run_phase<1, PHASE, WKIND>(g, lds, meta3, nb); break;
-    case 2: run_phase<2, PHASE, WKIND>(g, lds, meta3, nb); break;
-    case 3: run_phase<3, PHASE, WKIND>(g, lds, meta3, nb); break;
+    case 0: run_phase<0, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
+    case 1: run_phase<1, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
+    case 2: run_phase<2, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
+    case 3: run_phase<3, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
     default: break;
   }
 }
 
 // The fix-up of one phase's split tail tiles (Tile::fixup), one workgroup per
 // tail tile; the grid is the main launch's, which bounds the tail tiles.
-template <int PHASE, int WKIND>
+template <int PHASE, int WKIND, bool SH>
 __global__ void __launch_bounds__(kThreads) ffn_fixup_kernel(FfnArgs g) {
   __shared__ int meta[kMaxBlockM + 2];
   const int v = *g.variant;
   int nb = *g.num_blocks;
-  if (v < 0 || v >= kNumVariants || nb <= 0) return;
-  const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
-  nb = nb < nb_cap ? nb : nb_cap;
+  int nbr = nb;
+  if constexpr (!SH) {
+    if (v < 0 || v >= kNumVariants || nb <= 0) return;
+    const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
+    nb = nb < nb_cap ? nb : nb_cap;
+  } else {
+    if (!block_counts<SH>(g, v, nb, nbr)) return;
+  }
   const int G = gridDim.x, tq = blockIdx.x;
   switch (v) {
-    case 0: Cfg<0, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
-    case 1: Cfg<1, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
-    case 2: Cfg<2, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
-    case 3: Cfg<3, PHASE, WKIND>::R::fixup(g, meta, nb, G, tq); break;
+    case 0: Cfg<0, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
+    case 1: Cfg<1, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
+    case 2: Cfg<2, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
+    case 3: Cfg<3, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
     default: break;
   }
 }
 
-template <int PHASE, int WKIND>
-hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
+template <int PHASE, int WKIND, bool SH>
+hipError_t launch_phase_sh(const FfnArgs& g, int grid, hipStream_t s) {
   constexpr int lds = lds_bytes<PHASE, WKIND>();
   static_assert((lds + 4096) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
   static int done[64] = {0};
@@ -979,16 +1037,24 @@ hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev >= 0 && dev < 64 && !done[dev]) {
-    e = hipFuncSetAttribute((const void*)ffn_kernel<PHASE, WKIND>,
+    e = hipFuncSetAttribute((const void*)ffn_kernel<PHASE, WKIND, SH>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     done[dev] = 1;
   }
-  ffn_kernel<PHASE, WKIND><<<grid, kThreads, lds, s>>>(g);
+  ffn_kernel<PHASE, WKIND, SH><<<grid, kThreads, lds, s>>>(g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ffn_fixup_kernel<PHASE, WKIND><<<grid, kThreads, 0, s>>>(g);
+  ffn_fixup_kernel<PHASE, WKIND, SH><<<grid, kThreads, 0, s>>>(g);
   return hipGetLastError();
+}
+
+// the launch with shared experts is a separate instance, so that the routed-only
+// kernels carry none of its code
+template <int PHASE, int WKIND>
+hipError_t launch_phase(const FfnArgs& g, int grid, hipStream_t s) {
+  return g.n_shared > 0 ? launch_phase_sh<PHASE, WKIND, true>(g, grid, s)
+                        : launch_phase_sh<PHASE, WKIND, false>(g, grid, s);
 }
 
 template <int WKIND>
@@ -1012,7 +1078,7 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               int num_cus, int64_t rows_max, hipStream_t s) {
   FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
             h, y_slots, part, p.hidden, p.inter, p.top_k, p.local_experts,
-            p.tokens * p.top_k, rows_max, nullptr};
+            p.tokens * p.top_k, rows_max, nullptr, p.shared_experts};
   const int grid = num_cus * kWgPerCu < kMaxGrid ? num_cus * kWgPerCu : kMaxGrid;
   switch (p.weight_dtype) {
     case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);

@@ -21,6 +21,15 @@ int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// rows of sorted_slots / h / y_slots: every routed slot, padding of at most
+// BLOCK_M - 1 rows per active expert, and each shared expert's B rows plus padding
+int64_t rows_max_of(const moe_problem* p) {
+  const int64_t slots = (int64_t)p->tokens * p->top_k;
+  const int64_t active_max = slots < p->local_experts ? slots : p->local_experts;
+  return slots + active_max * (kMaxBlockM - 1) +
+         (int64_t)p->shared_experts * ((int64_t)p->tokens + kMaxBlockM - 1);
+}
+
 moe_status validate(const moe_problem* p) {
   if (!p) return MOE_ERR_INVALID_ARG;
   if (p->tokens < 1 || p->hidden < 128 || p->inter < 128) return MOE_ERR_INVALID_ARG;
@@ -31,6 +40,7 @@ moe_status validate(const moe_problem* p) {
   if (p->top_k < 1 || p->top_k > 32 || p->top_k > p->num_experts) return MOE_ERR_INVALID_ARG;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (p->act_quant < 0 || p->act_quant > 2) return MOE_ERR_INVALID_ARG;
+  if (p->shared_experts < 0 || p->shared_experts > kMaxShared) return MOE_ERR_INVALID_ARG;
   const int a = p->act_dtype, w = p->weight_dtype;
   if (a < MOE_F32 || a > MOE_FP8_E4M3 || w < MOE_F32 || w > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && w == MOE_BF16) ||
@@ -47,7 +57,7 @@ moe_status validate(const moe_problem* p) {
   // 32-bit byte offsets below 2^31 (buffer loads; offsets from 2^31 up mark
   // chunks with no operand)
   {
-    const int64_t rmax = slots + (int64_t)(slots < p->local_experts ? slots : p->local_experts) * (kMaxBlockM - 1);
+    const int64_t rmax = rows_max_of(p);
     const int64_t wide = p->hidden > p->inter ? p->hidden : p->inter;
     const int64_t ab = elem_bytes(a), wb = elem_bytes(w);
     if (rmax * wide * ab >= (1ll << 31) || (int64_t)p->tokens * p->hidden * ab >= (1ll << 31) ||
@@ -55,7 +65,7 @@ moe_status validate(const moe_problem* p) {
       return MOE_ERR_UNSUPPORTED;
   }
   // the cost model converts tile and wave counts to fp32 exactly (< 2^24)
-  const int64_t rows = slots + (int64_t)(slots < p->local_experts ? slots : p->local_experts) * (kMaxBlockM - 1);
+  const int64_t rows = rows_max_of(p);
   for (int v = 0; v < kNumVariants; ++v) {
     const int64_t rt = rows / kVariants[v].bm;
     const int64_t T = rt * (p->inter / kVariants[v].bn1 + (int64_t)(p->hidden / kVariants[v].bn2) * kVariants[v].splitk);
@@ -68,11 +78,6 @@ moe_status validate(const moe_problem* p) {
 int64_t codes_bytes(int64_t n, int64_t m) { return (n * m + 255) / 256 * 256; }
 int64_t scales_bytes(int64_t n, int64_t m) { return (n * (m / 128) * 4 + 255) / 256 * 256; }
 
-int64_t rows_max_of(const moe_problem* p) {
-  const int64_t slots = (int64_t)p->tokens * p->top_k;
-  const int64_t active_max = slots < p->local_experts ? slots : p->local_experts;
-  return slots + active_max * (kMaxBlockM - 1);
-}
 
 // x codes and scales (act_quant >= 1), then h codes and scales (act_quant == 2)
 int64_t quant_bytes(const moe_problem* p) {
@@ -88,7 +93,7 @@ int64_t quant_bytes(const moe_problem* p) {
 void sizes_of(const moe_problem* p, moe_sizes* s) {
   const int64_t slots = (int64_t)p->tokens * p->top_k;
   const int64_t active_max = slots < p->local_experts ? slots : p->local_experts;
-  s->rows_max = slots + active_max * (kMaxBlockM - 1);
+  s->rows_max = rows_max_of(p);
   s->blocks_max = s->rows_max / kMinBlockM + 1;
   const int eb = elem_bytes(p->act_dtype);
   s->y_slots_bytes = s->rows_max * p->hidden * eb;
@@ -128,7 +133,9 @@ moe_status fill_cost_table(const moe_problem* p, CostTable* t) {
     t->q2[v] = (p->hidden / kVariants[v].bn2) * kVariants[v].splitk;
     t->S1[v] = cus * kWgPerCu;
     t->S2[v] = cus * kWgPerCu;
+    t->rt_shared[v] = p->shared_experts * ((p->tokens + kVariants[v].bm - 1) / kVariants[v].bm);
   }
+  t->a_shared = p->shared_experts;
   return MOE_OK;
 }
 
@@ -343,11 +350,27 @@ moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t*
                        const float* topk_w, void* y, void* stream) {
   moe_status st = validate(p);
   if (st != MOE_OK) return st;
+  if (p->shared_experts) return MOE_ERR_INVALID_ARG;
   if (!y_slots || !slot_pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned(y_slots, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
   moe_sizes sz;
   sizes_of(p, &sz);
-  return hip_status(launch_combine(*p, y_slots, slot_pos, topk_w, y, sz.rows_max, (hipStream_t)stream));
+  return hip_status(launch_combine(*p, y_slots, slot_pos, topk_w, nullptr, nullptr, y, sz.rows_max,
+                                   (hipStream_t)stream));
+}
+
+moe_status moe_combine_shared(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,
+                              const float* topk_w, const int32_t* num_blocks,
+                              const int32_t* variant, void* y, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!p->shared_experts) return MOE_ERR_INVALID_ARG;
+  if (!y_slots || !slot_pos || !topk_w || !y || !num_blocks || !variant) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y_slots, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  moe_sizes sz;
+  sizes_of(p, &sz);
+  return hip_status(launch_combine(*p, y_slots, slot_pos, topk_w, num_blocks, variant, y,
+                                   sz.rows_max, (hipStream_t)stream));
 }
 
 }  // extern "C"

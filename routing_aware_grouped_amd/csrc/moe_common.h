@@ -86,13 +86,19 @@ constexpr int kPieceMax = piece_max();
 constexpr int64_t kPartBytes = (int64_t)kMaxGrid * 2 * kPieceMax * 4;
 
 // Device-side table of the cost-model constants (RaMP Eq. 1) per configuration.
+// With shared experts, each adds ceil(B / b) row-tiles (rt_shared) and one active
+// expert (a_shared) to the features of every configuration.
 struct CostTable {
   int32_t b[kNumVariants];
   int32_t q1[kNumVariants];
   int32_t q2[kNumVariants];
   int32_t S1[kNumVariants];
   int32_t S2[kNumVariants];
+  int32_t rt_shared[kNumVariants];
+  int32_t a_shared;
 };
+
+constexpr int kMaxShared = 8;
 
 // Host-side launchers (one per translation unit).
 hipError_t launch_route_topk(const moe_problem& p, const float* logits, int32_t* ids, float* w,
@@ -126,8 +132,10 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               const int32_t* block_expert, const int32_t* num_blocks,
                               const int32_t* variant, void* y_slots, void* h, float* part,
                               int num_cus, int64_t rows_max, hipStream_t s);
+// num_blocks / variant: device values of the sort, needed with shared experts only
 hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
-                          const float* w, void* y, int64_t rows_max, hipStream_t s);
+                          const float* w, const int32_t* num_blocks, const int32_t* variant,
+                          void* y, int64_t rows_max, hipStream_t s);
 
 
 }  // namespace moe

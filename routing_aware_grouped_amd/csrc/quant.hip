@@ -7,7 +7,8 @@
 // The same quantization serves h before the down GEMM (RaMP appendix A.8
 // quantizes the gated activation to FP8): there the rows are the padded slot rows
 // of the expert grouping, their count comes from device memory (the chosen
-// configuration's BLOCK_M times the row-block count) and padding rows are skipped.
+// configuration's BLOCK_M times the row-block count, then the shared experts' rows,
+// ceil(B / BLOCK_M) row-blocks each, tokens in order) and padding rows are skipped.
 //
 // Design: one group (128 bf16 = 256 bytes) per 16 lanes, each lane holding one
 // 16-byte chunk of 8 values; the group maximum is a 16-lane xor-shuffle
@@ -28,12 +29,20 @@ template <bool PADDED>
 __global__ void __launch_bounds__(kQuantThreads)
 quant_act_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s,
                  int64_t ngroups, int G, const int32_t* __restrict__ sorted_slots,
-                 const int32_t* __restrict__ num_blocks, const int32_t* __restrict__ variant) {
+                 const int32_t* __restrict__ num_blocks, const int32_t* __restrict__ variant,
+                 int B, int n_shared) {
   const int l16 = threadIdx.x & 15;
+  int64_t routed = 0, shn = 1;  // routed rows; rows per shared expert
   if constexpr (PADDED) {
     const int v = *variant;
     const int64_t nb = *num_blocks;
-    const int64_t rows = (v >= 0 && v < kNumVariants && nb > 0) ? nb * kVariants[v].bm : 0;
+    int64_t rows = 0;
+    if (v >= 0 && v < kNumVariants && nb >= 0) {
+      const int bm = kVariants[v].bm;
+      routed = nb * bm;
+      shn = (int64_t)((B + bm - 1) / bm) * bm;
+      rows = routed + n_shared * shn;
+    }
     ngroups = rows * G < ngroups ? rows * G : ngroups;
   }
   // 16 consecutive lanes share a group, so a group's lanes are always all
@@ -42,8 +51,8 @@ quant_act_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float*
        grp += (int64_t)gridDim.x * kGroupsPerWg) {
     const int64_t t = grp / G;
     const int g = (int)(grp - t * G);
-    if constexpr (PADDED) {
-      if (sorted_slots[t] < 0) continue;  // a padding row (uniform over the 16 lanes)
+    if constexpr (PADDED) {  // padding rows are skipped (uniform over the 16 lanes)
+      if (t < routed ? sorted_slots[t] < 0 : (t - routed) % shn >= B) continue;
     }
     const int64_t off = (t * G + g) * 128 + l16 * 8;  // = t * H + 128 g + 8 l16
     const u32x4 v = *(const u32x4*)(x + off);
@@ -86,7 +95,7 @@ hipError_t launch_quant_act(const moe_problem& p, const void* x, uint8_t* xq, fl
   int64_t grid = (ngroups + kGroupsPerWg - 1) / kGroupsPerWg;
   if (grid > 4096) grid = 4096;
   quant_act_kernel<false><<<(int)grid, kQuantThreads, 0, s>>>((const uint16_t*)x, xq, xs, ngroups,
-                                                               G, nullptr, nullptr, nullptr);
+                                                               G, nullptr, nullptr, nullptr, 0, 0);
   return hipGetLastError();
 }
 
@@ -98,7 +107,8 @@ hipError_t launch_quant_h(const moe_problem& p, const void* h, uint8_t* hq, floa
   int64_t grid = (ngroups + kGroupsPerWg - 1) / kGroupsPerWg;
   if (grid > 4096) grid = 4096;
   quant_act_kernel<true><<<(int)grid, kQuantThreads, 0, s>>>((const uint16_t*)h, hq, hs, ngroups,
-                                                              G, sorted_slots, num_blocks, variant);
+                                                              G, sorted_slots, num_blocks, variant,
+                                                              p.tokens, p.shared_experts);
   return hipGetLastError();
 }
 

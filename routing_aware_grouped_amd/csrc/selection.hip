@@ -297,14 +297,15 @@ __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
     const int b = tab.b[v];
     int rt = 0;
     for (int e = lane; e < E_loc; e += kWave) rt += (counts[e] + b - 1) / b;
-    rt = (int)group_reduce<kWave>((uint32_t)rt, 0u, IAdd{});
+    rt = (int)group_reduce<kWave>((uint32_t)rt, 0u, IAdd{}) + tab.rt_shared[v];
     if (lane == 0) {
       const int T1 = tab.q1[v] * rt, T2 = tab.q2[v] * rt;
       const int W = (T1 + tab.S1[v] - 1) / tab.S1[v] + (T2 + tab.S2[v] - 1) / tab.S2[v];
       const int T = T1 + T2;
       const float* th = theta + 4 * v;
       const float t = __builtin_fmaf(
-          th[3], (float)active, __builtin_fmaf(th[2], (float)T, __builtin_fmaf(th[1], (float)W, th[0])));
+          th[3], (float)(active + tab.a_shared),
+          __builtin_fmaf(th[2], (float)T, __builtin_fmaf(th[1], (float)W, th[0])));
       tv[v] = t;
       if (t_hat) t_hat[v] = t;
     }

@@ -12,7 +12,8 @@ import dataclasses
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_grouped_down,
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_combine_shared,
+               moe_grouped_down,
                moe_grouped_ffn, moe_grouped_gate_up, moe_num_variants, moe_problem,
                moe_query_sizes, moe_route_select_align, moe_route_topk, moe_select_config)
 
@@ -114,7 +115,11 @@ def down(b: Buffers, stream=None):
 
 
 def combine(b: Buffers, stream=None):
-    moe_combine(b.p, b.y_slots, b.slot_pos, b.topk_w, b.y, stream)
+    if b.p.shared_experts:
+        moe_combine_shared(b.p, b.y_slots, b.slot_pos, b.topk_w, b.num_blocks, b.variant, b.y,
+                           stream)
+    else:
+        moe_combine(b.p, b.y_slots, b.slot_pos, b.topk_w, b.y, stream)
 
 
 def forward(b: Buffers, stream=None, forced_variant: bool = False):
@@ -163,7 +168,7 @@ def problem_of(layer, renormalize: int = 1) -> moe_problem:
     sh = layer.shape
     return moe_problem(layer.tokens, sh.hidden, sh.inter, sh.num_experts, layer.expert_begin,
                        sh.local_experts, sh.top_k, sh.act_dtype, sh.weight_dtype, renormalize,
-                       getattr(sh, "act_quant", 0))
+                       getattr(sh, "act_quant", 0), getattr(sh, "shared", 0))
 
 
 def from_layer(layer, theta=None, device="cuda", weights=None, renormalize: int = 1) -> Buffers:

@@ -46,6 +46,7 @@ class Shape:
     out_dtype: int
     logits: str  # "normal" (tiny) or "dirichlet"
     act_quant: int = 0  # FP8 E4M3 activations: 1 in the gate/up GEMM, 2 in both GEMMs
+    shared: int = 0     # shared experts, stored after the local experts' weights
 
 
 SHAPES = {
@@ -69,11 +70,23 @@ SHAPES = {
     "kimi_share_fp8ah": Shape("kimi_share_fp8ah", 7168, 2048, 384, 48, 8, BF16, FP8, BF16,
                               "dirichlet", 2),
     "small_fp8ah": Shape("small_fp8ah", 384, 256, 8, 8, 2, BF16, FP8, BF16, "dirichlet", 2),
+    # with shared experts (DeepSeek-V3 and Kimi-K2 each have one, of the routed
+    # experts' size); the small ones have two, and the tiny one fp32 arithmetic
+    "dsv3_share_sh": Shape("dsv3_share_sh", 7168, 2048, 256, 32, 8, BF16, FP8, BF16, "dirichlet",
+                           0, 1),
+    "kimi_share_sh": Shape("kimi_share_sh", 7168, 2048, 384, 48, 8, BF16, FP8, BF16, "dirichlet",
+                           0, 1),
+    "small_sh": Shape("small_sh", 384, 256, 8, 8, 2, BF16, FP8, BF16, "dirichlet", 0, 2),
+    "tiny_sh": Shape("tiny_sh", 128, 256, 8, 8, 2, F32, F32, F32, "normal", 0, 2),
+    "small_sh_fp8ah": Shape("small_sh_fp8ah", 384, 256, 8, 8, 2, BF16, FP8, BF16, "dirichlet", 2,
+                            2),
 }
 
 CFG_INDEX = {"tiny": 1, "mixtral": 2, "qwen3": 3, "dsv3_share": 4, "kimi_share": 5,
              "dsv3_share_fp8a": 4, "kimi_share_fp8a": 5, "small_fp8a": 6,
-             "dsv3_share_fp8ah": 4, "kimi_share_fp8ah": 5, "small_fp8ah": 6}
+             "dsv3_share_fp8ah": 4, "kimi_share_fp8ah": 5, "small_fp8ah": 6,
+             "dsv3_share_sh": 4, "kimi_share_sh": 5, "small_sh": 6, "tiny_sh": 1,
+             "small_sh_fp8ah": 6}
 
 
 def seed_seq(shape: str, tokens: int, alpha: float | None, rep: int) -> np.random.SeedSequence:
@@ -216,7 +229,7 @@ def _encode(a32: np.ndarray, dtype: int) -> np.ndarray:
 
 def make_weights(shape: Shape, rng: np.random.Generator, std: float = 0.02):
     """Expert weights for all local experts, generated expert by expert."""
-    El, H, I = shape.local_experts, shape.hidden, shape.inter
+    El, H, I = shape.local_experts + shape.shared, shape.hidden, shape.inter
     wd = shape.weight_dtype
     out = {}
     for name, (r, c) in (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I))):
@@ -269,7 +282,7 @@ def make_weights_device(shape_name: str, device="cuda", std: float = 0.02, seed:
     """Dict w1, w3, w2 (+ s1, s3, s2 for fp8) of torch tensors on `device`, dtype-
     encoded (float32 / bfloat16 / float8_e4m3fn)."""
     shape = SHAPES[shape_name]
-    El, H, I = shape.local_experts, shape.hidden, shape.inter
+    El, H, I = shape.local_experts + shape.shared, shape.hidden, shape.inter
     wd = shape.weight_dtype
     g = torch.Generator(device=device)
     g.manual_seed(CFG_INDEX[shape_name] * 1_000_003 + 7777 if seed is None else seed)

@@ -48,8 +48,8 @@ def _p(**kw):
     base = dict(tokens=64, hidden=128, inter=256, num_experts=8, top_k=2, act_dtype=moe.MOE_F32,
                 weight_dtype=moe.MOE_F32)
     base.update(kw)
-    extra = {k: base.pop(k) for k in ("expert_begin", "local_experts", "renormalize", "act_quant")
-             if k in base}
+    extra = {k: base.pop(k) for k in ("expert_begin", "local_experts", "renormalize", "act_quant",
+                                      "shared_experts") if k in base}
     return moe.problem(base.pop("tokens"), base.pop("hidden"), base.pop("inter"),
                        base.pop("num_experts"), base.pop("top_k"), **base, **extra)
 
@@ -91,6 +91,8 @@ def test_query_sizes():
     # the FP8 activation path needs bf16 activations and fp8 weights
     (dict(act_quant=1, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_quant=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(shared_experts=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(shared_experts=9), moe.MOE_ERR_INVALID_ARG),
     (dict(tokens=1 << 20, num_experts=1024, local_experts=1024, top_k=8), moe.MOE_ERR_UNSUPPORTED),
     # one expert's bf16 weight matrix of 2^31 bytes: beyond the 32-bit buffer offsets
     (dict(hidden=32768, inter=32768, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16),
@@ -124,6 +126,25 @@ def test_act_quant_workspace_holds_codes_and_scales():
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
     with pytest.raises(moe.MoeError) as ei:  # x misaligned
         moe.moe_quant_act(_p(act_quant=1, **kw), 0x1008, 0x1000, 0x1000, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_shared_experts_sizes_and_combine_entry_points():
+    """Each shared expert adds B rows plus at most BLOCK_M - 1 of padding; the plain
+    combine refuses problems with shared experts and the shared combine the others."""
+    s0 = moe.moe_query_sizes(_p())
+    s2 = moe.moe_query_sizes(_p(shared_experts=2))
+    bmax = max(m[0] for m in spec.MENU)
+    assert s2.rows_max - s0.rows_max == 2 * (64 + bmax - 1)
+    a = 0x10000
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_combine(_p(shared_experts=1), a, a, a, a, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_combine_shared(_p(), a, a, a, a, a, a, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # needs the device block count
+        moe.moe_combine_shared(_p(shared_experts=1), a, a, a, None, a, a, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
 
 
