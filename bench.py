@@ -66,6 +66,8 @@ SWEEPS = {
     # and with FP8 activations in both GEMMs
     "dsv3_share_fp8ah": dict(tokens=[1, 16, 64, 256], alphas=[0.1, 1.0, 10.0]),  # B = 8T
     "kimi_share_fp8ah": dict(tokens=[8, 64, 512, 2048, 4096], alphas=[0.05]),
+    # the DeepSeek-V3 share with its shared expert fused into the same launches
+    "dsv3_share_sh": dict(tokens=[1, 16, 64, 256], alphas=[0.1, 1.0, 10.0]),  # B = 8T
 }
 
 
@@ -83,10 +85,12 @@ def work(layer, ids_np):
     H, I, k, El, e0 = sh.hidden, sh.inter, sh.top_k, sh.local_experts, layer.expert_begin
     B = layer.tokens
     loc = (ids_np >= e0) & (ids_np < e0 + El)
-    S = int(loc.sum())
     cnt = np.bincount((ids_np[loc] - e0).ravel(), minlength=El)
-    A = int((cnt > 0).sum())
-    U = int(loc.any(axis=1).sum())
+    # shared experts: B more slots each, every token, one more active expert each
+    nsh = getattr(sh, "shared", 0)
+    S = int(loc.sum()) + nsh * B
+    A = int((cnt > 0).sum()) + nsh
+    U = B if nsh else int(loc.any(axis=1).sum())
     wb = 1 if sh.weight_dtype == synth.FP8 else (4 if sh.weight_dtype == synth.F32 else 2)
     ab = 4 if sh.act_dtype == synth.F32 else 2
     mat_scale = (H // 128) * (I // 128) * 4 if sh.weight_dtype == synth.FP8 else 0
@@ -101,7 +105,9 @@ def work(layer, ids_np):
     mfma_s = 4 * S * H * I / gu_peak + 2 * S * H * I / dn_peak
     return dict(S=S, A=A, U=U, flops=6 * S * H * I, layer_bytes=layer_bytes,
                 gate_up_bytes=gate_up_bytes, gate_up_flops=4 * S * H * I, gate_up_peak=gu_peak,
-                mfma_s=mfma_s, eff_exp=synth.eff_exp(cnt), counts=cnt)
+                mfma_s=mfma_s, eff_exp=synth.eff_exp(cnt),
+                # the chooser's view: a shared expert is a local expert with B tokens
+                counts=np.concatenate([cnt, np.full(nsh, B, dtype=cnt.dtype)]))
 
 
 def roof_us(w):
@@ -339,7 +345,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=128)
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--sweep", default="mixtral,qwen3,dsv3_share,kimi_share,dsv3_share_fp8a,"
-                                       "kimi_share_fp8a,dsv3_share_fp8ah,kimi_share_fp8ah",
+                                       "kimi_share_fp8a,dsv3_share_fp8ah,kimi_share_fp8ah,"
+                                       "dsv3_share_sh",
                     help="comma-separated workloads to sweep ('' for none)")
     ap.add_argument("--sweep-reps", type=int, default=15)
     ap.add_argument("--cpu", type=int, default=1, help="1: time the CPU oracle baseline")

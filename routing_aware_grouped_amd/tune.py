@@ -50,6 +50,7 @@ FIT_TOKENS = {
     "kimi_share_fp8a": [8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096],
     "dsv3_share_fp8ah": [8, 32, 128, 512, 1024, 2048],
     "kimi_share_fp8ah": [8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096],
+    "dsv3_share_sh": [8, 32, 128, 512, 1024, 2048],
 }
 FIT_ALPHAS = [0.03, 0.5, 3.0, 30.0]
 FIT_REP0 = 100
@@ -197,7 +198,10 @@ def collect(shape_name: str, reps: int = 9, n_rep_loads: int = 1, log=print) -> 
                 b = L.from_layer(layer, weights=wts)
                 L.route(b)
                 torch.cuda.synchronize()
-                counts = b.counts.cpu().numpy().astype(np.int64)
+                # a shared expert counts as a local expert that every token reaches
+                # (the device cost model adds its row-tiles and one active expert)
+                counts = np.concatenate([b.counts.cpu().numpy().astype(np.int64),
+                                         np.full(layer.shape.shared, tok, np.int64)])
                 if cc is None or cc["_key"] != (b.p.hidden, b.p.inter):
                     cc = moe_cost_constants(b.p)
                     cc["_key"] = (b.p.hidden, b.p.inter)
