@@ -339,10 +339,12 @@ struct Tile {
   // Whether the r tail tiles of a phase are split across all G workgroups.  A
   // last round in which at least three quarters of the workgroups stream weights
   // runs near the HBM rate, so streaming configurations split only smaller tails
-  // (a split costs the fix-up launch its work, which a small layer cannot hide);
-  // the cached configuration (compute-bound loads) always splits.
-  __device__ __forceinline__ static bool split_tail(int r, int G) {
-    return r > 0 && (!STREAM || 4 * r < 3 * G);
+  // (a split costs the fix-up launch its work, which a small layer cannot hide).
+  // The cached configuration splits when the idle share of an unsplit phase,
+  // (G - r) / (G (F + 1)) of its time, would exceed one tenth: after several full
+  // rounds a nearly full last round costs less than summing its split tiles.
+  __device__ __forceinline__ static bool split_tail(int r, int G, int F) {
+    return r > 0 && (STREAM ? 4 * r < 3 * G : 10 * (G - r) > G * (F + 1));
   }
 
   // Runs the work of workgroup slot `slot` of `G` (hybrid Stream-K).  The phase's
@@ -375,7 +377,7 @@ struct Tile {
     const int nst = (K + BK - 1) / BK;
     const int F = total / G;                        // full rounds
     const int r = total - F * G;                    // tail tiles
-    const bool split = split_tail(r, G);
+    const bool split = split_tail(r, G, F);
     const int Fw = F + (!split && slot < r ? 1 : 0);  // whole tiles of this workgroup
     const int64_t Ut = split ? (int64_t)r * nst : 0;  // tail stages cut into ranges
     const int64_t u0 = (int64_t)slot * Ut / G;      // this workgroup's tail range
@@ -852,7 +854,7 @@ struct Tile {
     const int nst = (K + BK - 1) / BK;
     const int F = total / G;
     const int r = total - F * G;
-    if (tq >= r || !split_tail(r, G)) return;
+    if (tq >= r || !split_tail(r, G, F)) return;
     const int64_t Ut = (int64_t)r * nst;
     const int64_t ub = (int64_t)tq * nst;
     const int w0 = (int)(((ub + 1) * G - 1) / Ut);

@@ -30,8 +30,13 @@ def cost_constants(hidden: int, inter: int, num_cus: int) -> dict:
 MAX_GRID = 1024
 
 
-def splits_tail(r: int, grid: int, stream: int) -> bool:
+def splits_tail(r: int, grid: int, stream: int, full_rounds: int = 0) -> bool:
     """Whether a phase's last r (< grid) tiles are split by reduction stages across
-    the whole grid (hybrid Stream-K): always for the cached configuration, and for
-    streaming ones when fewer than three quarters of the workgroups would be busy."""
-    return r > 0 and (not stream or 4 * r < 3 * grid)
+    the whole grid (hybrid Stream-K): for streaming configurations when fewer than
+    three quarters of the workgroups would be busy; for the cached one when the idle
+    share of an unsplit phase, (grid - r) / (grid (F + 1)), exceeds one tenth."""
+    if r <= 0:
+        return False
+    if stream:
+        return 4 * r < 3 * grid
+    return 10 * (grid - r) > grid * (full_rounds + 1)

@@ -350,7 +350,8 @@ def test_split_tail_tiles(B):
         err, ref = G.check_y(layer, out, ids, w, toks, ref)
         G.say(f"  variant {v}: rel err {err:.3g}")
         for N, BN in ((I, spec.MENU[v][1]), (H, spec.MENU[v][2])):
-            if spec.splits_tail(out["num_blocks"] * (N // BN) % grid, grid, spec.MENU[v][8]):
+            tiles = out["num_blocks"] * (N // BN)
+            if spec.splits_tail(tiles % grid, grid, spec.MENU[v][8], tiles // grid):
                 split.add(v)
         first = b.y.clone()
         for _ in range(2):
