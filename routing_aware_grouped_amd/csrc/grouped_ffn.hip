@@ -866,6 +866,40 @@ struct Tile {
     const int64_t row0 = (int64_t)rb * BM;
     const int n0 = nt * BN;
     const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wk = wave % WK;
+    const int wn = (wave / WK) % WN;
+    const int wm = wave / (WK * WN);
+    // The pieces in reduction order: (owner w, its piece slot).  The first one is
+    // loaded before the tile's metadata, so the two memory round trips overlap.
+    const bool w0_before = Ut >= G && (int64_t)w0 * Ut / G < ub;
+    auto piece_of = [&](int q, int& w, int& pc) __attribute__((always_inline)) {
+      if (Ut >= G) {
+        w = w0 + q;
+        pc = q == 0 && w0_before ? 1 : 0;
+      } else {  // (u + 1) * G <= Ut * G < G * G fits 32 bits
+        w = (int)(((unsigned)(ub + q + 1) * (unsigned)G - 1u) / (unsigned)Ut);
+        pc = 0;
+      }
+    };
+    const int npieces = Ut >= G ? w1 - w0 + 1 : nst;
+    f32x4 acc[NMAT][FM][FN];
+    auto load_piece = [&](int q, bool add) __attribute__((always_inline)) {
+      int w, pc;
+      piece_of(q, w, pc);
+      const float* src = g.part + ((int64_t)w * 2 + pc) * PIECE + (wm * WN + wn) * NFRAG * 256;
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) {
+            const f32x4 v = *(const f32x4*)(src + (((mt * FM + i) * FN + jn) * 64 + lane) * 4);
+            acc[mt][i][jn] = add ? acc[mt][i][jn] + v : v;
+          }
+    };
+    if (wk == 0) load_piece(0, false);
     if (SH && rb >= nbr) {  // a shared expert's row-block (see run_all)
       const int Btok = g.slots / g.k;
       const int nbs = (Btok + BM - 1) / BM;
@@ -882,37 +916,8 @@ struct Tile {
       }
     }
     __syncthreads();
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int wk = wave % WK;
-    const int wn = (wave / WK) % WN;
-    const int wm = wave / (WK * WN);
     if (wk != 0) return;
-    f32x4 acc[NMAT][FM][FN];
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto add_piece = [&](int w, int pc) __attribute__((always_inline)) {
-      const float* src = g.part + ((int64_t)w * 2 + pc) * PIECE + (wm * WN + wn) * NFRAG * 256;
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int jn = 0; jn < FN; ++jn)
-            acc[mt][i][jn] += *(const f32x4*)(src + (((mt * FM + i) * FN + jn) * 64 + lane) * 4);
-    };
-    if (Ut >= G) {
-      const bool w0_before = (int64_t)w0 * Ut / G < ub;
-      for (int w = w0; w <= w1; ++w) add_piece(w, w == w0 && w0_before ? 1 : 0);
-    } else {
-      // (u + 1) * G <= Ut * G < G * G fits 32 bits
-      for (int u = (int)ub; u < (int)ub + nst; ++u)
-        add_piece((int)(((unsigned)(u + 1) * (unsigned)G - 1u) / (unsigned)Ut), 0);
-    }
+    for (int q = 1; q < npieces; ++q) load_piece(q, true);
     store_acc(g, acc, meta, row0, n0, wm, wn, lane);
   }
 };
