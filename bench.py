@@ -360,7 +360,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the layer on one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the layer runs on one GPU "
               "(one GPU's expert share at its real size); no multi-GPU figure is produced.",
               file=sys.stderr)
         sys.exit(2)
