@@ -87,3 +87,32 @@ def test_select_counts_shared_row_tiles():
         ref_v, ref_t, _ = oracle.select(cnt, cc["b"], cc["q1"], cc["q2"], cc["S1"], cc["S2"], th)
         assert out["variant"] == ref_v
         np.testing.assert_array_equal(b.t_hat.cpu().numpy().view(np.uint32), ref_t.view(np.uint32))
+
+
+def test_graph_replay_fp8_activations_and_shared():
+    """The whole layer with FP8 activations in both GEMMs and shared experts (two
+    quantization launches, shared row-blocks, shared combine lanes) captured in one
+    HIP graph replays to the eager result, with eager work between replays."""
+    layer = synth.make_layer("small_sh_fp8ah", 130, 1.0, 4)
+    th = torch.tensor([[5.0, 0.0, 0.01, 0.1]] * V, dtype=torch.float32)
+    th[:, 0] += torch.arange(V, dtype=torch.float32)
+    b = L.from_layer(layer, theta=th, weights=G.device_weights(layer))
+    L.forward(b)
+    torch.cuda.synchronize()
+    eager = b.y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.forward(b, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    b.y.zero_()
+    with torch.cuda.graph(g):
+        L.forward(b)
+    for r in range(4):
+        b.y.fill_(float(r + 1))
+        b.workspace.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.y.view(torch.int16), eager.view(torch.int16)), r
