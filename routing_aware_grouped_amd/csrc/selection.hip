@@ -341,19 +341,25 @@ __host__ __device__ __forceinline__ size_t align_table_bytes(int B, int E_loc) {
   return (size_t)kAlignWaves * E_loc * 8 + nblk * E_loc * 4 + (size_t)(2 * E_loc + 1) * 4;
 }
 
-__device__ __forceinline__ void build_masks(unsigned long long* masks, const int32_t* ids, int blk,
+// Local expert index of a routed id: ids are global expert ids (int32_t), or local
+// indices staged in LDS as bytes with 255 for an expert of another GPU (uint8_t).
+__device__ __forceinline__ int local_of(int32_t v, int e0) { return v - e0; }
+__device__ __forceinline__ int local_of(uint8_t v, int) { return v == 255 ? -1 : (int)v; }
+
+template <typename IdT>
+__device__ __forceinline__ void build_masks(unsigned long long* masks, const IdT* ids, int blk,
                                             int B, int k, int e0, int E_loc, int lane) {
   for (int e = lane; e < E_loc; e += kWave) masks[e] = 0ull;
   __builtin_amdgcn_wave_barrier();
   const int t = blk * kWave + lane;
   const int tc = t < B ? t : B - 1;  // loads stay in bounds; results of t >= B are dropped
   for (int j0 = 0; j0 < k; j0 += 4) {
-    int v[4];
+    IdT v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = ids[(int64_t)tc * k + (j0 + u < k ? j0 + u : k - 1)];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int e = v[u] - e0;
+      const int e = local_of(v[u], e0);
       if (t < B && j0 + u < k && e >= 0 && e < E_loc) atomicOr(&masks[e], 1ull << lane);
     }
   }
@@ -363,7 +369,8 @@ __device__ __forceinline__ void build_masks(unsigned long long* masks, const int
 // The alignment by one workgroup of kAlignThreads threads for tile rows b (b = 0:
 // no valid configuration, so no tiles and no local slots); lds_u64 holds
 // align_lds_bytes(B, E_loc) bytes.
-__device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int b, int B, int k,
+template <typename IdT>
+__device__ __forceinline__ void align_block(const IdT* __restrict__ ids, int b, int B, int k,
                                             int e0, int E_loc, int32_t* __restrict__ sorted_slots,
                                             int32_t* __restrict__ block_expert,
                                             int32_t* __restrict__ num_blocks,
@@ -458,14 +465,14 @@ __device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int
     const int tc = t < B ? t : B - 1;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     for (int j0 = 0; j0 < k; j0 += 4) {
-      int v[4];
+      IdT v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = ids[(int64_t)tc * k + (j0 + u < k ? j0 + u : k - 1)];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (t >= B || j0 + u >= k) continue;
         const int64_t s = (int64_t)t * k + j0 + u;
-        const int e = v[u] - e0;
+        const int e = local_of(v[u], e0);
         if (e >= 0 && e < E_loc) {
           const int pos = base[(size_t)blk * E_loc + e] + __popcll(masks[e] & below);
           sorted_slots[pos] = (int32_t)s;
@@ -537,18 +544,50 @@ route_select_align_kernel(const float* __restrict__ logits, const float* __restr
               slot_pos, al);
 }
 
-// Steps 2-3 in one workgroup, after a multi-workgroup routing launch.
+// Steps 2-3 in one workgroup, after a multi-workgroup routing launch.  With
+// stage_ids the ids are first copied into LDS after the alignment's tables (16-byte
+// loads, issued before the selection so that they overlap it), and both alignment
+// passes read them there: stage_ids 1 copies the int32 ids, 2 stores each as its
+// local expert index in one byte (255: another GPU's expert; needs E_loc < 255),
+// for batches whose int32 ids would not fit.
 __global__ void __launch_bounds__(kAlignThreads)
 select_align_kernel(const int32_t* __restrict__ counts, const float* __restrict__ theta,
                     CostTable tab, const int32_t* __restrict__ ids, int32_t* __restrict__ variant,
                     float* __restrict__ t_hat, int32_t* __restrict__ sorted_slots,
                     int32_t* __restrict__ block_expert, int32_t* __restrict__ num_blocks,
-                    int32_t* __restrict__ slot_pos, int B, int k, int e0, int E_loc) {
+                    int32_t* __restrict__ slot_pos, int B, int k, int e0, int E_loc,
+                    int stage_ids) {
   extern __shared__ unsigned long long lds_u64[];
+  // after the tables, at a 16-byte boundary
+  int32_t* lds_ids = (int32_t*)((char*)lds_u64 + (align_table_bytes(B, E_loc) + 15) / 16 * 16);
+  uint8_t* lds_loc = (uint8_t*)lds_ids;
+  const int n = B * k;
+  const int n4 = n / 4;  // ids is 16-byte aligned (checked by the host before staging)
+  if (stage_ids == 1) {
+    for (int i = threadIdx.x; i < n4; i += kAlignThreads)
+      ((u32x4*)lds_ids)[i] = ((const u32x4*)ids)[i];
+    for (int i = n4 * 4 + threadIdx.x; i < n; i += kAlignThreads) lds_ids[i] = ids[i];
+  } else if (stage_ids == 2) {
+    auto loc = [&](int32_t id) __attribute__((always_inline)) {
+      const int e = id - e0;
+      return (uint32_t)(e >= 0 && e < E_loc ? e : 255);
+    };
+    for (int i = threadIdx.x; i < n4; i += kAlignThreads) {
+      const u32x4 q = ((const u32x4*)ids)[i];
+      ((uint32_t*)lds_loc)[i] = loc((int32_t)q[0]) | loc((int32_t)q[1]) << 8 |
+                                loc((int32_t)q[2]) << 16 | loc((int32_t)q[3]) << 24;
+    }
+    for (int i = n4 * 4 + threadIdx.x; i < n; i += kAlignThreads) lds_loc[i] = (uint8_t)loc(ids[i]);
+  }
+  // both paths below start with a barrier, which publishes the copy
   const int v = theta ? select_block<kAlignThreads>(counts, E_loc, theta, tab, variant, t_hat)
                       : given_variant(variant);
-  align_block(ids, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
-              slot_pos, lds_u64);
+  if (stage_ids == 2)
+    align_block(lds_loc, tile_rows(v), B, k, e0, E_loc, sorted_slots, block_expert, num_blocks,
+                slot_pos, lds_u64);
+  else
+    align_block(stage_ids ? lds_ids : ids, tile_rows(v), B, k, e0, E_loc, sorted_slots,
+                block_expert, num_blocks, slot_pos, lds_u64);
 }
 
 // more than 64 KiB of dynamic LDS needs an opt-in (gfx950 has 160 KiB per CU)
@@ -579,12 +618,23 @@ hipError_t launch_rsa(const moe_problem& p, const float* logits, const float* th
   }
   hipError_t e = launch_lm<L, MMAX>(p, logits, ids, w, counts, s);
   if (e != hipSuccess) return e;
-  e = allow_lds((const void*)select_align_kernel, al_bytes);
+  // the ids go to LDS too when they fit beside the tables (and are 16-byte aligned)
+  const size_t ids_bytes = (size_t)B * p.top_k * sizeof(int32_t);
+  const size_t al16 = (al_bytes + 15) / 16 * 16;
+  const size_t loc_bytes = ((size_t)B * p.top_k + 15) / 16 * 16;
+  const bool aligned16 = ((uintptr_t)ids & 15) == 0;
+  int stage = 0;
+  if (aligned16 && al16 + ids_bytes <= 150 * 1024)
+    stage = 1;
+  else if (aligned16 && p.local_experts < 255 && al16 + loc_bytes <= 150 * 1024)
+    stage = 2;
+  const size_t lds = stage == 1 ? al16 + ids_bytes : (stage == 2 ? al16 + loc_bytes : al_bytes);
+  e = allow_lds((const void*)select_align_kernel, lds);
   if (e != hipSuccess) return e;
-  select_align_kernel<<<1, kAlignThreads, al_bytes, s>>>(counts, theta, tab, ids, variant, t_hat,
-                                                         sorted_slots, block_expert, num_blocks,
-                                                         slot_pos, B, p.top_k, p.expert_begin,
-                                                         p.local_experts);
+  select_align_kernel<<<1, kAlignThreads, lds, s>>>(counts, theta, tab, ids, variant, t_hat,
+                                                    sorted_slots, block_expert, num_blocks,
+                                                    slot_pos, B, p.top_k, p.expert_begin,
+                                                    p.local_experts, stage);
   return hipGetLastError();
 }
 
