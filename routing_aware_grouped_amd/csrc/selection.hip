@@ -255,7 +255,9 @@ hipError_t launch_lm(const moe_problem& p, const float* logits, int32_t* ids, fl
   if (!single) {
     const int groups = threads / L;
     grid = (B + groups - 1) / groups;
-    if (grid > 4096) grid = 4096;
+    // at most two workgroups per CU: each then routes several token groups and
+    // adds its LDS histogram to the counts once, which cuts the global atomics
+    if (grid > 512) grid = 512;
     zero_counts_kernel<<<(p.local_experts + 255) / 256, 256, 0, s>>>(counts, p.local_experts);
   }
   if (single)
