@@ -32,7 +32,8 @@ template <bool F32>
 __global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slot_pos,
                const float* __restrict__ w, void* __restrict__ y, int B, int H, int k,
-               int64_t rows_max, int chunks, int n_shared, const int32_t* __restrict__ num_blocks,
+               int64_t rows_max, int chunks, int cw, int n_shared,
+               const int32_t* __restrict__ num_blocks,
                const int32_t* __restrict__ variant) {
   constexpr int VEC = F32 ? 4 : 8;  // elements per 16-byte vector
   __shared__ int s_pos[32 + kMaxShared];
@@ -66,44 +67,47 @@ combine_kernel(const void* __restrict__ y_slots, const int32_t* __restrict__ slo
       s_w[threadIdx.x] = 1.0f;
     }
     __syncthreads();
-    const int h0 = (c * kCombineThreads + (int)threadIdx.x) * VEC;
-    if (h0 >= H) continue;
-    float acc[VEC];
+    const int hend = (c + 1) * cw < H ? (c + 1) * cw : H;  // this item's columns [c cw, hend)
+    for (int h0 = c * cw + (int)threadIdx.x * VEC; h0 < hend; h0 += kCombineThreads * VEC) {
+      float acc[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int j0 = 0; j0 < lanes; j0 += kCombineBatch) {
-      u32x4 v[kCombineBatch];
+      for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+      for (int j0 = 0; j0 < lanes; j0 += kCombineBatch) {
+        u32x4 v[kCombineBatch];
 #pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u) {
-        const int pos = j0 + u < lanes ? s_pos[j0 + u] : -1;
-        v[u] = pos >= 0 ? *(const u32x4*)((const char*)y_slots + ((int64_t)pos * H + h0) * (F32 ? 4 : 2))
-                        : u32x4{0u, 0u, 0u, 0u};
-      }
-      // accumulated in ascending j, in fp32
+        for (int u = 0; u < kCombineBatch; ++u) {
+          const int pos = j0 + u < lanes ? s_pos[j0 + u] : -1;
+          const char* src = (const char*)y_slots + ((int64_t)pos * H + h0) * (F32 ? 4 : 2);
+          v[u] = pos >= 0 ? *(const u32x4*)src : u32x4{0u, 0u, 0u, 0u};
+        }
+        // accumulated in ascending j, in fp32
 #pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u) {
-        if (j0 + u >= lanes || s_pos[j0 + u] < 0) continue;
-        const float g = s_w[j0 + u];
-        if (F32) {
+        for (int u = 0; u < kCombineBatch; ++u) {
+          if (j0 + u >= lanes || s_pos[j0 + u] < 0) continue;
+          const float g = s_w[j0 + u];
+          if (F32) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(g, __uint_as_float(v[u][i]), acc[i]);
-        } else {
+            for (int i = 0; i < 4; ++i)
+              acc[i] = __builtin_fmaf(g, __uint_as_float(v[u][i]), acc[i]);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = __builtin_fmaf(g, __uint_as_float(v[u][i] << 16), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(g, __uint_as_float(v[u][i] & 0xFFFF0000u), acc[2 * i + 1]);
+            for (int i = 0; i < 4; ++i) {
+              acc[2 * i] = __builtin_fmaf(g, __uint_as_float(v[u][i] << 16), acc[2 * i]);
+              acc[2 * i + 1] =
+                  __builtin_fmaf(g, __uint_as_float(v[u][i] & 0xFFFF0000u), acc[2 * i + 1]);
+            }
           }
         }
       }
-    }
-    if (F32) {
-      f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)((float*)y + (int64_t)t * H + h0) = o;
-    } else {
-      u32x4 o;
+      if (F32) {
+        f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
+        *(f32x4*)((float*)y + (int64_t)t * H + h0) = o;
+      } else {
+        u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      *(u32x4*)((uint16_t*)y + (int64_t)t * H + h0) = o;
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        *(u32x4*)((uint16_t*)y + (int64_t)t * H + h0) = o;
+      }
     }
   }
 }
@@ -114,17 +118,21 @@ hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32
                           const float* w, const int32_t* num_blocks, const int32_t* variant,
                           void* y, int64_t rows_max, hipStream_t s) {
   const int n_shared = num_blocks && variant ? p.shared_experts : 0;
+  // a small batch splits each token's columns over workgroups (2048 bf16 columns
+  // per item); a large one gives each workgroup whole tokens
   const int vec = p.act_dtype == MOE_F32 ? 4 : 8;
-  const int chunks = (p.hidden / vec + kCombineThreads - 1) / kCombineThreads;
+  const int span = kCombineThreads * vec;
+  const int chunks = p.tokens >= 512 ? 1 : (p.hidden + span - 1) / span;
+  const int cw = (p.hidden + chunks * span - 1) / (chunks * span) * span;
   const int64_t items = (int64_t)p.tokens * chunks;
   const int grid = items < 4096 ? (int)items : 4096;
   if (p.act_dtype == MOE_F32)
     combine_kernel<true><<<grid, kCombineThreads, 0, s>>>(y_slots, slot_pos, w, y, p.tokens,
-                                                          p.hidden, p.top_k, rows_max, chunks,
+                                                          p.hidden, p.top_k, rows_max, chunks, cw,
                                                           n_shared, num_blocks, variant);
   else
     combine_kernel<false><<<grid, kCombineThreads, 0, s>>>(y_slots, slot_pos, w, y, p.tokens,
-                                                           p.hidden, p.top_k, rows_max, chunks,
+                                                           p.hidden, p.top_k, rows_max, chunks, cw,
                                                            n_shared, num_blocks, variant);
   return hipGetLastError();
 }
