@@ -206,7 +206,7 @@ moe_status moe_align_sort(const moe_problem* p, const int32_t* topk_ids, const i
  * that counts, chooses and lays out the tiles; here a batch that one workgroup
  * routes (B <= 4 * (1024 / L), L the lanes per token: the smallest power of two
  * >= E up to 64) runs in a single one-workgroup launch, a larger one as the
- * routing launch(es) followed by one select-and-align workgroup.  theta NULL: no
+ * routing launch(es) followed by one select-and-align launch.  theta NULL: no
  * selection; the configuration already in *variant is used and t_hat is not
  * written (t_hat may be NULL in any case).  Errors: as the three calls. */
 moe_status moe_route_select_align(const moe_problem* p, const float* logits, const float* theta,

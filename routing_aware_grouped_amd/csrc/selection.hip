@@ -2,7 +2,7 @@
 // histogram, the on-GPU choice of the tile configuration, and the stable grouping
 // of the routed slots into padded tiles; each as its own kernel (the three C entry
 // points) and fused (moe_route_select_align): one workgroup for batches one
-// workgroup routes, else the routing launch then one select+align workgroup.
+// workgroup routes, else the routing launch then one select+align launch.
 //
 // ---- step 1 ----
 //
@@ -50,7 +50,9 @@
 // (ceil(0/b) = 0, as in Eq. 1).  Outputs: sorted_slots [R], block_expert[R/b],
 // num_blocks, and the inverse map slot_pos (-1 for slots of other GPUs' experts).
 //
-// Design (one workgroup of 16 waves; the whole step stays in LDS):
+// Design (workgroups of 16 waves; the whole step stays in LDS; a grid of up to 64
+// workgroups, one per 64-token block, where each repeats passes 1-2 and writes its
+// share of passes 3-4):
 //   * a token's k experts are distinct, so inside one expert ascending s means
 //     ascending token t.  Tokens are cut into 64-token blocks, one lane per token.
 //     For a block, each wave builds a 64-bit lane mask per expert in LDS (bit i set
@@ -309,7 +311,7 @@ __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
           th[3], (float)(active + tab.a_shared),
           __builtin_fmaf(th[2], (float)T, __builtin_fmaf(th[1], (float)W, th[0])));
       tv[v] = t;
-      if (t_hat) t_hat[v] = t;
+      if (t_hat && blockIdx.x == 0) t_hat[v] = t;
     }
   }
   __syncthreads();
@@ -317,7 +319,7 @@ __device__ __forceinline__ int select_block(const int32_t* counts, int E_loc,
     int best = 0;
     for (int v = 1; v < kNumVariants; ++v)
       if (tv[v] < tv[best]) best = v;
-    *variant = best;
+    if (blockIdx.x == 0) *variant = best;  // every workgroup of a grid chooses the same
     chosen = best;
   }
   __syncthreads();
@@ -368,9 +370,13 @@ __device__ __forceinline__ void build_masks(unsigned long long* masks, const IdT
   __builtin_amdgcn_wave_barrier();
 }
 
-// The alignment by one workgroup of kAlignThreads threads for tile rows b (b = 0:
-// no valid configuration, so no tiles and no local slots); lds_u64 holds
-// align_lds_bytes(B, E_loc) bytes.
+// The alignment for tile rows b (b = 0: no valid configuration, so no tiles and no
+// local slots) by a grid of workgroups of kAlignThreads threads; lds_u64 holds
+// align_lds_bytes(B, E_loc) bytes.  Every workgroup computes the counts and the
+// offsets (passes 1-2) in full; the writes (passes 3-4) are divided among the
+// workgroups: padding rows by expert, block_expert by row-block and the scatter
+// by 64-token block.  The scatter is bound by one CU's store path (64 scattered
+// 4-byte stores per wave instruction), which the division spreads over CUs.
 template <typename IdT>
 __device__ __forceinline__ void align_block(const IdT* __restrict__ ids, int b, int B, int k,
                                             int e0, int E_loc, int32_t* __restrict__ sorted_slots,
@@ -390,9 +396,12 @@ __device__ __forceinline__ void align_block(const IdT* __restrict__ ids, int b, 
   const int wave = tid / kWave;
   unsigned long long* masks = masks_all + (size_t)wave * E_loc;
 
+  const int wg = blockIdx.x, nwg = gridDim.x;
   if (b == 0) {  // configuration index out of range: no tiles, no local slots
-    for (int64_t s = tid; s < (int64_t)B * k; s += kAlignThreads) slot_pos[s] = -1;
-    if (tid == 0) *num_blocks = 0;
+    for (int64_t s = (int64_t)wg * kAlignThreads + tid; s < (int64_t)B * k;
+         s += (int64_t)nwg * kAlignThreads)
+      slot_pos[s] = -1;
+    if (wg == 0 && tid == 0) *num_blocks = 0;
     return;
   }
 
@@ -443,13 +452,13 @@ __device__ __forceinline__ void align_block(const IdT* __restrict__ ids, int b, 
   for (int i = tid; i < nblk * E_loc; i += kAlignThreads) base[i] += off[i % E_loc];
   const int R = off[E_loc];
   const int nb = R / b;
-  if (tid == 0) *num_blocks = nb;
+  if (wg == 0 && tid == 0) *num_blocks = nb;
 
   // pass 3: padding rows [off[e] + n_e, off[e + 1]), one wave per expert, and the
   // block -> expert table
-  for (int e = wave; e < E_loc; e += kAlignWaves)
+  for (int e = wg * kAlignWaves + wave; e < E_loc; e += nwg * kAlignWaves)
     for (int r = off[e] + tot[e] + lane; r < off[e + 1]; r += kWave) sorted_slots[r] = -1;
-  for (int i = tid; i < nb; i += kAlignThreads) {
+  for (int i = wg * kAlignThreads + tid; i < nb; i += nwg * kAlignThreads) {
     const int row = i * b;
     int lo = 0, hi = E_loc - 1;  // the largest e with off[e] <= row
     while (lo < hi) {
@@ -460,8 +469,8 @@ __device__ __forceinline__ void align_block(const IdT* __restrict__ ids, int b, 
   }
   __syncthreads();
 
-  // pass 4: stable scatter
-  for (int blk = wave; blk < nblk; blk += kAlignWaves) {
+  // pass 4: stable scatter; workgroup wg takes blocks wg, wg + nwg, ...
+  for (int blk = wave * nwg + wg; blk < nblk; blk += kAlignWaves * nwg) {
     build_masks(masks, ids, blk, B, k, e0, E_loc, lane);
     const int t = blk * kWave + lane;
     const int tc = t < B ? t : B - 1;
@@ -485,6 +494,13 @@ __device__ __forceinline__ void align_block(const IdT* __restrict__ ids, int b, 
       }
     }
   }
+}
+
+// Workgroups of an alignment grid: one per 64-token block, at most kAlignMaxWg.
+constexpr int kAlignMaxWg = 64;
+inline int align_grid(int B) {
+  const int nblk = (B + kWave - 1) / kWave;
+  return nblk < 1 ? 1 : (nblk < kAlignMaxWg ? nblk : kAlignMaxWg);
 }
 
 __device__ __forceinline__ int tile_rows(int v) {
@@ -546,7 +562,8 @@ route_select_align_kernel(const float* __restrict__ logits, const float* __restr
               slot_pos, al);
 }
 
-// Steps 2-3 in one workgroup, after a multi-workgroup routing launch.  With
+// Steps 2-3 after a multi-workgroup routing launch, on the alignment grid (every
+// workgroup makes the same choice; workgroup 0 writes it).  With
 // stage_ids the ids are first copied into LDS after the alignment's tables (16-byte
 // loads, issued before the selection so that they overlap it), and both alignment
 // passes read them there: stage_ids 1 copies the int32 ids, 2 stores each as its
@@ -633,10 +650,9 @@ hipError_t launch_rsa(const moe_problem& p, const float* logits, const float* th
   const size_t lds = stage == 1 ? al16 + ids_bytes : (stage == 2 ? al16 + loc_bytes : al_bytes);
   e = allow_lds((const void*)select_align_kernel, lds);
   if (e != hipSuccess) return e;
-  select_align_kernel<<<1, kAlignThreads, lds, s>>>(counts, theta, tab, ids, variant, t_hat,
-                                                    sorted_slots, block_expert, num_blocks,
-                                                    slot_pos, B, p.top_k, p.expert_begin,
-                                                    p.local_experts, stage);
+  select_align_kernel<<<align_grid(B), kAlignThreads, lds, s>>>(
+      counts, theta, tab, ids, variant, t_hat, sorted_slots, block_expert, num_blocks, slot_pos, B,
+      p.top_k, p.expert_begin, p.local_experts, stage);
   return hipGetLastError();
 }
 
@@ -674,9 +690,9 @@ hipError_t launch_align_sort(const moe_problem& p, const int32_t* ids, const int
   const size_t lds = align_lds_bytes(p.tokens, p.local_experts);
   hipError_t e = allow_lds((const void*)align_sort_kernel, lds);
   if (e != hipSuccess) return e;
-  align_sort_kernel<<<1, kAlignThreads, lds, s>>>(ids, variant, p.tokens, p.top_k, p.expert_begin,
-                                                  p.local_experts, sorted_slots, block_expert,
-                                                  num_blocks, slot_pos);
+  align_sort_kernel<<<align_grid(p.tokens), kAlignThreads, lds, s>>>(
+      ids, variant, p.tokens, p.top_k, p.expert_begin, p.local_experts, sorted_slots, block_expert,
+      num_blocks, slot_pos);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ def test_routing_and_permutation_full_batch(shape, B, alpha):
     ("kimi_share", 2048, 0.05)])
 def test_fused_selection_matches_steps(shape, B, alpha):
     """moe_route_select_align (one launch for a batch one workgroup routes, else
-    the routing launches and one select+align workgroup) writes exactly what
+    the routing launches and one select+align launch) writes exactly what
     moe_route_topk, moe_select_config and moe_align_sort write, with a chosen and
     with a given configuration."""
     G.say(f"fused selection {shape} B={B} alpha={alpha}")
