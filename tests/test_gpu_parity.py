@@ -58,7 +58,9 @@ def test_tiny_large_activations_and_ragged_tokens():
 @pytest.mark.parametrize("shape,B,alpha", [
     ("qwen3", 1, 0.3), ("qwen3", 4096, 0.05), ("qwen3", 1000, 10.0), ("mixtral", 2048, 0.1),
     ("mixtral", 3, 1.0), ("dsv3_share", 2048, 1.0), ("kimi_share", 4096, 0.05),
-    ("kimi_share", 65, 0.05)])
+    ("kimi_share", 65, 0.05),
+    # more 64-token blocks than alignment workgroups (64): some take two or three
+    ("qwen3", 6000, 1.0), ("mixtral", 8193, 1.0)])
 def test_routing_and_permutation_full_batch(shape, B, alpha):
     G.say(f"routing {shape} B={B} alpha={alpha}")
     sh = synth.SHAPES[shape]
@@ -246,6 +248,28 @@ def test_out_of_range_variant_gives_no_tiles():
     assert int(b.num_blocks.item()) == 0
     assert torch.all(b.slot_pos == -1)
     assert torch.all(b.y == 0)
+
+
+def test_out_of_range_variant_on_an_alignment_grid():
+    """The same at B = 1000 (16 alignment workgroups, each clearing its share of
+    slot_pos)."""
+    sh = synth.SHAPES["qwen3"]
+    B = 1000
+    logits, p = synth.routing_logits(sh, B, 1.0, np.random.default_rng([B, 5]))
+    p_ = L.moe_problem(B, 256, 256, sh.num_experts, 0, sh.local_experts, sh.top_k, synth.BF16,
+                       synth.BF16, 1)
+    z = torch.zeros
+    w1 = z(sh.local_experts, 256, 256, dtype=torch.bfloat16)
+    b = L.allocate(p_, torch.from_numpy(logits), z(B, 256, dtype=torch.bfloat16), w1, w1, w1,
+                   theta=G.theta_forcing(0))
+    L.route(b)
+    b.variant.fill_(V + 3)
+    b.slot_pos.fill_(7)
+    b.num_blocks.fill_(9)
+    L.align(b)
+    torch.cuda.synchronize()
+    assert int(b.num_blocks.item()) == 0
+    assert torch.all(b.slot_pos == -1)
 
 
 def test_fp8_decode_every_code():
