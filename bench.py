@@ -16,8 +16,11 @@ It is replayed from a HIP graph with the inputs resident in HBM and the caches
 cold. Before every timed replay a 1 GiB scratch write evicts L2 and the Infinity
 Cache; the write is outside the timed events.
 
-The headline point is the Mixtral-8x7B-shaped layer (H 4096, I 14336, 8 experts,
-top-2, bf16) at 128 tokens, alpha = 1.
+The headline point is the largest single-GPU configuration the metric is quoted
+on: the Mixtral-8x7B-shaped layer (H 4096, I 14336, 8 experts, top-2, bf16) at
+2048 tokens, alpha = 1.  The last stdout line is one compact JSON record (the
+headline, its roofline and CPU baseline, one summary per swept workload); the
+full result with every sweep point goes to --out.
 
 The same run sweeps the four full-size workloads over their token counts and
 alphas:
@@ -258,29 +261,35 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
 
 
 def kernel_segments(torch, L, b, T, reps):
-    """Per-call HIP-event timing on the launch stream, eager, each step cold."""
+    """Per-call HIP-event timing, eager, each step cold.  Every call is launched on
+    one dedicated stream and its events are recorded on that same stream, so each
+    pair brackets exactly that call's kernels."""
     names = ["route_select_align", "grouped_gate_up", "grouped_down", "combine"]
     fns = [L.route_select_align, L.gate_up, L.down, L.combine]
     acc = {n: [] for n in names}
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
     for _ in range(reps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(fns))]
         for i, f in enumerate(fns):
             T.flush()
-            evs[2 * i].record()
-            f(b)
-            evs[2 * i + 1].record()
+            s.wait_stream(torch.cuda.current_stream())
+            evs[2 * i].record(s)
+            f(b, stream=s)
+            evs[2 * i + 1].record(s)
+            torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for i, n in enumerate(names):
             acc[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3)
     return {n: statistics.fmean(v) for n, v in acc.items()}
 
 
-def cpu_baseline(np, oracle, layer, sample_tokens):
+def cpu_baseline(np, oracle, layer, sample_tokens, nthreads=None):
     """The CPU oracle as it stands, on a bounded token sample of the same load;
     reported as microseconds per layer scaled by B / sample."""
     n = min(layer.tokens, sample_tokens)
     toks = np.random.default_rng(1234).choice(layer.tokens, n, replace=False).astype(np.int32)
-    nthreads = oracle.max_threads()
+    nthreads = nthreads or oracle.max_threads()
     t0 = time.perf_counter()
     ids, w = oracle.route_topk(layer.logits, layer.shape.top_k)
     oracle.counts(ids, layer.expert_begin, layer.shape.local_experts)
@@ -296,31 +305,93 @@ def cpu_baseline(np, oracle, layer, sample_tokens):
                        f"measured {t_route + t_ffn:.1f} s")
 
 
-def sweep_shape(torch, np, synth, L, T, shape, V, reps, log_prefix=""):
-    sw = SWEEPS[shape]
+def cpu_one_thread(np, oracle, synth):
+    """The oracle on one thread for the tiny workload (whole layer, 64 tokens) and
+    the Qwen3-30B-A3B-shaped one (B = 128, alpha = 1, 32-token sample scaled)."""
+    out = {}
+    for name, shape, B, alpha, sample in (("tiny_b64", "tiny", 64, None, 64),
+                                          ("qwen3_b128_a1", "qwen3", 128, 1.0, 32)):
+        layer = synth.make_layer(shape, B, alpha, 0)
+        r = cpu_baseline(np, oracle, layer, sample, nthreads=1)
+        out[name] = dict(us=r["value"], sample=f"{min(B, sample)} of {B} tokens")
+    return out
+
+
+# the scoring grid of the blueprint: every power-of-two token count of each
+# workload's range and reps 0..7 (used with --density full)
+DENSE = {
+    "mixtral": dict(tokens=[1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048],
+                    alphas=[0.1, 1.0, 10.0, 100.0]),
+    "qwen3": dict(tokens=[1 << i for i in range(13)], alphas=[0.05, 0.3, 1.0, 10.0]),
+    "dsv3_share": dict(tokens=[1 << i for i in range(9)], alphas=[0.1, 1.0, 10.0]),
+    "kimi_share": dict(tokens=[8 << i for i in range(10)], alphas=[0.05]),
+}
+
+
+def ranks(xs):
+    """Ranks 1..n with ties averaged."""
+    order = sorted(range(len(xs)), key=lambda i: xs[i])
+    r = [0.0] * len(xs)
+    i = 0
+    while i < len(order):
+        j = i
+        while j + 1 < len(order) and xs[order[j + 1]] == xs[order[i]]:
+            j += 1
+        for q in range(i, j + 1):
+            r[order[q]] = (i + j) / 2 + 1
+        i = j + 1
+    return r
+
+
+def spearman(a, b):
+    """Spearman rank correlation (Pearson correlation of the tie-averaged ranks)."""
+    ra, rb = ranks(a), ranks(b)
+    ma, mb = statistics.fmean(ra), statistics.fmean(rb)
+    num = sum((x - ma) * (y - mb) for x, y in zip(ra, rb))
+    den = math.sqrt(sum((x - ma) ** 2 for x in ra) * sum((y - mb) ** 2 for y in rb))
+    return num / den if den > 0 else None
+
+
+def sweep_shape(torch, np, synth, L, T, shape, V, reps, density="grid"):
+    base = shape.split("_fp8")[0].removesuffix("_sh")
+    sw = DENSE[base] if density == "full" else SWEEPS[shape]
+    rep_list = range(8) if density == "full" else range(1)
     wdev = synth.make_weights_device(shape)
     theta, theta_src = load_theta(shape, V)
     nowts = {"w1": None, "w3": None, "w2": None, "s1": None, "s3": None, "s2": None}
     out = []
     for tok in sw["tokens"]:
         for a in sw["alphas"]:
-            tb = 8 * tok if shape.startswith("dsv3_share") else tok
-            r, *_ = run_point(torch, np, synth, L, T, shape, tb, a, wdev, nowts, theta, V, reps, 3,
-                              exhaustive=True)
-            if shape.startswith("dsv3_share"):
-                r["tokens_per_gpu"] = tok
-            log(f"[bench] {shape} B={tb} alpha={a}: {r['us']:.1f} us, v={r['variant']} "
-                f"best={r['best_variant']} gap={r['gap_to_exhaustive']:.3f} "
-                f"roof={r['roof_frac']:.3f} ({r['binding']}) per-variant {r['us_per_variant']}")
-            out.append(r)
+            for rep in rep_list:
+                tb = 8 * tok if shape.startswith("dsv3_share") else tok
+                r, *_ = run_point(torch, np, synth, L, T, shape, tb, a, wdev, nowts, theta, V, reps,
+                                  3, exhaustive=True, rep=rep)
+                r["rep"] = rep
+                if shape.startswith("dsv3_share"):
+                    r["tokens_per_gpu"] = tok
+                log(f"[bench] {shape} B={tb} alpha={a} rep={rep}: {r['us']:.1f} us, "
+                    f"v={r['variant']} best={r['best_variant']} "
+                    f"gap={r['gap_to_exhaustive']:.3f} roof={r['roof_frac']:.3f} ({r['binding']}) "
+                    f"per-variant {r['us_per_variant']}")
+                out.append(r)
     del wdev
     torch.cuda.empty_cache()
     gaps = [max(r["gap_to_exhaustive"], 0.0) for r in out]
+    # rank agreement of the model's predictions with the measured times (RaMP
+    # section 3.1 reports it): per load over the compiled configurations, and pooled
+    # over every (load, configuration) pair
+    per_load = [spearman(r["t_hat"], r["us_per_variant"]) for r in out]
+    per_load = [x for x in per_load if x is not None]
+    pooled = spearman([t for r in out for t in r["t_hat"]], [t for r in out for t in r["us_per_variant"]])
+    worst = max(out, key=lambda r: r["gap_to_exhaustive"])
     chooser = dict(geomean_gap=round(math.exp(statistics.fmean([math.log1p(x) for x in gaps])) - 1, 4),
                    worst_gap=round(max(gaps), 4),
+                   worst_load=dict(tokens=worst["tokens"], alpha=worst["alpha"], rep=worst["rep"]),
                    within_5pct=round(sum(g_ <= 0.05 for g_ in gaps) / len(gaps), 3),
+                   spearman_rho=round(statistics.fmean(per_load), 4) if per_load else None,
+                   spearman_rho_pooled=round(pooled, 4) if pooled is not None else None,
                    theta=theta_src or "untuned default (th1 = 1: fewest waves)")
-    res = dict(points=out, chooser=chooser)
+    res = dict(points=out, chooser=chooser, density=density)
     loads = fit_loads(shape)
     if loads:
         # the pages' simpler policies, fit on the cost model's fit loads and scored
@@ -336,24 +407,55 @@ def sweep_shape(torch, np, synth, L, T, shape, V, reps, log_prefix=""):
 
 
 # ----------------------------------------------------------------------- main --
+WORKLOAD_NAMES = {
+    "mixtral": "Mixtral-8x7B-shaped fused MoE layer",
+    "qwen3": "Qwen3-30B-A3B-shaped fused MoE layer",
+    "dsv3_share": "DeepSeek-V3-shaped one-GPU expert share",
+    "kimi_share": "Kimi-K2-shaped one-GPU expert share",
+}
+
+
+def geomean(xs):
+    xs = [x for x in xs if x and x > 0]
+    return round(math.exp(statistics.fmean([math.log(x) for x in xs])), 4) if xs else None
+
+
+def sweep_summary(res):
+    """One short record per workload: points, the binding-roofline fraction of the
+    chosen configuration (geomean, min, max) and the chooser's gap to exhaustive."""
+    pts = res["points"]
+    fr = [p["roof_frac"] for p in pts]
+    out = dict(n=len(pts), roof_geo=geomean(fr), roof_min=round(min(fr), 4),
+               roof_max=round(max(fr), 4), gap_geo=res["chooser"]["geomean_gap"],
+               gap_worst=res["chooser"]["worst_gap"], within5=res["chooser"]["within_5pct"])
+    rho = res["chooser"].get("spearman_rho")
+    if rho is not None:
+        out["rho"] = rho
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--shape", default="mixtral", choices=sorted(SWEEPS))
-    ap.add_argument("--tokens", type=int, default=128)
+    ap.add_argument("--tokens", type=int, default=2048)
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--sweep", default="mixtral,qwen3,dsv3_share,kimi_share,dsv3_share_fp8a,"
                                        "kimi_share_fp8a,dsv3_share_fp8ah,kimi_share_fp8ah,"
                                        "dsv3_share_sh",
                     help="comma-separated workloads to sweep ('' for none)")
     ap.add_argument("--sweep-reps", type=int, default=15)
+    ap.add_argument("--density", default="grid", choices=["grid", "full"],
+                    help="grid: the token counts and alphas of SWEEPS, rep 0; full: every "
+                         "power-of-two token count and reps 0..7")
     ap.add_argument("--cpu", type=int, default=1, help="1: time the CPU oracle baseline")
-    ap.add_argument("--cpu-sample", type=int, default=128)
+    ap.add_argument("--cpu-sample", type=int, default=256)
     ap.add_argument("--exhaustive", type=int, default=1,
                     help="1: also time every configuration at the headline point")
-    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "bench_full.json"),
+                    help="file for the full result (every sweep point); '' for none")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size kernel that scales HBM byte counters) and exit")
@@ -400,7 +502,7 @@ def main():
     # ---- headline point: K timed steps ------------------------------------------------
     log(f"[bench] headline {args.shape} B={args.tokens} alpha={args.alpha}")
     head, layer, b, w = run_point(torch, np, synth, L, T, args.shape, args.tokens, args.alpha, wdev,
-                                  whost, theta, V, args.steps, args.warmup,
+                                  whost, theta, V, max(10, args.steps // 2), 3,
                                   exhaustive=bool(args.exhaustive))
     g = T.graph(lambda: L.forward(b))
     torch.cuda.synchronize()
@@ -424,17 +526,18 @@ def main():
     wl_key = f"{args.shape}:B{args.tokens}:a{args.alpha:g}:v{head['variant']}"
     roofline = dict(bound=bound, achieved=round(achieved, 2), peak=round(peak, 1), unit=unit,
                     frac=round(achieved / peak, 4), traffic=measured_traffic(wl_key),
-                    kernel="ffn_kernel<1,*> (moe_grouped_gate_up: grouped gate/up GEMM + SwiGLU)",
-                    alg_bytes_per_launch=int(w["gate_up_bytes"]),
-                    alg_flops_per_launch=int(w["gate_up_flops"]),
-                    avg_launch_us=round(seg["grouped_gate_up"], 3), traffic_key=wl_key,
-                    kernel_source_sha=kernel_source_hash())
+                    kernel="ffn_kernel<1,*> (moe_grouped_gate_up)",
+                    alg_bytes=int(w["gate_up_bytes"]), alg_flops=int(w["gate_up_flops"]),
+                    avg_launch_us=round(seg["grouped_gate_up"], 3))
 
     # ---- CPU oracle baseline ------------------------------------------------------------
-    cpu = None
+    cpu = cpu1 = None
     if args.cpu:
-        log("[bench] timing the CPU oracle on a token sample")
+        log(f"[bench] timing the CPU oracle on a {args.cpu_sample}-token sample")
         cpu = cpu_baseline(np, oracle, layer, args.cpu_sample)
+        log(f"[bench] cpu_baseline {cpu}")
+        cpu1 = cpu_one_thread(np, oracle, synth)
+        log(f"[bench] oracle on one thread: {cpu1}")
     del whost
 
     # ---- sweeps -------------------------------------------------------------------------
@@ -446,9 +549,20 @@ def main():
         torch.cuda.empty_cache()
     for shp in shapes:
         log(f"[bench] sweep {shp}")
-        sweeps[shp] = sweep_shape(torch, np, synth, L, T, shp, V, args.sweep_reps)
+        sweeps[shp] = sweep_shape(torch, np, synth, L, T, shp, V, args.sweep_reps,
+                                   args.density)
 
     sh = layer.shape
+    head_layer = dict(variant=head["variant"], best_variant=head.get("best_variant"),
+                      gap_to_exhaustive=head.get("gap_to_exhaustive"),
+                      us_per_variant=head.get("us_per_variant"), roof_us=head["roof_us"],
+                      roof_frac=round(head["roof_us"] / st["median"], 4), binding=head["binding"],
+                      hbm_frac=round(w["layer_bytes"] / (st["median"] * 1e-6) / HBM_PEAK, 4),
+                      mfma_frac=round(w["mfma_s"] / (st["median"] * 1e-6), 4),
+                      segments_us={k: round(v, 1) for k, v in seg.items()},
+                      p10=round(st["p10"], 1), p90=round(st["p90"], 1),
+                      timed_wall_s=round(t_wall, 3))
+    wname = WORKLOAD_NAMES.get(sh.name.split("_fp8")[0].removesuffix("_sh"), sh.name)
     out = {
         "metric": METRIC,
         "value": round(st["median"], 3),
@@ -462,29 +576,30 @@ def main():
         "vs_baseline": None,
         "dtype": {synth.F32: "f32", synth.BF16: "bf16"}[sh.act_dtype],
         "data": "synthetic (Dirichlet-skewed Gumbel-top-k routing, N(0,0.02) activations/weights)",
-        "config": {"workload": f"{args.shape}-shaped fused MoE layer", "tokens": args.tokens,
-                   "alpha": args.alpha, "hidden": sh.hidden, "inter": sh.inter,
-                   "experts": sh.num_experts, "local_experts": sh.local_experts, "top_k": sh.top_k,
+        "config": {"workload": f"{wname}, B={args.tokens}, alpha={args.alpha:g}",
+                   "tokens": args.tokens, "alpha": args.alpha, "hidden": sh.hidden,
+                   "inter": sh.inter, "experts": sh.num_experts, "top_k": sh.top_k,
                    "weights": synth.DTYPE_NAMES[sh.weight_dtype], "parallelism": "single GPU",
                    "timing": "HIP graph replay, cold L2/Infinity Cache, hipEvent per step, median"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "layer": dict(variant=head["variant"], best_variant=head.get("best_variant"),
-                      gap_to_exhaustive=head.get("gap_to_exhaustive"),
-                      us_per_variant=head.get("us_per_variant"), roof_us=head["roof_us"],
-                      roof_frac=round(head["roof_us"] / st["median"], 4), binding=head["binding"],
-                      hbm_frac=round(w["layer_bytes"] / (st["median"] * 1e-6) / HBM_PEAK, 4),
-                      mfma_frac=round(w["mfma_s"] / (st["median"] * 1e-6), 4),
-                      segments_us={k: round(v, 3) for k, v in seg.items()},
-                      theta=theta_src or "untuned default (th1 = 1: fewest waves)",
-                      timed_wall_s=round(t_wall, 3), p10=round(st["p10"], 3), p90=round(st["p90"], 3)),
-        "sweeps": sweeps,
+        "layer": head_layer,
     }
-    line = json.dumps(out)
-    print(line, flush=True)
+    full = dict(out, cpu_one_thread=cpu1, theta=theta_src or "untuned default (th1 = 1)",
+                sweeps=sweeps, roofline=dict(roofline, traffic_key=wl_key,
+                                             kernel_source_sha=kernel_source_hash()))
     if args.out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
         with open(args.out, "w") as f:
-            f.write(line + "\n")
+            json.dump(full, f)
+            f.write("\n")
+        log(f"[bench] full result (every sweep point) written to {args.out}")
+    # the last stdout line: compact (a few kB), one summary record per swept workload
+    out["sweep_summary"] = {k: sweep_summary(v) for k, v in sweeps.items()}
+    if cpu1:
+        out["cpu_one_thread_us"] = {k: v["us"] for k, v in cpu1.items()}
+    line = json.dumps(out, separators=(",", ":"))
+    print(line, flush=True)
 
 
 if __name__ == "__main__":

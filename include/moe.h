@@ -85,6 +85,26 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
+/* The device status word.  Host validation cannot see values that live in device
+ * memory (the chosen configuration, the row-block count), so the grouped FFN
+ * checks them on the device and reports what it found in the int32 at byte
+ * offset MOE_DEVICE_STATUS_OFFSET of its workspace: 0 (MOE_DEV_OK) when both were
+ * valid, else one of the codes below.  Every grouped-FFN launch rewrites it
+ * (workgroup 0, once per launch), so after a call it describes that call's
+ * inputs; the caller reads it with an ordinary device-to-host copy when it wants
+ * to (the library itself never does).  What the kernels do on such inputs:
+ *   MOE_DEV_BAD_VARIANT  *variant outside [0, V): no tile runs, y_slots and h are
+ *                        not written (moe_align_sort has already written
+ *                        num_blocks = 0 and slot_pos = -1 for such a variant, so
+ *                        moe_combine then writes zeros);
+ *   MOE_DEV_BAD_BLOCKS   *num_blocks < 0, or more row-blocks (shared experts'
+ *                        included) than rows_max holds: only the row-blocks that
+ *                        fit are computed. */
+#define MOE_DEVICE_STATUS_OFFSET 0
+#define MOE_DEV_OK 0
+#define MOE_DEV_BAD_VARIANT 1
+#define MOE_DEV_BAD_BLOCKS 2
+
 /* The problem statement shared by every call (B tokens of H hidden activations,
  * E experts of intermediate size I, top-k routing; this GPU holds the contiguous
  * expert block [expert_begin, expert_begin + local_experts), as under expert
@@ -119,8 +139,9 @@ typedef struct moe_sizes {
   int64_t rows_max;        /* capacity (elements) of sorted_slots; rows of y_slots */
   int64_t blocks_max;      /* capacity (elements) of block_expert                  */
   int64_t y_slots_bytes;   /* rows_max * H * sizeof(act)                           */
-  int64_t workspace_bytes; /* grouped_ffn workspace: header, h, (act_quant: x codes
-                              and scales; 2: h codes and scales), partial tiles     */
+  int64_t workspace_bytes; /* grouped_ffn workspace: a 256-byte header (the device
+                              status word first), h, (act_quant: x codes and
+                              scales; 2: h codes and scales), partial tiles         */
   int64_t align_ws_bytes;  /* reserved, 0 in this version                          */
 } moe_sizes;
 
@@ -160,7 +181,8 @@ moe_status moe_variant_info(int32_t v, int32_t* out);
  *   b[v]  = BLOCK_M;  q1[v] = I / BLOCK_N1 and q2[v] = (H / BLOCK_N2) * split_k,
  *   the tiles of one row-block in each phase (q_c of RaMP Eq. 1, summed over the
  *   two phases); S1[v], S2[v] = tiles resident on the GPU at once in each phase
- *   = compute units * workgroups per compute unit (S_c of RaMP Eq. 1).
+ *   = the persistent grid, min(compute units * 2, 512) workgroups (S_c of RaMP
+ *   Eq. 1).
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP. */
 moe_status moe_cost_constants(const moe_problem* p, int32_t* b, int32_t* q1, int32_t* q2,
                               int32_t* S1, int32_t* S2);

@@ -210,6 +210,7 @@ struct FfnArgs {
   int64_t rows_max;
   const float* xs;  // [B][H/128] activation scales of the FP8 activation path
   int n_shared;     // shared experts (row-blocks after the routed ones)
+  int32_t* status;  // device status word (MOE_DEV_* bits)
 };
 
 // ring slots of per-tile metadata (see Tile::run_all)
@@ -986,6 +987,25 @@ __device__ __forceinline__ bool block_counts(const FfnArgs& g, int v, int& nb, i
   return nb > 0;
 }
 
+// The device status word: MOE_DEV_BAD_VARIANT for a configuration index outside
+// the menu, MOE_DEV_BAD_BLOCKS for a row-block count below zero or beyond what the
+// buffers hold (the launch then runs only the row-blocks that fit).  Workgroup 0
+// writes it once per launch, so each call reports its own inputs.
+template <bool SH>
+__device__ __forceinline__ void report_status(const FfnArgs& g, int v, int nbr) {
+  if (blockIdx.x != 0 || threadIdx.x != 0 || g.status == nullptr) return;
+  int st = 0;
+  if (v < 0 || v >= kNumVariants) {
+    st = MOE_DEV_BAD_VARIANT;
+  } else {
+    const int bm = kVariants[v].bm;
+    int64_t nb = nbr;
+    if (SH) nb += (int64_t)g.n_shared * ((g.slots / g.k + bm - 1) / bm);
+    if (nbr < 0 || nb > g.rows_max / bm) st = MOE_DEV_BAD_BLOCKS;
+  }
+  *g.status = st;
+}
+
 template <int PHASE, int WKIND, bool SH>
 __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -993,6 +1013,7 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   const int v = *g.variant;
   int nb = *g.num_blocks;
   int nbr = nb;
+  report_status<SH>(g, v, nbr);
   if constexpr (!SH) {
     if (v < 0 || v >= kNumVariants || nb <= 0) return;  // no tiles (align_sort wrote none)
     // never address rows beyond the buffers, whatever the device state says
@@ -1039,16 +1060,8 @@ template <int PHASE, int WKIND, bool SH>
 hipError_t launch_phase_sh(const FfnArgs& g, int grid, hipStream_t s) {
   constexpr int lds = lds_bytes<PHASE, WKIND>();
   static_assert((lds + 4096) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
-  static int done[64] = {0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = opt_in_lds((const void*)ffn_kernel<PHASE, WKIND, SH>, lds);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && !done[dev]) {
-    e = hipFuncSetAttribute((const void*)ffn_kernel<PHASE, WKIND, SH>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    done[dev] = 1;
-  }
   ffn_kernel<PHASE, WKIND, SH><<<grid, kThreads, lds, s>>>(g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1082,10 +1095,10 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,
                               const int32_t* variant, void* y_slots, void* h, float* part,
-                              int num_cus, int64_t rows_max, hipStream_t s) {
+                              int32_t* status, int num_cus, int64_t rows_max, hipStream_t s) {
   FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
             h, y_slots, part, p.hidden, p.inter, p.top_k, p.local_experts,
-            p.tokens * p.top_k, rows_max, nullptr, p.shared_experts};
+            p.tokens * p.top_k, rows_max, nullptr, p.shared_experts, status};
   const int grid = num_cus * kWgPerCu < kMaxGrid ? num_cus * kWgPerCu : kMaxGrid;
   switch (p.weight_dtype) {
     case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);

@@ -3,17 +3,59 @@
 // memory from the host, so every call can be captured into a HIP graph.
 #include <string.h>
 
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "moe_common.h"
 
 namespace moe {
 size_t align_lds_bytes(int B, int E_loc);
+
+hipError_t opt_in_lds(const void* fn, int bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> granted;  // (kernel, device) -> bytes
+  std::lock_guard<std::mutex> lock(mu);
+  int& have = granted[{fn, dev}];
+  if (have >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
 }
+
+hipError_t device_cus(int* cus) {
+  static std::atomic<int> cache[64];  // zero-initialised: 0 = not yet queried
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return hipSuccess;
+}
+}  // namespace moe
 
 using namespace moe;
 
 namespace {
 
-// workspace: a 256-byte header (reserved), h, then the partial tiles
+// workspace: a 256-byte header (the device status word at offset 0, then
+// reserved bytes), h, then the partial tiles
 constexpr int64_t kWsHeader = 256;
 constexpr size_t kMaxLds = 160 * 1024;
 
@@ -111,16 +153,9 @@ int64_t h_bytes(const moe_problem* p, int64_t rows_max) {
 
 
 int num_cus_current(hipError_t* err) {
-  static int cache[64] = {0};
-  int dev = 0;
-  *err = hipGetDevice(&dev);
-  if (*err != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
   int n = 0;
-  *err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-  if (*err != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  return n;
+  *err = device_cus(&n);
+  return *err == hipSuccess ? n : 0;
 }
 
 moe_status fill_cost_table(const moe_problem* p, CostTable* t) {
@@ -131,8 +166,10 @@ moe_status fill_cost_table(const moe_problem* p, CostTable* t) {
     t->b[v] = kVariants[v].bm;
     t->q1[v] = p->inter / kVariants[v].bn1;
     t->q2[v] = (p->hidden / kVariants[v].bn2) * kVariants[v].splitk;
-    t->S1[v] = cus * kWgPerCu;
-    t->S2[v] = cus * kWgPerCu;
+    // tiles resident at once: the persistent grid of the grouped FFN
+    const int grid = cus * kWgPerCu < kMaxGrid ? cus * kWgPerCu : kMaxGrid;
+    t->S1[v] = grid;
+    t->S2[v] = grid;
     t->rt_shared[v] = p->shared_experts * ((p->tokens + kVariants[v].bm - 1) / kVariants[v].bm);
   }
   t->a_shared = p->shared_experts;
@@ -267,6 +304,7 @@ moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, c
   hipError_t err;
   const int cus = num_cus_current(&err);
   if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
+  int32_t* status = (int32_t*)((char*)workspace + MOE_DEVICE_STATUS_OFFSET);
   void* h = (char*)workspace + kWsHeader;
   float* part = (float*)((char*)workspace + (sz.workspace_bytes - kPartBytes));
   uint8_t* xq = nullptr;
@@ -288,8 +326,8 @@ moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, c
   if (up && down) {  // two calls, so that h is quantized between the phases
     const moe_status st1 = hip_status(launch_grouped_ffn(
         *p, 1, x, xq, xs, nullptr, nullptr, w1, w3, w2, fp8 ? s1 : nullptr, fp8 ? s3 : nullptr,
-        fp8 ? s2 : nullptr, sorted_slots, block_expert, num_blocks, variant, y_slots, h, part, cus,
-        sz.rows_max, (hipStream_t)stream));
+        fp8 ? s2 : nullptr, sorted_slots, block_expert, num_blocks, variant, y_slots, h, part,
+        status, cus, sz.rows_max, (hipStream_t)stream));
     if (st1 != MOE_OK) return st1;
   }
   if (down && p->act_quant == 2) {
@@ -300,8 +338,8 @@ moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, c
   if (up && down) phases = 2;
   return hip_status(launch_grouped_ffn(*p, phases, x, xq, xs, hq, hs, w1, w3, w2, fp8 ? s1 : nullptr,
                                        fp8 ? s3 : nullptr, fp8 ? s2 : nullptr, sorted_slots,
-                                       block_expert, num_blocks, variant, y_slots, h, part, cus,
-                                       sz.rows_max, (hipStream_t)stream));
+                                       block_expert, num_blocks, variant, y_slots, h, part, status,
+                                       cus, sz.rows_max, (hipStream_t)stream));
 }
 
 }  // namespace

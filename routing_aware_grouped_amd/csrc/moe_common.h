@@ -69,11 +69,11 @@ constexpr int kMaxBlockM = 128;
 // workgroups per CU of the persistent grouped-FFN launch
 constexpr int kWgPerCu = 2;
 
-// The persistent grouped-FFN grid is min(CUs * kWgPerCu, kMaxGrid) workgroups.
-// Each may leave up to two partial tiles of at most kPieceMax fp32 sums in the
-// workspace (the split tail tiles), so the workspace size does not depend on the
-// device.
-constexpr int kMaxGrid = 1024;
+// The persistent grouped-FFN grid is min(CUs * kWgPerCu, kMaxGrid) workgroups
+// (MI355X: 256 CUs, so 512).  Each may leave up to two partial tiles of at most
+// kPieceMax fp32 sums in the workspace (the split tail tiles), so the workspace
+// size does not depend on the device.
+constexpr int kMaxGrid = 512;
 constexpr int piece_floats(const VariantDesc& d) {
   return 2 * d.bm * d.bn1 > d.bm * d.bn2 ? 2 * d.bm * d.bn1 : d.bm * d.bn2;
 }
@@ -100,6 +100,13 @@ struct CostTable {
 
 constexpr int kMaxShared = 8;
 
+// Raises the dynamic-LDS limit of kernel `fn` on the current device to at least
+// `bytes`: one hipFuncSetAttribute per kernel and device, safe to call from
+// several host threads at once.
+hipError_t opt_in_lds(const void* fn, int bytes);
+// Compute units of the current device, queried once per device (thread-safe).
+hipError_t device_cus(int* cus);
+
 // Host-side launchers (one per translation unit).
 hipError_t launch_route_topk(const moe_problem& p, const float* logits, int32_t* ids, float* w,
                              int32_t* counts, hipStream_t s);
@@ -125,13 +132,15 @@ hipError_t launch_quant_h(const moe_problem& p, const void* h, uint8_t* hq, floa
 // phases: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both (two launches).
 // With p.act_quant the gate/up phase reads the quantized x (xq, xs) instead of x,
 // and with act_quant 2 the down phase reads the quantized h (hq, hs).
+// status: the device status word (MOE_DEV_* bits), written by workgroup 0 of
+// every grouped-FFN launch.
 hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const uint8_t* xq,
                               const float* xs, const uint8_t* hq, const float* hs, const void* w1,
                               const void* w3, const void* w2, const float* s1, const float* s3,
                               const float* s2, const int32_t* sorted_slots,
                               const int32_t* block_expert, const int32_t* num_blocks,
                               const int32_t* variant, void* y_slots, void* h, float* part,
-                              int num_cus, int64_t rows_max, hipStream_t s);
+                              int32_t* status, int num_cus, int64_t rows_max, hipStream_t s);
 // num_blocks / variant: device values of the sort, needed with shared experts only
 hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
                           const float* w, const int32_t* num_blocks, const int32_t* variant,

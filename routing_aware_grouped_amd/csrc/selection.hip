@@ -609,10 +609,11 @@ select_align_kernel(const int32_t* __restrict__ counts, const float* __restrict_
                 block_expert, num_blocks, slot_pos, lds_u64);
 }
 
-// more than 64 KiB of dynamic LDS needs an opt-in (gfx950 has 160 KiB per CU)
+// more than 64 KiB of dynamic LDS needs an opt-in (gfx950 has 160 KiB per CU); the
+// whole 160 KiB is granted once per kernel and device
 hipError_t allow_lds(const void* fn, size_t bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  return opt_in_lds(fn, 160 * 1024);
 }
 
 template <int L, int MMAX>

@@ -17,17 +17,18 @@ WG_PER_CU = (2, 2)
 
 def cost_constants(hidden: int, inter: int, num_cus: int) -> dict:
     """b, q1, q2, S1, S2 per configuration, per the definitions in include/moe.h."""
+    grid = min(num_cus * WG_PER_CU[0], MAX_GRID)
     return {
         "b": [m[0] for m in MENU],
         "q1": [inter // m[1] for m in MENU],
         "q2": [(hidden // m[2]) * m[7] for m in MENU],
-        "S1": [num_cus * WG_PER_CU[0]] * len(MENU),
-        "S2": [num_cus * WG_PER_CU[1]] * len(MENU),
+        "S1": [grid] * len(MENU),
+        "S2": [grid] * len(MENU),
     }
 
 
 # The persistent grouped-FFN grid: min(CUs * workgroups per CU, MAX_GRID).
-MAX_GRID = 1024
+MAX_GRID = 512
 
 
 def splits_tail(r: int, grid: int, stream: int, full_rounds: int = 0) -> bool:

@@ -236,9 +236,18 @@ def test_empty_rank_gives_zero_output():
     assert np.all(out["Y"] == 0.0)
 
 
+def _status(b) -> int:
+    """The device status word at the start of the grouped-FFN workspace."""
+    from routing_aware_grouped_amd import MOE_DEVICE_STATUS_OFFSET
+    o = MOE_DEVICE_STATUS_OFFSET
+    return int(b.workspace[o:o + 4].view(torch.int32).item())
+
+
 def test_out_of_range_variant_gives_no_tiles():
+    from routing_aware_grouped_amd import MOE_DEV_BAD_VARIANT, MOE_DEV_OK
     layer = synth.make_layer("tiny", 64, None, 3)
     b = G.run(layer, variant=0)
+    assert _status(b) == MOE_DEV_OK
     b.variant.fill_(V + 3)
     b.y.fill_(1.0)
     L.align(b)
@@ -248,6 +257,36 @@ def test_out_of_range_variant_gives_no_tiles():
     assert int(b.num_blocks.item()) == 0
     assert torch.all(b.slot_pos == -1)
     assert torch.all(b.y == 0)
+    assert _status(b) == MOE_DEV_BAD_VARIANT
+    # a valid configuration again: the next call reports its own inputs
+    b.variant.fill_(1)
+    L.align(b)
+    L.ffn(b)
+    torch.cuda.synchronize()
+    assert _status(b) == MOE_DEV_OK
+
+
+def test_block_count_beyond_buffers_is_reported():
+    """A row-block count below zero or beyond what rows_max holds (a value the
+    alignment step never writes) sets MOE_DEV_BAD_BLOCKS; the kernels compute only
+    the row-blocks that fit (here rows past the real ones hold no slot)."""
+    from routing_aware_grouped_amd import MOE_DEV_BAD_BLOCKS
+    layer = synth.make_layer("tiny", 64, None, 3)
+    b = G.run(layer, variant=2)
+    nb = int(b.num_blocks.item())
+    bm = spec.MENU[2][0]
+    ref = b.y_slots[:nb * bm].clone()
+    b.sorted_slots[nb * bm:].fill_(-1)
+    b.block_expert[nb:].fill_(0)
+    for bad in (b.sorted_slots.numel() // bm + 5, -3):
+        b.num_blocks.fill_(bad)
+        L.ffn(b)
+        torch.cuda.synchronize()
+        assert _status(b) == MOE_DEV_BAD_BLOCKS, bad
+    b.num_blocks.fill_(nb)
+    L.ffn(b)
+    torch.cuda.synchronize()
+    assert torch.equal(b.y_slots[:nb * bm], ref)
 
 
 def test_out_of_range_variant_on_an_alignment_grid():

@@ -82,8 +82,13 @@ def test_select_counts_shared_row_tiles():
         th = (rng.random((V, 4)) * np.array([20, 5, 0.05, 0.5])).astype(np.float32)
         b = G.run(layer, theta=torch.from_numpy(th))
         out = G.fetch(b)
-        cc = moe_cost_constants(b.p)
-        cnt = np.concatenate([out["counts"], np.full(layer.shape.shared, B, np.int32)])
+        # the oracle's own counts and the documented constants (never the library's)
+        cc = spec.cost_constants(layer.shape.hidden, layer.shape.inter, G.num_cus())
+        assert moe_cost_constants(b.p) == cc
+        ids, _ = oracle.route_topk(layer.logits, layer.shape.top_k)
+        cnt_ref = oracle.counts(ids, layer.expert_begin, layer.shape.local_experts)
+        np.testing.assert_array_equal(out["counts"], cnt_ref)
+        cnt = np.concatenate([cnt_ref, np.full(layer.shape.shared, B, np.int32)])
         ref_v, ref_t, _ = oracle.select(cnt, cc["b"], cc["q1"], cc["q2"], cc["S1"], cc["S2"], th)
         assert out["variant"] == ref_v
         np.testing.assert_array_equal(b.t_hat.cpu().numpy().view(np.uint32), ref_t.view(np.uint32))
