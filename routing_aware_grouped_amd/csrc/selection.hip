@@ -610,11 +610,8 @@ select_align_kernel(const int32_t* __restrict__ counts, const float* __restrict_
 }
 
 // more than 64 KiB of dynamic LDS needs an opt-in (gfx950 has 160 KiB per CU); the
-// whole 160 KiB is granted once per kernel and device
-hipError_t allow_lds(const void* fn, size_t bytes) {
-  if (bytes <= 64 * 1024) return hipSuccess;
-  return opt_in_lds(fn, 160 * 1024);
-}
+// attribute is raised only when a launch needs more than any earlier one did
+hipError_t allow_lds(const void* fn, size_t bytes) { return opt_in_lds(fn, (int)bytes); }
 
 template <int L, int MMAX>
 hipError_t launch_rsa(const moe_problem& p, const float* logits, const float* theta,
