@@ -269,6 +269,32 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, 
                            const int32_t* num_blocks, const int32_t* variant, void* y_slots,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Step 4 for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * moe_grouped_ffn, with the same arguments apart from the workspace, which here is
+ * an array the library owns on each GPU (moe_noalloc_workspace_limit() bytes,
+ * 256 MiB, reserved when the library is loaded on that GPU and held until the
+ * process ends).  The call allocates and frees nothing.  Its outputs are the
+ * bits moe_grouped_ffn writes for the same inputs.
+ *   - Problems whose moe_query_sizes().workspace_bytes exceed the limit get
+ *     MOE_ERR_WORKSPACE, with nothing enqueued.
+ *   - Every call on one GPU uses that GPU's one array and overwrites what the
+ *     previous call left there; nothing in it needs to start at zero.  Calls
+ *     that overlap in time on one GPU (on different streams, or from several
+ *     host threads) race on it: serialize them.
+ *   - The device status word of such a call is at MOE_DEVICE_STATUS_OFFSET of
+ *     the library's array and is not readable through this ABI.
+ * Errors: as moe_grouped_ffn; MOE_ERR_HIP if the array's device address cannot
+ * be obtained on the current device. */
+moe_status moe_grouped_ffn_noalloc(const moe_problem* p, const void* x, const void* w1,
+                                   const void* w3, const void* w2, const float* s1,
+                                   const float* s3, const float* s2, const int32_t* sorted_slots,
+                                   const int32_t* block_expert, const int32_t* num_blocks,
+                                   const int32_t* variant, void* y_slots, void* stream);
+
+/* Size in bytes of the per-GPU array moe_grouped_ffn_noalloc works in. */
+int64_t moe_noalloc_workspace_limit(void);
+
 /* Step 4a alone: the grouped gate/up GEMM with the fused SwiGLU, writing h into
  * workspace (as moe_grouped_ffn's first launch; with act_quant = 1 it is preceded
  * by moe_quant_act of x into the workspace).  Arguments and errors as for

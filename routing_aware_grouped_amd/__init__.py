@@ -75,6 +75,9 @@ _SIGS = {
     "moe_combine": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
     "moe_quant_act": ([ctypes.POINTER(moe_problem), P, P, P, P], ctypes.c_int),
     "moe_combine_shared": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P], ctypes.c_int),
+    "moe_grouped_ffn_noalloc": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P, P, P,
+                                 P], ctypes.c_int),
+    "moe_noalloc_workspace_limit": ([], ctypes.c_int64),
 }
 
 
@@ -186,6 +189,18 @@ def moe_grouped_ffn(p, x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, nu
         _pp(p), _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2),
         _ptr(sorted_slots), _ptr(block_expert), _ptr(num_blocks), _ptr(variant), _ptr(y_slots),
         _ptr(workspace), _ws_bytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def moe_grouped_ffn_noalloc(p, x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks,
+                            variant, y_slots, stream=None):
+    _check("moe_grouped_ffn_noalloc", lib().moe_grouped_ffn_noalloc(
+        _pp(p), _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2),
+        _ptr(sorted_slots), _ptr(block_expert), _ptr(num_blocks), _ptr(variant), _ptr(y_slots),
+        _stream(stream)))
+
+
+def moe_noalloc_workspace_limit() -> int:
+    return int(lib().moe_noalloc_workspace_limit())
 
 
 def moe_grouped_gate_up(p, x, w1, w3, s1, s3, sorted_slots, block_expert, num_blocks, variant,

@@ -182,7 +182,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
@@ -342,9 +342,61 @@ moe_status grouped_ffn_phases(int phases, const moe_problem* p, const void* x, c
                                        cus, sz.rows_max, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------------------
+// The library-owned workspace of moe_grouped_ffn_noalloc: one array per GPU,
+// reserved when the library's code object is loaded on that GPU and held until the
+// process ends.  In host code `scratch` is only a stand-in for the array: its
+// device address comes from hipGetSymbolAddress, once per device, with that device
+// current, and only that address is ever passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = 256ll << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    ptr = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (ptr == nullptr || ((uintptr_t)ptr & 255) != 0) return hipErrorInvalidSymbol;
+      scratch_addr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_grouped_ffn_noalloc(const moe_problem* p, const void* x, const void* w1,
+                                   const void* w3, const void* w2, const float* s1,
+                                   const float* s3, const float* s2, const int32_t* sorted_slots,
+                                   const int32_t* block_expert, const int32_t* num_blocks,
+                                   const int32_t* variant, void* y_slots, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  moe_sizes sz;
+  sizes_of(p, &sz);
+  if (sz.workspace_bytes > kScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return grouped_ffn_phases(3, p, x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert,
+                            num_blocks, variant, y_slots, ws, (size_t)kScratchBytes, stream);
+}
+
+int64_t moe_noalloc_workspace_limit(void) { return kScratchBytes; }
 
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
                            const void* w2, const float* s1, const float* s3, const float* s2,

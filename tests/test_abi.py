@@ -14,7 +14,7 @@ HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 def _declared():
     src = open(HDR).read()
-    return sorted(set(re.findall(r"^\s*(?:moe_status|int32_t|size_t)\s+(moe_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:moe_status|int32_t|int64_t|size_t)\s+(moe_\w+)\s*\(", src, re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -34,7 +34,7 @@ def test_binding_mirrors_names():
 
 
 def test_variant_menu_matches_spec():
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
     assert moe.moe_num_variants() == len(spec.MENU)
     for v, m in enumerate(spec.MENU):
         assert tuple(moe.moe_variant_info(v)) == m
@@ -202,3 +202,17 @@ def test_compute_calls_validate_before_any_gpu_work():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_query_sizes(None)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_problems_beyond_its_array():
+    """moe_grouped_ffn_noalloc checks the problem's workspace against its fixed
+    per-GPU array on the host, before any HIP call (so this runs without a GPU)."""
+    limit = moe.moe_noalloc_workspace_limit()
+    assert limit == 256 << 20
+    p = _p(tokens=4096, hidden=7168, inter=2048, num_experts=384, top_k=8, local_experts=48,
+           expert_begin=0, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3, act_quant=2)
+    assert moe.moe_query_sizes(p).workspace_bytes > limit
+    d = 1 << 16  # placeholder device address, never dereferenced on the host
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_grouped_ffn_noalloc(p, d, d, d, d, d, d, d, d, d, d, d, d, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
