@@ -221,16 +221,20 @@ def device_weights(wdev):
 
 
 def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, V, reps, warmup,
-              exhaustive=True, rep=0):
+              exhaustive=True, rep=0, force=None):
     layer = synth.make_layer(shape, tokens, alpha, rep, weights=whost)
     b = L.from_layer(layer, theta=theta, weights=device_weights(wdev))
     L.forward(b)
     torch.cuda.synchronize()
     ids = b.topk_ids.cpu().numpy()
-    chosen = int(b.variant.item())
     t_hat = b.t_hat.cpu().numpy().tolist()
+    if force is not None:  # a given configuration instead of the device's choice
+        b.variant.fill_(force)
+        L.forward(b, forced_variant=True)
+        torch.cuda.synchronize()
+    chosen = int(b.variant.item())
     w = work(layer, ids)
-    g_chosen = T.graph(lambda: L.forward(b))
+    g_chosen = T.graph(lambda: L.forward(b, forced_variant=force is not None))
     t_chosen = stats(T.time_graph(g_chosen, reps, warmup))
     res = dict(tokens=tokens, alpha=alpha, expert_begin=layer.expert_begin, S=w["S"], A=w["A"],
                eff_exp=round(w["eff_exp"], 3),
@@ -260,12 +264,13 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
     return res, layer, b, w
 
 
-def kernel_segments(torch, L, b, T, reps):
+def kernel_segments(torch, L, b, T, reps, forced=False):
     """Per-call HIP-event timing, eager, each step cold.  Every call is launched on
     one dedicated stream and its events are recorded on that same stream, so each
     pair brackets exactly that call's kernels."""
     names = ["route_select_align", "grouped_gate_up", "grouped_down", "combine"]
-    fns = [L.route_select_align, L.gate_up, L.down, L.combine]
+    fns = [lambda b_, stream: L.route_select_align(b_, stream, forced_variant=forced), L.gate_up,
+           L.down, L.combine]
     acc = {n: [] for n in names}
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -454,6 +459,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256)
     ap.add_argument("--exhaustive", type=int, default=1,
                     help="1: also time every configuration at the headline point")
+    ap.add_argument("--force-variant", type=int, default=None,
+                    help="run the headline in this configuration instead of the device's choice "
+                         "(for profiling one configuration)")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "bench_full.json"),
                     help="file for the full result (every sweep point); '' for none")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -503,15 +511,15 @@ def main():
     log(f"[bench] headline {args.shape} B={args.tokens} alpha={args.alpha}")
     head, layer, b, w = run_point(torch, np, synth, L, T, args.shape, args.tokens, args.alpha, wdev,
                                   whost, theta, V, max(10, args.steps // 2), 3,
-                                  exhaustive=bool(args.exhaustive))
-    g = T.graph(lambda: L.forward(b))
+                                  exhaustive=bool(args.exhaustive), force=args.force_variant)
+    g = T.graph(lambda: L.forward(b, forced_variant=args.force_variant is not None))
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     steps_us = T.time_graph(g, args.steps, args.warmup)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     st = stats(steps_us)
-    seg = kernel_segments(torch, L, b, T, max(10, args.steps))
+    seg = kernel_segments(torch, L, b, T, max(10, args.steps), forced=args.force_variant is not None)
     log(f"[bench] headline median {st['median']:.1f} us; segments " +
         ", ".join(f"{k} {v:.1f}" for k, v in seg.items()))
 

@@ -168,21 +168,26 @@ int32_t moe_num_variants(void);
  *   [1] BLOCK_N of the gate/up phase (output columns of W1 and of W3 per tile)
  *   [2] BLOCK_N of the down phase
  *   [3] BLOCK_K  reduction depth per pipeline stage for bf16 operands (the fp32
- *                problem uses half of it; fp8 weights are staged as bf16)
+ *                problem uses half of it; fp8 weights are staged as bf16; in the
+ *                wide class the fp32 and fp8 tiles stage twice the bytes)
  *   [4] waves along M, [5] waves along N, [6] waves splitting K inside a tile
  *   [7] split-K of the down phase across tiles (1 = none)
  *   [8] 1 if weights are read with non-temporal (streaming) loads, 0 if cached
+ *   [9] workgroups per compute unit of its persistent launch (its occupancy
+ *       class: 2 for the 256-thread streaming class, 1 for the 512-thread wide
+ *       class)
+ *   [10] threads per workgroup
  * Errors: MOE_ERR_INVALID_ARG for v outside [0, V) or out == NULL. */
-#define MOE_VARIANT_FIELDS 9
+#define MOE_VARIANT_FIELDS 11
 moe_status moe_variant_info(int32_t v, int32_t* out);
 
 /* The cost-model constants moe_select_config uses for problem *p on the current
  * HIP device, per configuration v (arrays of V int32, host memory):
- *   b[v]  = BLOCK_M;  q1[v] = I / BLOCK_N1 and q2[v] = (H / BLOCK_N2) * split_k,
+ *   b[v]  = BLOCK_M;  q1[v] = ceil(I / BLOCK_N1), q2[v] = ceil(H / BLOCK_N2) * split_k,
  *   the tiles of one row-block in each phase (q_c of RaMP Eq. 1, summed over the
  *   two phases); S1[v], S2[v] = tiles resident on the GPU at once in each phase
- *   = the persistent grid, min(compute units * 2, 512) workgroups (S_c of RaMP
- *   Eq. 1).
+ *   = the persistent grid of v's class, min(compute units * workgroups per CU,
+ *   512) workgroups (S_c of RaMP Eq. 1).
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP. */
 moe_status moe_cost_constants(const moe_problem* p, int32_t* b, int32_t* q1, int32_t* q2,
                               int32_t* S1, int32_t* S2);

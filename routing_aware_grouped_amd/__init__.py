@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-MOE_VARIANT_FIELDS = 9
+MOE_VARIANT_FIELDS = 11
 # the device status word in the grouped-FFN workspace (include/moe.h)
 MOE_DEVICE_STATUS_OFFSET = 0
 MOE_DEV_OK, MOE_DEV_BAD_VARIANT, MOE_DEV_BAD_BLOCKS = 0, 1, 2

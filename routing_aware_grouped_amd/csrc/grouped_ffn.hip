@@ -46,6 +46,8 @@
 // section 3.3 and appendix A.8).  Waves
 // are arranged WM x WN x WK over the tile; waves that split K inside a tile add
 // their partial sums through LDS in a fixed order, so results are deterministic.
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -138,16 +140,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // LDS row swizzle in 16-byte units for rows of C chunks: chunk c of row r sits at
-// c ^ (r & 7) for 128-byte rows and c ^ (r & 15) for longer ones.  A quarter
-// wave's MFMA fragment read (16 consecutive rows, one logical chunk) then hits
-// every one of the 64 banks once: 128-byte rows alternate between the two bank
-// halves and take 8 distinct chunks each, longer rows all start on bank 0 and
-// take 16 distinct chunks.  A stage write covers each row's chunks once.
+// c ^ ((r >> 2) & 3) for 64-byte rows, c ^ (r & 7) for 128-byte rows and
+// c ^ (r & 15) for longer ones.  A quarter wave's MFMA fragment read (16
+// consecutive rows, one logical chunk) then hits every one of the 64 banks once:
+// 64-byte rows cover the banks four rows at a time and the four such groups take
+// four distinct chunks, 128-byte rows alternate between the two bank halves and
+// take 8 distinct chunks each, longer rows all start on bank 0 and take 16
+// distinct chunks.  A stage write covers each row's chunks once.
 // Measured with rocprofv3 on gfx950 for 128-byte rows: a fragment read costs 4
 // LDS cycles and no bank-conflict cycles, against 8 cycles (half of them
 // conflicts) for the swizzle c ^ ((r & 7) ^ ((r >> 3) & 1)) and 16 without one.
 template <int C>
-__device__ __forceinline__ int swz(int row) { return row & (C >= 16 ? 15 : 7); }
+__device__ __forceinline__ int swz(int row) {
+  return C == 4 ? (row >> 2) & 3 : row & (C >= 16 ? 15 : 7);
+}
 
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
@@ -211,6 +217,7 @@ struct FfnArgs {
   const float* xs;  // [B][H/128] activation scales of the FP8 activation path
   int n_shared;     // shared experts (row-blocks after the routed ones)
   int32_t* status;  // device status word (MOE_DEV_* bits)
+  int grid_stream;  // workgroups of the streaming class's launch (its fix-up needs it)
 };
 
 // ring slots of per-tile metadata (see Tile::run_all)
@@ -227,9 +234,11 @@ __device__ __forceinline__ int xcd_slot(int wg, int grid) {
 // one tile configuration of one phase
 //   BM x BN tile (BN weight rows per matrix; the gate/up phase has two matrices),
 //   ROWB = LDS bytes per tile row per stage, waves WM x WN x WK, RS register
-//   stages in flight.
+//   stages in flight, NT threads per workgroup (256: streaming class, two
+//   workgroups per CU; 512: wide class, one per CU).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int WK, int ROWB, int RS, int STREAM, int PHASE, int WKIND>
+template <int BM, int BN, int WM, int WN, int WK, int ROWB, int RS, int STREAM, int PHASE, int WKIND,
+          int NT>
 struct Tile {
   using T = Types<WKIND>;
   using Act = typename T::Act;
@@ -247,7 +256,9 @@ struct Tile {
   // FP8 activation path: 128-deep scale blocks per stage, and the stage's scales
   // in LDS after its rows: x scales [KB][BM], weight scales [NMAT][KB], 1 spare
   static constexpr int KB = FP8A ? ROWB / 128 : 0;
-  static constexpr int SC_FLOATS = FP8A ? BM * KB + NMAT * KB + 1 : 0;
+  // weight-scale blocks (128 output rows each) per matrix that a tile spans
+  static constexpr int NSB = BN > 128 ? BN / 128 : 1;
+  static constexpr int SC_FLOATS = FP8A ? BM * KB + NMAT * NSB * KB + 1 : 0;
   static constexpr int SC_BYTES = (SC_FLOATS * 4 + 15) / 16 * 16;
   static constexpr int STAGE = ROWS * ROWB + SC_BYTES;  // LDS bytes per stage
   static constexpr int EPC_A = 16 / ASZ;     // elements per global A chunk
@@ -256,8 +267,8 @@ struct Tile {
   static constexpr int GCB = BK / EPC_B;     // global chunks per weight row per stage
   static constexpr int GA = BM * GCA;
   static constexpr int GB = NMAT * BN * GCB;
-  static constexpr int NA = (GA + kThreads - 1) / kThreads;
-  static constexpr int NB = (GB + kThreads - 1) / kThreads;
+  static constexpr int NA = (GA + NT - 1) / NT;
+  static constexpr int NB = (GB + NT - 1) / NT;
   static constexpr int MW = BM / WM, NW = BN / WN;
   static constexpr int FM = MW / 16, FN = NW / 16;
   static constexpr int KSTEPS = BK / (FP8A ? 128 : 32);  // MFMA steps per stage
@@ -266,16 +277,22 @@ struct Tile {
   static constexpr int PIECE = NMAT * BM * BN;   // floats of one partial tile
   static constexpr int LDS_BYTES = 2 * STAGE;
   static_assert(RED_FLOATS * 4 <= STAGE, "the K-split sums reuse one stage buffer");
-  static_assert(WM * WN * WK * 64 == kThreads, "waves must cover the workgroup");
+  static_assert(WM * WN * WK * 64 == NT, "waves must cover the workgroup");
   static_assert(FM >= 1 && FN >= 1 && MW % 16 == 0 && NW % 16 == 0, "wave tile too small");
-  static_assert(C >= 8 && (C & (C - 1)) == 0, "LDS rows must be a power of two of >= 128 bytes");
+  static_assert(C >= 4 && (C & (C - 1)) == 0, "LDS rows must be a power of two of >= 64 bytes");
+  static_assert(C >= 8 || !(F32 || FP8A), "fp32 and fp8 x fp8 fragments take 128-byte rows");
   static_assert(KSTEPS % WK == 0, "K-split waves must divide the stage");
   static_assert(!FP8 || GCB * 2 == C, "fp8 chunk pairs");
-  static_assert(GA % kThreads == 0 && GB % kThreads == 0, "every thread owns whole chunks");
-  static_assert((BN * GCB) % kThreads == 0, "each weight load instruction reads one matrix");
-  static_assert(!FP8A || (BM * KB <= kThreads && NMAT * KB <= kThreads && BN <= 128 && 128 % BN == 0),
-                "one scale load per thread; a tile's columns share one 128-row weight block");
-  static_assert(WM * WN * NFRAG * 256 == PIECE && PIECE <= kPieceMax, "partial tile layout");
+  static_assert(GA % NT == 0 && GB % NT == 0, "every thread owns whole chunks");
+  static_assert((BN * GCB) % NT == 0, "each weight load instruction reads one matrix");
+  static_assert(!FP8A || (BM * KB <= NT && NMAT * NSB * KB <= NT && (BN <= 128 ? 128 % BN == 0
+                                                                             : BN % 128 == 0) &&
+                          (BN / WN) <= 128 && 128 % (BN / WN) == 0),
+                "one scale load per thread; a wave's columns share one 128-row weight block");
+  // the wide class never splits a tile, so its pieces need no workspace
+  static constexpr bool SPLITS = NT == kThreads;
+  static_assert(WM * WN * NFRAG * 256 == PIECE && (!SPLITS || PIECE <= kPieceMax),
+                "partial tile layout");
 
   struct Regs {
     u32x4 a[NA];
@@ -307,6 +324,8 @@ struct Tile {
         Out* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn) {
+          // a tile of the wide class may reach past N (ragged last column tile)
+          if (BN > 128 && n0 + wn * NW + jn * 16 + lr >= N) continue;
           const float v = PHASE == 1 ? silu_mul(acc[0][i][jn][c], acc[NMAT - 1][i][jn][c])
                                      : acc[0][i][jn][c];
           store_out<Out>(orow + jn * 16, v);
@@ -321,8 +340,8 @@ struct Tile {
   // tiles, so that XCD's L2 serves each token row and each weight slice to many
   // workgroups.
   static constexpr int kChunk = 16;
-  __device__ __forceinline__ static void tile_rc(int t, int nb, int NT, int& rb, int& nt) {
-    const int full = NT / kChunk;
+  __device__ __forceinline__ static void tile_rc(int t, int nb, int ncol, int& rb, int& nt) {
+    const int full = ncol / kChunk;
     const int cs = nb * kChunk;
     const int c = t / cs;
     if (c < full) {
@@ -330,7 +349,7 @@ struct Tile {
       rb = l / kChunk;
       nt = c * kChunk + l % kChunk;
     } else {  // the last, narrower chunk (t past the last tile: any finite result)
-      const int w = NT > full * kChunk ? NT - full * kChunk : kChunk;
+      const int w = ncol > full * kChunk ? ncol - full * kChunk : kChunk;
       const int l = t - full * cs;
       rb = l / w;
       nt = full * kChunk + l % w;
@@ -344,8 +363,9 @@ struct Tile {
   // The cached configuration splits when the idle share of an unsplit phase,
   // (G - r) / (G (F + 1)) of its time, would exceed one tenth: after several full
   // rounds a nearly full last round costs less than summing its split tiles.
+  // The wide class never splits (its tiles are dealt as whole rounds).
   __device__ __forceinline__ static bool split_tail(int r, int G, int F) {
-    return r > 0 && (STREAM ? 4 * r < 3 * G : 10 * (G - r) > G * (F + 1));
+    return SPLITS && r > 0 && (STREAM ? 4 * r < 3 * G : 10 * (G - r) > G * (F + 1));
   }
 
   // Runs the work of workgroup slot `slot` of `G` (hybrid Stream-K).  The phase's
@@ -366,15 +386,15 @@ struct Tile {
   // shared expert i, ceil(B / BM) row-blocks of tokens 0..B-1 in order, with
   // local expert index E_loc + i.  Their slot ids are encoded as g.slots + token.
   template <bool SH>
-  __device__ __forceinline__ static void run_all(const FfnArgs& g, uint8_t* lds, int* meta3,
-                                                int nb, int nbr, int slot, int G) {
+  __device__ __forceinline__ static void run_all(const FfnArgs& g, uint8_t* lds0, uint8_t* lds1,
+                                                int* meta3, int nb, int nbr, int slot, int G) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
     const int Btok = g.slots / g.k;
     const int nbs = SH ? (Btok + BM - 1) / BM : 1;  // row-blocks per shared expert
     const int slot_end = SH ? g.slots + Btok : g.slots;
     const int e_end = SH ? g.E_loc + g.n_shared : g.E_loc;
-    const int total = nb * (N / BN);
+    const int total = nb * ((N + BN - 1) / BN);
     const int nst = (K + BK - 1) / BK;
     const int F = total / G;                        // full rounds
     const int r = total - F * G;                    // tail tiles
@@ -417,7 +437,7 @@ struct Tile {
     int ms0 = -1, ms1 = -1, me = -1;
     auto fetch_meta = [&](int j) __attribute__((always_inline)) {
       int rb, nt;
-      tile_rc(item_tile(j), nb, N / BN, rb, nt);
+      tile_rc(item_tile(j), nb, (N + BN - 1) / BN, rb, nt);
       const int64_t row0 = (int64_t)rb * BM;
       if (SH && rb >= nbr) {  // a shared expert's row-block: tokens in order
         const int t0 = ((rb - nbr) % nbs) * BM + tid;
@@ -466,9 +486,9 @@ struct Tile {
     uint32_t l_aoff[NA];
     // FP8 activation path: thread tid < BM * KB loads the A scale (x: per token;
     // h: per padded row) of tile row tid % BM, block tid / BM of each stage
-    // (l_xsoff: that row's scale row, or kOob); threads tid < NMAT * KB load the
-    // weight scale of matrix tid / KB, block tid % KB (l_wsbase: the tile's first
-    // scale of its 128-row block)
+    // (l_xsoff: that row's scale row, or kOob); threads tid < NMAT * NSB * KB load
+    // the weight scales (l_wsbase: the tile's first scale of its first 128-row
+    // block)
     const uint32_t a_rows = PHASE == 1 ? (uint32_t)(g.slots / g.k) : (uint32_t)g.rows_max;
     const __amdgpu_buffer_rsrc_t xs_rsrc =
         make_rsrc(g.xs, FP8A ? a_rows * (uint32_t)(K / 128) * 4u : 0u);
@@ -480,7 +500,7 @@ struct Tile {
     uint32_t b_off[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int q = i * kThreads + tid;
+      const int q = i * NT + tid;
       const int row = (q / GCB) % BN;
       b_off[i] = (uint32_t)(row * K + (q % GCB) * EPC_B) * WSZ;
     }
@@ -489,7 +509,7 @@ struct Tile {
     auto enter_load_tile = [&](int j) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
       int rb, nt;
-      tile_rc(item_tile(j), nb, N / BN, rb, nt);
+      tile_rc(item_tile(j), nb, (N + BN - 1) / BN, rb, nt);
       l_n0 = nt * BN;
       l_e = __builtin_amdgcn_readfirstlane(m[BM + 1]);
       l_eok = j < nitem && (unsigned)l_e < (unsigned)e_end;
@@ -503,7 +523,7 @@ struct Tile {
       if constexpr (NMAT == 2) l_b_rsrc[1] = make_rsrc(wmat1 + wrow0, wbytes);
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int q = i * kThreads + tid;
+        const int q = i * NT + tid;
         const int row = q / GCA, c = q % GCA;
         const int sl = m[row];
         l_aoff[i] = kOob;
@@ -529,14 +549,14 @@ struct Tile {
       const int kl = K - k0;  // reduction elements left from this stage on
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int kel = ((i * kThreads + tid) % GCA) * EPC_A;
+        const int kel = ((i * NT + tid) % GCA) * EPC_A;
         R.a[i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, kel < kl ? l_aoff[i] : kOob, k0 * ASZ, 0));
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int q = i * kThreads + tid;
-        const int mt = i * kThreads / (BN * GCB);  // one matrix per load instruction (tid < kThreads)
+        const int q = i * NT + tid;
+        const int mt = i * NT / (BN * GCB);  // one matrix per load instruction (tid < NT)
         const int kel = (q % GCB) * EPC_B;
         // non-temporal loads (cache policy nt) stream weights that no other tile reads
         R.b[i] = __builtin_bit_cast(
@@ -545,7 +565,7 @@ struct Tile {
         if constexpr (FP8) {
           const int row = (q / GCB) % BN;
           const float* sm = mt == 0 ? smat0 : smat1;
-          const bool ok = l_eok && kel < kl;
+          const bool ok = l_eok && kel < kl && l_n0 + row < N;  // rows past N have no scale
           R.s[i] = sm[ok ? ((int64_t)l_e * (N / 128) + (l_n0 + row) / 128) * (K / 128) + (k0 + kel) / 128 : 0];
         }
       }
@@ -556,9 +576,12 @@ struct Tile {
         const bool xin = kb0 + tid / BM < K / 128;
         R.xs = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, xin ? l_xsoff : kOob, kb0 * 4, 0));
-        const float* sm = tid / KB == 0 ? smat0 : smat1;
-        const bool wok = l_eok && tid < NMAT * KB && kb0 + tid % KB < K / 128;
-        R.ws = sm[wok ? l_wsbase + kb0 + tid % KB : 0];
+        // thread (mt * NSB + sb) * KB + kb: matrix mt, scale block sb of the tile's
+        // columns, reduction block kb of the stage
+        const float* sm = tid / (NSB * KB) == 0 ? smat0 : smat1;
+        const bool wok = l_eok && tid < NMAT * NSB * KB && kb0 + tid % KB < K / 128 &&
+                         l_n0 + ((tid / KB) % NSB) * 128 < N;  // no scale block past N
+        R.ws = sm[wok ? l_wsbase + (int64_t)((tid / KB) % NSB) * (K / 128) + kb0 + tid % KB : 0];
       }
       if (++l_s == l_se) {  // past the last item the cursor runs on harmlessly
         ++l_j;
@@ -570,13 +593,13 @@ struct Tile {
     auto write_stage = [&](const Regs& R, uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int q = i * kThreads + tid;
+        const int q = i * NT + tid;
         const int row = q / GCA, c = q % GCA;
         *(u32x4*)(buf + row * ROWB + ((c ^ swz<C>(row)) << 4)) = R.a[i];
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int q = i * kThreads + tid;
+        const int q = i * NT + tid;
         const int c = q % GCB;
         const int row = BM + q / GCB;  // LDS row: matrices follow each other
         const int sw = swz<C>(row);
@@ -593,7 +616,7 @@ struct Tile {
       if constexpr (FP8A) {  // the stage's scales; threads without one write the spare
         float* sc = (float*)(buf + ROWS * ROWB);
         sc[tid < BM * KB ? tid : SC_FLOATS - 1] = R.xs;
-        sc[tid < NMAT * KB ? BM * KB + tid : SC_FLOATS - 1] = R.ws;
+        sc[tid < NMAT * NSB * KB ? BM * KB + tid : SC_FLOATS - 1] = R.ws;
       }
     };
 
@@ -601,20 +624,24 @@ struct Tile {
     f32x4 acc[NMAT][FM][FN];
     const int lr = lane & 15;   // row of the fragment
     const int lg = lane >> 4;   // k-group of 8 inside a 32-step
-    auto read_frag = [&](const uint8_t* buf, int row, int step, FragT& f) __attribute__((always_inline)) {
-      const uint8_t* rp = buf + row * ROWB;
-      const int sw = swz<C>(row);
+    // A fragment of 16 rows starting at row16 (a multiple of 16): lane row lr.  The
+    // swizzle depends on row & 15 only, so a fragment's address is a per-lane
+    // offset (frag_off) plus row16 * ROWB, which the fragment loops turn into
+    // immediate offsets instead of one live address per fragment.
+    auto frag_off = [&](int step, int half) __attribute__((always_inline)) {
+      const int c0 = (FP8A || F32) ? step * 8 + 2 * lg + half : step * 4 + lg;
+      return lr * ROWB + ((c0 ^ swz<C>(lr)) << 4);
+    };
+    auto read_frag = [&](const uint8_t* buf, int row16, int step, FragT& f) __attribute__((always_inline)) {
+      const uint8_t* rp = buf + row16 * ROWB;
       if constexpr (FP8A) {  // 32 consecutive bytes of the step's 128-byte block
-        const int c0 = step * 8 + 2 * lg;
-        f.lo = *(const u32x4*)(rp + ((c0 ^ sw) << 4));
-        f.hi = *(const u32x4*)(rp + (((c0 + 1) ^ sw) << 4));
+        f.lo = *(const u32x4*)(rp + frag_off(step, 0));
+        f.hi = *(const u32x4*)(rp + frag_off(step, 1));
       } else if constexpr (F32) {
-        const int c0 = step * 8 + 2 * lg;
-        f.lo = *(const f32x4*)(rp + ((c0 ^ sw) << 4));
-        f.hi = *(const f32x4*)(rp + (((c0 + 1) ^ sw) << 4));
+        f.lo = *(const f32x4*)(rp + frag_off(step, 0));
+        f.hi = *(const f32x4*)(rp + frag_off(step, 1));
       } else {
-        const int c0 = step * 4 + lg;
-        f.v = __builtin_bit_cast(bf16x8, *(const u32x4*)(rp + ((c0 ^ sw) << 4)));
+        f.v = __builtin_bit_cast(bf16x8, *(const u32x4*)(rp + frag_off(step, 0)));
       }
     };
     // 16-row groups with no routed slot are skipped (their rows are never stored),
@@ -624,18 +651,42 @@ struct Tile {
     // takes the guarded path.  Reduction steps beyond K need no guard: they were
     // loaded as zeros and add nothing.
     auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
-     if constexpr (!FP8A) {
+     const uint8_t* bufA = buf + wm * MW * ROWB;         // this wave's A rows
+     const uint8_t* bufB = buf + (BM + wn * NW) * ROWB;  // its weight rows (matrix mt: + mt * BN rows)
+     if constexpr (!FP8A && NT == kThreadsWide) {
+      // wide class: the B fragments of a step stay in registers and the A
+      // fragments are read one at a time, which keeps the 128 accumulators, two
+      // register stages and the fragments within 256 registers
+#pragma unroll
+      for (int jj = 0; jj < KSTEPS / WK; ++jj) {
+        const int step = jj * WK + wk;
+        FragT fb[NMAT][FN];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) read_frag(bufB, mt * BN + j * 16, step, fb[mt][j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          FragT fa;
+          read_frag(bufA, i * 16, step, fa);
+#pragma unroll
+          for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa, fb[mt][j]);
+        }
+      }
+     } else if constexpr (!FP8A) {
 #pragma unroll
       for (int jj = 0; jj < KSTEPS / WK; ++jj) {
         const int step = jj * WK + wk;
         FragT fa[FM];
         FragT fb[NMAT][FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
+        for (int i = 0; i < FM; ++i) read_frag(bufA, i * 16, step, fa[i]);
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
+          for (int j = 0; j < FN; ++j) read_frag(bufB, mt * BN + j * 16, step, fb[mt][j]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -648,6 +699,8 @@ struct Tile {
     // FP8 activation path: each step is one 128-deep block; its sums are scaled by
     // the row's x scale times the tile's weight scale and added in fp32
     auto compute_f8 = [&](const uint8_t* buf, int nvalid) __attribute__((always_inline)) {
+     const uint8_t* bufA = buf + wm * MW * ROWB;         // this wave's A rows
+     const uint8_t* bufB = buf + (BM + wn * NW) * ROWB;  // its weight rows (matrix mt: + mt * BN rows)
      if constexpr (FP8A) {
       if (wm * MW >= nvalid) return;
       const bool full = wm * MW + MW <= nvalid;
@@ -659,15 +712,15 @@ struct Tile {
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
+          for (int j = 0; j < FN; ++j) read_frag(bufB, mt * BN + j * 16, step, fb[mt][j]);
         float wsv[NMAT];
 #pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) wsv[mt] = sc[BM * KB + mt * KB + step];
+        for (int mt = 0; mt < NMAT; ++mt) wsv[mt] = sc[BM * KB + (mt * NSB + (wn * NW) / 128) * KB + step];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           if (!full && wm * MW + i * 16 >= nvalid) continue;
           FragT fa;
-          read_frag(buf, wm * MW + i * 16 + lr, step, fa);
+          read_frag(bufA, i * 16, step, fa);
           // x scales of this lane's output rows 4 * (lane / 16) + c
           const f32x4 xsv = *(const f32x4*)(sc + step * BM + wm * MW + i * 16 + 4 * lg);
 #pragma unroll
@@ -687,12 +740,36 @@ struct Tile {
      }
     };
     auto compute_stage = [&](const uint8_t* buf, int nvalid) __attribute__((always_inline)) {
+     const uint8_t* bufA = buf + wm * MW * ROWB;         // this wave's A rows
+     const uint8_t* bufB = buf + (BM + wn * NW) * ROWB;  // its weight rows (matrix mt: + mt * BN rows)
      if constexpr (FP8A) {
       compute_f8(buf, nvalid);
      } else {
       if (wm * MW >= nvalid) return;
       if (wm * MW + MW <= nvalid) {
         compute_full(buf);
+        return;
+      }
+      if constexpr (NT == kThreadsWide) {  // as compute_full, one A fragment at a time
+#pragma unroll
+        for (int jj = 0; jj < KSTEPS / WK; ++jj) {
+          const int step = jj * WK + wk;
+          FragT fb[NMAT][FN];
+#pragma unroll
+          for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) read_frag(bufB, mt * BN + j * 16, step, fb[mt][j]);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            if (wm * MW + i * 16 < nvalid) {
+              FragT fa;
+              read_frag(bufA, i * 16, step, fa);
+#pragma unroll
+              for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mma(acc[mt][i][j], fa, fb[mt][j]);
+            }
+        }
         return;
       }
 #pragma unroll
@@ -702,11 +779,11 @@ struct Tile {
         FragT fb[NMAT][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          if (wm * MW + i * 16 < nvalid) read_frag(buf, wm * MW + i * 16 + lr, step, fa[i]);
+          if (wm * MW + i * 16 < nvalid) read_frag(bufA, i * 16, step, fa[i]);
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) read_frag(buf, BM + mt * BN + wn * NW + j * 16 + lr, step, fb[mt][j]);
+          for (int j = 0; j < FN; ++j) read_frag(bufB, mt * BN + j * 16, step, fb[mt][j]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           if (wm * MW + i * 16 < nvalid) {
@@ -724,7 +801,7 @@ struct Tile {
     auto epilogue = [&](int j, uint8_t* red_area, bool whole) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
       int rb, nt;
-      tile_rc(item_tile(j), nb, N / BN, rb, nt);
+      tile_rc(item_tile(j), nb, (N + BN - 1) / BN, rb, nt);
       const int64_t row0 = (int64_t)rb * BM;
       const int n0 = nt * BN;
       if ((unsigned)m[BM + 1] >= (unsigned)e_end) return;  // uniform: no such tile
@@ -802,7 +879,7 @@ struct Tile {
     // v + RS into Ru, the MFMAs of stage v
     auto step = [&](const int v, Regs& Ru) __attribute__((always_inline)) {
           const int* m = meta3 + (c_j % kMetaSlots) * META;
-          uint8_t* buf = lds + (v & 1) * STAGE;
+          uint8_t* buf = (v & 1) ? lds1 : lds0;
           write_stage(Ru, buf);
           const bool more = v + RS < nv;  // a real load follows this step
           if (more && l_new && v >= 1) store_meta(l_j);
@@ -837,6 +914,278 @@ struct Tile {
     }
   }
 
+  // ---------------------------------------------------------------------------
+  // The wide class's bf16 tiles with direct global -> LDS loads.  Each stage's A
+  // rows and weight rows go from HBM (or L2) straight into one of ND LDS stage
+  // buffers with the buffer-load LDS form of gfx950, ND - 1 stages ahead of the
+  // MFMAs and with no register staging, so the loads in flight are bounded by LDS
+  // (ND x 32 KiB) instead of by registers.  The buffers are distinct LDS arrays, so
+  // the compiler tracks which stage each fragment read depends on and waits for
+  // exactly that stage's loads.  Each step waits until this wave's loads of the
+  // stage are in LDS, then a barrier makes every wave's loads of the stage visible
+  // and releases the buffer computed in the previous step, which takes the loads
+  // of the stage ND - 1 ahead.  Loads past the last stage (and of rows that hold
+  // no slot) use an offset past the buffer's range: no memory is read.  The
+  // schedule is run_all's for a class that never splits: whole tiles, F or F + 1
+  // per workgroup.
+  static constexpr int kDmaInstr = ROWS * C / NT;  // 16-byte loads per thread per stage
+  template <int N_, bool Q>
+  __device__ __forceinline__ static void wait_vm_lgkm0() {
+    // vmcnt(N_) and lgkmcnt(0) (the LDS writes of this wave done), then the barrier
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
+    if constexpr (Q)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N_) : "memory");
+  }
+
+  template <bool SH, int ND>
+  __device__ __forceinline__ static void run_dma(const FfnArgs& g, uint8_t* b0, uint8_t* b1,
+                                                 uint8_t* b2, uint8_t* b3, int* meta3, int nb,
+                                                 int nbr, int slot, int G) {
+    static_assert(WKIND == W_BF16 && NT == kThreadsWide && WK == 1 && KSTEPS == 1 && C == 4,
+                  "the direct-load pipeline serves the wide class's bf16 tiles");
+    static_assert(ND == 4, "four stage buffers");
+    static_assert((NT / C) * 2 == BM && (BN % (NT / C)) == 0 && kDmaInstr == 4,
+                  "each load instruction covers 128 rows of one operand");
+    const int N = PHASE == 1 ? g.I : g.H;
+    const int K = PHASE == 1 ? g.H : g.I;
+    const int Btok = g.slots / g.k;
+    const int nbs = SH ? (Btok + BM - 1) / BM : 1;
+    const int slot_end = SH ? g.slots + Btok : g.slots;
+    const int e_end = SH ? g.E_loc + g.n_shared : g.E_loc;
+    const int ncol = (N + BN - 1) / BN;
+    const int total = nb * ncol;
+    const int nst = K / BK;  // the caller checks K % BK == 0 and nst >= ND + 2
+    const int F = total / G;
+    const int nit = F + (slot < total - F * G ? 1 : 0);  // whole tiles of this workgroup
+    const int nv = nit * nst;
+    if (nv == 0) return;
+    const int tid = threadIdx.x;
+    // wave coordinates in scalar registers: every row test below is then a scalar
+    // branch, not an exec mask around each group of MFMAs
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wn = wave % WN;
+    const int wm = wave / WN;
+    const Act* abase = (const Act*)(PHASE == 1 ? g.x : g.h);
+    const Wt* wmat0 = (const Wt*)(PHASE == 1 ? g.w1 : g.w2);
+    const Wt* wmat1 = (const Wt*)(PHASE == 1 ? g.w3 : g.w2);
+
+    // ---- tile metadata (as run_all: a ring of kMetaSlots slots in LDS) ----
+    int ms0 = -1, ms1 = -1, me = -1;
+    auto fetch_meta = [&](int j) __attribute__((always_inline)) {
+      int rb, nt;
+      tile_rc(slot + j * G, nb, ncol, rb, nt);
+      const int64_t row0 = (int64_t)rb * BM;
+      if (SH && rb >= nbr) {
+        const int t0 = ((rb - nbr) % nbs) * BM + tid;
+        if (tid < BM) {
+          ms0 = t0 < Btok ? g.slots + t0 : -1;
+          ms1 = tid + 1 < BM && t0 + 1 < Btok ? g.slots + t0 + 1 : -1;
+        }
+        if (tid == 0) me = g.E_loc + (rb - nbr) / nbs;
+      } else {
+        if (tid < BM) {
+          ms0 = g.sorted_slots[row0 + tid];
+          ms1 = tid + 1 < BM ? g.sorted_slots[row0 + tid + 1] : -1;
+        }
+        if (tid == 0) me = g.block_expert[rb];
+      }
+    };
+    auto store_meta = [&](int j) __attribute__((always_inline)) {
+      int* m = meta3 + (j % kMetaSlots) * META;
+      if (tid < BM) {
+        const bool v0 = ms0 >= 0 && ms0 < slot_end;
+        const bool v1 = ms1 >= 0 && ms1 < slot_end;
+        m[tid] = v0 ? ms0 : -1;
+        if (v0 && !v1) m[BM] = tid + 1;
+        if (tid == 0 && !v0) m[BM] = 0;
+      }
+      if (tid == 0) m[BM + 1] = me;
+    };
+
+    // ---- the loads of one stage ----
+    // Load instruction i of thread tid fills LDS chunk i * NT + tid of the stage
+    // buffer: row (i * NT + tid) / 4, physical chunk tid % 4, which holds logical
+    // chunk c = (tid % 4) ^ swz(row) (the swizzle of read_frag).  Instructions 0-1
+    // take A rows 0-255, 2-3 weight rows 0-255 (gate/up: W1 then W3; down: W2).
+    const int c_log = (tid & 3) ^ ((tid >> 4) & 3);
+    const uint32_t a_bytes = PHASE == 1 ? (uint32_t)Btok * (uint32_t)K * ASZ
+                                        : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
+    uint32_t l_aoff[2] = {kOob, kOob};
+    uint32_t l_boff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = NMAT == 2 ? (tid >> 2) : i * (NT / C) + (tid >> 2);
+      l_boff[i] = (uint32_t)(rr * K + c_log * 8) * WSZ;
+    }
+    __amdgpu_buffer_rsrc_t l_b_rsrc[2];
+    int l_j = 0, l_s = 0;
+    bool l_new = true;
+    auto enter_load_tile = [&](int j) __attribute__((always_inline)) {
+      const int* m = meta3 + (j % kMetaSlots) * META;
+      int rb, nt;
+      tile_rc(slot + j * G, nb, ncol, rb, nt);
+      int e = __builtin_amdgcn_readfirstlane(m[BM + 1]);
+      int n0 = nt * BN;
+      const bool eok = j < nit && (unsigned)e < (unsigned)e_end;
+      if (!eok) {
+        e = 0;
+        n0 = 0;
+      }
+      const int64_t wrow0 = ((int64_t)e * N + n0) * K;
+      const uint32_t wbytes = eok ? (uint32_t)(N - n0) * (uint32_t)K * WSZ : 0u;
+      l_b_rsrc[0] = make_rsrc(wmat0 + wrow0, wbytes);
+      l_b_rsrc[1] = make_rsrc(wmat1 + wrow0, wbytes);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = i * (NT / C) + (tid >> 2);
+        const int sl = m[row];
+        l_aoff[i] = kOob;
+        if (eok && sl >= 0 && sl < slot_end) {
+          const int arow = PHASE == 1 ? (SH && sl >= g.slots ? sl - g.slots : sl / g.k) : rb * BM + row;
+          l_aoff[i] = (uint32_t)(arow * K + c_log * 8) * ASZ;
+        }
+      }
+    };
+    auto issue = [&](uint8_t* buf) __attribute__((always_inline)) {
+      if (l_new) enter_load_tile(l_j);
+      l_new = false;
+      const int soff = l_s * BK * ASZ;
+      typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+      for (int i = 0; i < kDmaInstr; ++i) {
+        lds_void* dst = (lds_void*)(buf + (i * NT + wave * 64) * 16);
+        if (i < 2)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, l_aoff[i], soff, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(l_b_rsrc[NMAT == 2 ? i - 2 : 0], dst, 16,
+                                                   l_boff[i - 2], soff, 0, 0);
+      }
+      if (++l_s == nst) {  // past the last tile the offsets are out of range
+        ++l_j;
+        l_s = 0;
+        l_new = true;
+      }
+    };
+
+    // ---- MFMAs of one stage (one 32-deep step) ----
+    f32x4 acc[NMAT][FM][FN];
+    const int lr = lane & 15, lg = lane >> 4;
+    const int foff = lr * ROWB + ((lg ^ swz<C>(lr)) << 4);
+    // every row of this wave's part holds a slot: all reads first, then the MFMAs
+    auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
+      const uint8_t* bufA = buf + wm * MW * ROWB + foff;
+      const uint8_t* bufB = buf + (BM + wn * NW) * ROWB + foff;
+      bf16x8 fb[NMAT][FN], fa[FM];
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[mt][j] = *(const bf16x8*)(bufB + (mt * BN + j * 16) * ROWB);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(bufA + i * 16 * ROWB);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[mt][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[mt][j], acc[mt][i][j], 0, 0, 0);
+    };
+    // the last row-block of an expert: 16-row groups past nvalid are skipped
+    auto compute_part = [&](const uint8_t* buf, int nvalid) __attribute__((always_inline)) {
+      const uint8_t* bufA = buf + wm * MW * ROWB + foff;
+      const uint8_t* bufB = buf + (BM + wn * NW) * ROWB + foff;
+      bf16x8 fb[NMAT][FN];
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[mt][j] = *(const bf16x8*)(bufB + (mt * BN + j * 16) * ROWB);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (wm * MW + i * 16 >= nvalid) continue;
+        const bf16x8 fa = *(const bf16x8*)(bufA + i * 16 * ROWB);
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[mt][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[mt][j], acc[mt][i][j], 0, 0, 0);
+      }
+    };
+
+    // ---- the pipeline ----
+    // item j's metadata: fetched at step j * nst - ND - 1 and stored at step
+    // j * nst - ND (before that step's barrier), so that it is published before
+    // step j * nst - ND + 1 issues the first loads of item j; items whose first
+    // loads come earlier are described before the loop.
+    auto buf_of = [&](int u) __attribute__((always_inline)) {
+      return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : b3));
+    };
+    for (int j = 0; j < nit && j * nst - ND <= 0; ++j) {
+      fetch_meta(j);
+      store_meta(j);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < ND - 1; ++u) issue(buf_of(u));
+    int c_j = 0, c_s = 0;
+    bool after_store = false;
+    auto step = [&](int v, auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const int jn = (v + ND + 1) / nst;  // item whose metadata this step fetches
+      if ((v + ND + 1) % nst == 0 && jn < nit && jn * nst - ND > 0) fetch_meta(jn);
+      if ((v + ND) % nst == 0 && (v + ND) / nst < nit && v + ND > ND) store_meta((v + ND) / nst);
+      // this stage's loads are the oldest but (ND - 2) stages of this wave's loads;
+      // after tile stores (counted in the same counter) wait for everything
+      if (after_store)
+        wait_vm_lgkm0<0, true>();
+      else
+        wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
+      after_store = false;
+      issue(buf_of((u + ND - 1) % ND));  // the buffer computed in the previous step
+      const int* m = meta3 + (c_j % kMetaSlots) * META;
+      if (c_s == 0) {
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jn2 = 0; jn2 < FN; ++jn2) acc[mt][i][jn2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const bool live = c_j < nit && (unsigned)m[BM + 1] < (unsigned)e_end;
+      const int nvalid = m[BM];
+      if (live && wm * MW < nvalid) {
+        if (wm * MW + MW <= nvalid)
+          compute_full(buf_of(u));
+        else
+          compute_part(buf_of(u), nvalid);
+      }
+      if (c_s == nst - 1) {
+        int rb, nt;
+        tile_rc(slot + c_j * G, nb, ncol, rb, nt);
+        if (live) {
+          store_acc(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane);
+          after_store = true;
+        }
+        ++c_j;
+        c_s = 0;
+      } else {
+        ++c_s;
+      }
+    };
+    // every step of the unrolled loop runs (steps past nv compute nothing and load
+    // out of range), so the compiler can count the loads in flight at each read
+    for (int v0 = 0; v0 < nv; v0 += ND) {
+      step(v0, std::integral_constant<int, 0>{});
+      step(v0 + 1, std::integral_constant<int, 1>{});
+      step(v0 + 2, std::integral_constant<int, 2>{});
+      step(v0 + 3, std::integral_constant<int, 3>{});
+    }
+    // every load of this workgroup has landed before it exits (the last steps'
+    // loads were out of range, so this costs nothing)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
   // The fix-up of tail tile tq (the tile F * G + tq of the schedule in run_all):
   // if more than one workgroup's range holds part of it, add their pieces in
   // reduction order (workgroup order) and store the tile.  Workgroup w's tail
@@ -851,7 +1200,7 @@ struct Tile {
                                                int tq) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
-    const int total = nb * (N / BN);
+    const int total = nb * ((N + BN - 1) / BN);
     const int nst = (K + BK - 1) / BK;
     const int F = total / G;
     const int r = total - F * G;
@@ -863,11 +1212,14 @@ struct Tile {
     if (w0 == w1) return;  // one range holds the whole tile; run_all stored it
     const int t = F * G + tq;
     int rb, nt;
-    tile_rc(t, nb, N / BN, rb, nt);
+    tile_rc(t, nb, (N + BN - 1) / BN, rb, nt);
     const int64_t row0 = (int64_t)rb * BM;
     const int n0 = nt * BN;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // a launch of more than NT threads runs this too: the extra threads only
+    // take part in the barrier
+    const bool act = tid < NT;
+    const int wave = act ? tid >> 6 : 0;
     const int lane = tid & 63;
     const int wk = wave % WK;
     const int wn = (wave / WK) % WN;
@@ -900,7 +1252,7 @@ struct Tile {
             acc[mt][i][jn] = add ? acc[mt][i][jn] + v : v;
           }
     };
-    if (wk == 0) load_piece(0, false);
+    if (act && wk == 0) load_piece(0, false);
     if (SH && rb >= nbr) {  // a shared expert's row-block (see run_all)
       const int Btok = g.slots / g.k;
       const int nbs = (Btok + BM - 1) / BM;
@@ -917,7 +1269,7 @@ struct Tile {
       }
     }
     __syncthreads();
-    if (wk != 0) return;
+    if (!act || wk != 0) return;
     for (int q = 1; q < npieces; ++q) load_piece(q, true);
     store_acc(g, acc, meta, row0, n0, wm, wn, lane);
   }
@@ -926,49 +1278,77 @@ struct Tile {
 // ---------------------------------------------------------------------------
 // configuration table: must match kVariants in moe_common.h
 //   Cfg<V, PHASE, WKIND>::R is the tile runner of configuration V in that phase.
+//   NT threads per workgroup; RX multiplies the LDS row bytes of the fp32, fp8 and
+//   fp8 x fp8 tiles (their fragments, decode or load shapes need 128-byte rows
+//   where the bf16 tile of the wide class uses 64).
 // ---------------------------------------------------------------------------
 template <int V, int PHASE, int WKIND>
 struct Cfg;
-#define MOE_CFG(V, BM, BN1, BN2, ROWB1, ROWB2, WM, WN, WK, RS, STREAM)                         \
+#define MOE_CFG(V, BM, BN1, BN2, ROWB1, ROWB2, WM, WN, WK, RS, STREAM, NT, RX)                 \
   template <int PHASE, int WKIND>                                                             \
   struct Cfg<V, PHASE, WKIND> {                                                               \
     static constexpr int BN = PHASE == 1 ? BN1 : BN2;                                         \
-    using R = Tile<BM, BN, WM, WN, WK, (PHASE == 1 ? ROWB1 : ROWB2), RS, STREAM, PHASE, WKIND>; \
+    static constexpr int ROWB = (PHASE == 1 ? ROWB1 : ROWB2) * (WKIND == W_BF16 ? 1 : RX);    \
+    using R = Tile<BM, BN, WM, WN, WK, ROWB, RS, STREAM, PHASE, WKIND, NT>;                   \
   };                                                                                          \
   static_assert(kVariants[V].bm == BM && kVariants[V].bn1 == BN1 && kVariants[V].bn2 == BN2 && \
                     kVariants[V].rowb == ROWB1 && kVariants[V].wm == WM &&                    \
                     kVariants[V].wn == WN && kVariants[V].wk == WK && kVariants[V].splitk == 1 && \
-                    kVariants[V].stream == STREAM,                                            \
+                    kVariants[V].stream == STREAM &&                                          \
+                    kVariants[V].wgcu == (NT == kThreads ? kWgPerCu : 1),                     \
                 "kernel configuration table out of sync with kVariants");
-// Two workgroups share a compute unit, so each stage buffer holds at most 32 KiB:
-// every stage carries 16 KiB of weights (the down phase has one weight matrix, so
-// its LDS rows are twice as wide).  The small-M configurations read each weight
-// tile once (one row-block per expert is the common case), so they stream the
-// weights with non-temporal loads, which sustain a markedly higher HBM rate; the
-// largest one serves many row-blocks per expert that re-read each weight tile
-// from L2, so it keeps cached loads.
-MOE_CFG(0, 16, 16, 16, 512, 1024, 1, 1, 4, 2, 1)
-MOE_CFG(1, 32, 32, 32, 256, 512, 1, 2, 2, 2, 1)
-MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2, 1)
-MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2, 0)
+// Streaming class: two workgroups share a compute unit, so each stage buffer
+// holds at most 32 KiB: every stage carries 16 KiB of weights (the down phase has
+// one weight matrix, so its LDS rows are twice as wide).  The small-M
+// configurations read each weight tile once (one row-block per expert is the
+// common case), so they stream the weights with non-temporal loads, which sustain
+// a markedly higher HBM rate; the largest one serves many row-blocks per expert
+// that re-read each weight tile from L2, so it keeps cached loads.
+MOE_CFG(0, 16, 16, 16, 512, 1024, 1, 1, 4, 2, 1, kThreads, 1)
+MOE_CFG(1, 32, 32, 32, 256, 512, 1, 2, 2, 2, 1, kThreads, 1)
+MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2, 1, kThreads, 1)
+MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2, 0, kThreads, 1)
+// Wide class: one 512-thread workgroup per compute unit computes a 256 x 256
+// output tile (gate/up: 128 gate and 128 up columns), eight waves of 128 x 64
+// each.  Per byte staged it does twice the MFMA work of the 128-row streaming
+// tile, which halves the L2 and fabric traffic per FLOP where the matrix units
+// bound the layer.  bf16 stages are 32 deep (64-byte LDS rows, 32 KiB a stage).
+MOE_CFG(4, 256, 128, 256, 64, 64, 2, 4, 1, 2, 0, kThreadsWide, 2)
+// more of the streaming class: other column widths, stage depths and load policies
+MOE_CFG(5, 16, 32, 32, 256, 512, 1, 2, 2, 2, 1, kThreads, 1)
+MOE_CFG(6, 32, 16, 32, 512, 512, 1, 1, 4, 2, 1, kThreads, 1)
+MOE_CFG(7, 64, 32, 64, 256, 256, 2, 2, 1, 2, 1, kThreads, 1)
+MOE_CFG(8, 32, 64, 64, 128, 256, 1, 4, 1, 2, 1, kThreads, 1)
+MOE_CFG(9, 64, 64, 64, 128, 256, 2, 2, 1, 2, 0, kThreads, 1)
+MOE_CFG(10, 128, 64, 128, 128, 128, 2, 2, 1, 2, 1, kThreads, 1)
+MOE_CFG(11, 32, 32, 32, 256, 512, 1, 2, 2, 2, 0, kThreads, 1)
 #undef MOE_CFG
+// the streaming class's entries, for the dispatch switches
+#define MOE_STREAM_VARIANTS(X) X(0) X(1) X(2) X(3) X(5) X(6) X(7) X(8) X(9) X(10) X(11)
 
 template <int PHASE, int WKIND>
-constexpr int lds_bytes() {
+constexpr int lds_bytes_stream() {
   int m = 0;
 #define MOE_LDS(V)                                                                            \
   m = Cfg<V, PHASE, WKIND>::R::LDS_BYTES > m ? Cfg<V, PHASE, WKIND>::R::LDS_BYTES : m;
-  MOE_LDS(0) MOE_LDS(1) MOE_LDS(2) MOE_LDS(3)
+  MOE_STREAM_VARIANTS(MOE_LDS)
 #undef MOE_LDS
   return m;
 }
+// dynamic LDS of the wide launch; its bf16 tiles use four static stage buffers
+template <int PHASE, int WKIND>
+constexpr int lds_bytes_wide() {
+  return WKIND == W_BF16 ? 0 : Cfg<kWideVariant, PHASE, WKIND>::R::LDS_BYTES;
+}
 
-// The tiles of configuration V in phase PHASE, dealt out statically.
+// The tiles of configuration V in phase PHASE, dealt out statically over the
+// launch's grid.
 template <int V, int PHASE, int WKIND, bool SH>
 __device__ __forceinline__ void run_phase(const FfnArgs& g, uint8_t* lds, int* meta3, int nb,
                                           int nbr) {
   using R = typename Cfg<V, PHASE, WKIND>::R;
-  R::template run_all<SH>(g, lds, meta3, nb, nbr, xcd_slot(blockIdx.x, gridDim.x), gridDim.x);
+  R::template run_all<SH>(g, lds, lds + R::STAGE, meta3, nb, nbr, xcd_slot(blockIdx.x, gridDim.x),
+                          gridDim.x);
 }
 
 // Row-blocks of the launch: the routed ones the sort wrote (nbr), then with
@@ -990,7 +1370,8 @@ __device__ __forceinline__ bool block_counts(const FfnArgs& g, int v, int& nb, i
 // The device status word: MOE_DEV_BAD_VARIANT for a configuration index outside
 // the menu, MOE_DEV_BAD_BLOCKS for a row-block count below zero or beyond what the
 // buffers hold (the launch then runs only the row-blocks that fit).  Workgroup 0
-// writes it once per launch, so each call reports its own inputs.
+// of the streaming-class launch writes it once per phase, so each call reports
+// its own inputs.
 template <bool SH>
 __device__ __forceinline__ void report_status(const FfnArgs& g, int v, int nbr) {
   if (blockIdx.x != 0 || threadIdx.x != 0 || g.status == nullptr) return;
@@ -1006,66 +1387,90 @@ __device__ __forceinline__ void report_status(const FfnArgs& g, int v, int nbr) 
   *g.status = st;
 }
 
+// Streaming class: configurations 0-3, two 256-thread workgroups per CU.
 template <int PHASE, int WKIND, bool SH>
 __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int meta3[kMetaSlots * (kMaxBlockM + 2)];
   const int v = *g.variant;
-  int nb = *g.num_blocks;
-  int nbr = nb;
-  report_status<SH>(g, v, nbr);
-  if constexpr (!SH) {
-    if (v < 0 || v >= kNumVariants || nb <= 0) return;  // no tiles (align_sort wrote none)
-    // never address rows beyond the buffers, whatever the device state says
-    const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
-    nb = nb < nb_cap ? nb : nb_cap;
-  } else {
-    if (!block_counts<SH>(g, v, nb, nbr)) return;
-  }
+  report_status<SH>(g, v, *g.num_blocks);
+  int nb, nbr;
+  if (v == kWideVariant || !block_counts<SH>(g, v, nb, nbr)) return;
   switch (v) {
-    case 0: run_phase<0, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
-    case 1: run_phase<1, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
-    case 2: run_phase<2, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
-    case 3: run_phase<3, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); break;
+#define MOE_RUN(V)                                         \
+  case V:                                                  \
+    run_phase<V, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr); \
+    break;
+    MOE_STREAM_VARIANTS(MOE_RUN)
+#undef MOE_RUN
     default: break;
   }
 }
 
-// The fix-up of one phase's split tail tiles (Tile::fixup), one workgroup per
-// tail tile; the grid is the main launch's, which bounds the tail tiles.
+// The launch that follows the streaming one in each phase: one 512-thread
+// workgroup per CU.  With the wide configuration chosen it computes all of the
+// phase's tiles; otherwise it is the streaming class's fix-up, adding the
+// partial sums of each split tail tile (Tile::fixup; tail tile tq for tq =
+// workgroup, workgroup + grid, ...).
 template <int PHASE, int WKIND, bool SH>
-__global__ void __launch_bounds__(kThreads) ffn_fixup_kernel(FfnArgs g) {
-  __shared__ int meta[kMaxBlockM + 2];
+__global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int meta3[kMetaSlots * (kMaxBlockM + 2)];
   const int v = *g.variant;
-  int nb = *g.num_blocks;
-  int nbr = nb;
-  if constexpr (!SH) {
-    if (v < 0 || v >= kNumVariants || nb <= 0) return;
-    const int nb_cap = (int)(g.rows_max / kVariants[v].bm);
-    nb = nb < nb_cap ? nb : nb_cap;
-  } else {
-    if (!block_counts<SH>(g, v, nb, nbr)) return;
+  int nb, nbr;
+  if (!block_counts<SH>(g, v, nb, nbr)) return;
+  if (v == kWideVariant) {
+    if constexpr (WKIND == W_BF16) {
+      // four distinct LDS arrays: the compiler then waits for each stage's own
+      // direct loads only (see Tile::run_dma)
+      using R = typename Cfg<kWideVariant, PHASE, W_BF16>::R;
+      __shared__ __attribute__((aligned(16))) uint8_t s0[R::STAGE];
+      __shared__ __attribute__((aligned(16))) uint8_t s1[R::STAGE];
+      __shared__ __attribute__((aligned(16))) uint8_t s2[R::STAGE];
+      __shared__ __attribute__((aligned(16))) uint8_t s3[R::STAGE];
+      const int K = PHASE == 1 ? g.H : g.I;
+      const int slot = xcd_slot(blockIdx.x, gridDim.x);
+      if (K % R::BK == 0 && K / R::BK >= 6)
+        R::template run_dma<SH, 4>(g, s0, s1, s2, s3, meta3, nb, nbr, slot, gridDim.x);
+      else  // a reduction too short for the four-stage pipeline
+        R::template run_all<SH>(g, s0, s1, meta3, nb, nbr, slot, gridDim.x);
+    } else {
+      run_phase<kWideVariant, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr);
+    }
+    return;
   }
-  const int G = gridDim.x, tq = blockIdx.x;
-  switch (v) {
-    case 0: Cfg<0, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
-    case 1: Cfg<1, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
-    case 2: Cfg<2, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
-    case 3: Cfg<3, PHASE, WKIND>::R::template fixup<SH>(g, meta, nb, nbr, G, tq); break;
-    default: break;
+  const int G = g.grid_stream;
+  for (int tq = blockIdx.x; tq < G; tq += gridDim.x) {
+    __syncthreads();  // the previous tail tile's readers of meta3 are done
+    switch (v) {
+#define MOE_FIX(V)                                                              \
+  case V:                                                                       \
+    Cfg<V, PHASE, WKIND>::R::template fixup<SH>(g, meta3, nb, nbr, G, tq); \
+    break;
+      MOE_STREAM_VARIANTS(MOE_FIX)
+#undef MOE_FIX
+      default: break;
+    }
   }
 }
 
 template <int PHASE, int WKIND, bool SH>
-hipError_t launch_phase_sh(const FfnArgs& g, int grid, hipStream_t s) {
-  constexpr int lds = lds_bytes<PHASE, WKIND>();
-  static_assert((lds + 4096) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
+hipError_t launch_phase_sh(const FfnArgs& g, int grid_wide, hipStream_t s) {
+  constexpr int meta_bytes = kMetaSlots * (kMaxBlockM + 2) * 4;
+  constexpr int lds = lds_bytes_stream<PHASE, WKIND>();
+  static_assert((lds + meta_bytes) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
+  constexpr int ldsw = lds_bytes_wide<PHASE, WKIND>();
+  constexpr int ldsw_static = WKIND == W_BF16 ? 4 * Cfg<kWideVariant, PHASE, W_BF16>::R::STAGE : 0;
+  static_assert(ldsw + ldsw_static + meta_bytes <= 160 * 1024,
+                "LDS budget of one wide workgroup per CU");
   hipError_t e = opt_in_lds((const void*)ffn_kernel<PHASE, WKIND, SH>, lds);
   if (e != hipSuccess) return e;
-  ffn_kernel<PHASE, WKIND, SH><<<grid, kThreads, lds, s>>>(g);
+  e = opt_in_lds((const void*)ffn_wide_kernel<PHASE, WKIND, SH>, ldsw);
+  if (e != hipSuccess) return e;
+  ffn_kernel<PHASE, WKIND, SH><<<g.grid_stream, kThreads, lds, s>>>(g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ffn_fixup_kernel<PHASE, WKIND, SH><<<grid, kThreads, 0, s>>>(g);
+  ffn_wide_kernel<PHASE, WKIND, SH><<<grid_wide, kThreadsWide, ldsw, s>>>(g);
   return hipGetLastError();
 }
 
@@ -1096,10 +1501,11 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               const int32_t* block_expert, const int32_t* num_blocks,
                               const int32_t* variant, void* y_slots, void* h, float* part,
                               int32_t* status, int num_cus, int64_t rows_max, hipStream_t s) {
+  const int grid_stream = num_cus * kWgPerCu < kMaxGrid ? num_cus * kWgPerCu : kMaxGrid;
+  const int grid = num_cus < kMaxGrid ? num_cus : kMaxGrid;  // the wide class's launch
   FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
             h, y_slots, part, p.hidden, p.inter, p.top_k, p.local_experts,
-            p.tokens * p.top_k, rows_max, nullptr, p.shared_experts, status};
-  const int grid = num_cus * kWgPerCu < kMaxGrid ? num_cus * kWgPerCu : kMaxGrid;
+            p.tokens * p.top_k, rows_max, nullptr, p.shared_experts, status, grid_stream};
   switch (p.weight_dtype) {
     case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);
     case MOE_BF16: return launch_w<W_BF16>(g, phases, grid, s);

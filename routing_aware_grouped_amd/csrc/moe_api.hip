@@ -110,7 +110,9 @@ moe_status validate(const moe_problem* p) {
   const int64_t rows = rows_max_of(p);
   for (int v = 0; v < kNumVariants; ++v) {
     const int64_t rt = rows / kVariants[v].bm;
-    const int64_t T = rt * (p->inter / kVariants[v].bn1 + (int64_t)(p->hidden / kVariants[v].bn2) * kVariants[v].splitk);
+    const int64_t q1 = (p->inter + kVariants[v].bn1 - 1) / kVariants[v].bn1;
+    const int64_t q2 = (p->hidden + kVariants[v].bn2 - 1) / kVariants[v].bn2 * kVariants[v].splitk;
+    const int64_t T = rt * (q1 + q2);
     if (T >= (1ll << 24)) return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
@@ -164,10 +166,12 @@ moe_status fill_cost_table(const moe_problem* p, CostTable* t) {
   if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
   for (int v = 0; v < kNumVariants; ++v) {
     t->b[v] = kVariants[v].bm;
-    t->q1[v] = p->inter / kVariants[v].bn1;
-    t->q2[v] = (p->hidden / kVariants[v].bn2) * kVariants[v].splitk;
-    // tiles resident at once: the persistent grid of the grouped FFN
-    const int grid = cus * kWgPerCu < kMaxGrid ? cus * kWgPerCu : kMaxGrid;
+    // column tiles per row-block (a wide tile may reach past H: ragged last tile)
+    t->q1[v] = (p->inter + kVariants[v].bn1 - 1) / kVariants[v].bn1;
+    t->q2[v] = (p->hidden + kVariants[v].bn2 - 1) / kVariants[v].bn2 * kVariants[v].splitk;
+    // tiles resident at once: the persistent grid of the configuration's class
+    const int per_cu = kVariants[v].wgcu;
+    const int grid = cus * per_cu < kMaxGrid ? cus * per_cu : kMaxGrid;
     t->S1[v] = grid;
     t->S2[v] = grid;
     t->rt_shared[v] = p->shared_experts * ((p->tokens + kVariants[v].bm - 1) / kVariants[v].bm);
@@ -182,7 +186,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 5; }
+int32_t moe_abi_version(void) { return 6; }
 
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
@@ -197,7 +201,9 @@ int32_t moe_num_variants(void) { return kNumVariants; }
 moe_status moe_variant_info(int32_t v, int32_t* out) {
   if (!out || v < 0 || v >= kNumVariants) return MOE_ERR_INVALID_ARG;
   const VariantDesc& d = kVariants[v];
-  const int32_t vals[MOE_VARIANT_FIELDS] = {d.bm, d.bn1, d.bn2, d.rowb / 2, d.wm, d.wn, d.wk, d.splitk, d.stream};
+  const int32_t vals[MOE_VARIANT_FIELDS] = {d.bm,     d.bn1,    d.bn2,  d.rowb / 2,
+                                            d.wm,     d.wn,     d.wk,   d.splitk,
+                                            d.stream, d.wgcu,   64 * d.wm * d.wn * d.wk};
   memcpy(out, vals, sizeof vals);
   return MOE_OK;
 }

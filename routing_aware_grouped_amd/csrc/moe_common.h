@@ -34,52 +34,74 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// Compiled tile configurations of the polymorphic grouped FFN.  All share one
-// workgroup size (256 threads = 4 waves), one launch shape per GEMM phase, one LDS
-// allocation and one register budget, so they are one occupancy class (RaMP,
-// section 3.3: one shared-memory buffer and one register count for every entry).
+// Compiled tile configurations of the polymorphic grouped FFN.  They come in two
+// occupancy classes, each one kernel per GEMM phase with one workgroup size, one
+// LDS allocation and one register budget for all its entries (RaMP, section 3.3:
+// one shared-memory buffer and one register count for every entry of a
+// polymorphic kernel):
+//   - the streaming class: 256 threads, two workgroups per CU (entries 0-3);
+//   - the wide class: 512 threads, one workgroup per CU, a 256 x 256 output tile
+//     whose larger per-workgroup reuse of every staged byte suits the loads where
+//     the matrix units, not HBM, bound the time (entry 4).
 //   bm    token rows per tile (b_c of RaMP Eq. 1)
 //   bn1   weight rows per tile of W1 and of W3 in the gate/up phase
 //   bn2   weight rows per tile of W2 in the down phase
-//   rowb  LDS bytes per tile row per pipeline stage (BLOCK_K = rowb / 2 for
-//         bf16 operands, rowb / 4 for fp32)
+//   rowb  LDS bytes per tile row per pipeline stage for bf16 operands (BLOCK_K =
+//         rowb / 2; fp32 operands use half the depth, and in the wide class the
+//         fp32 and fp8 x fp8 tiles use twice the row bytes)
 //   wm, wn, wk  waves along M, along N, and splitting K inside a tile
 //   splitk      tiles splitting K of the down phase (1 = none)
 //   stream      1: weights are read with non-temporal (streaming) loads, for the
 //               small-M configurations where each weight tile is read once;
 //               0: cached loads, for row-blocks that re-read a weight tile
+//   wgcu        workgroups per CU (2: streaming class, 1: wide class)
 // ---------------------------------------------------------------------------
 struct VariantDesc {
-  int bm, bn1, bn2, rowb, wm, wn, wk, splitk, stream;
+  int bm, bn1, bn2, rowb, wm, wn, wk, splitk, stream, wgcu;
 };
 
-constexpr int kNumVariants = 4;
-constexpr int kThreads = 256;
+constexpr int kNumVariants = 12;
+constexpr int kThreads = 256;      // streaming class
+constexpr int kThreadsWide = 512;  // wide class
+constexpr int kWideVariant = 4;
 
+// The compiled configuration space.  The served menu of a workload is chosen
+// from it offline (RaMP section 3.1: greedily, on timed fit loads); entries left
+// out of a menu get a cost-model prediction that never wins.
 constexpr VariantDesc kVariants[kNumVariants] = {
-    {16, 16, 16, 512, 1, 1, 4, 1, 1},
-    {32, 32, 32, 256, 1, 2, 2, 1, 1},
-    {64, 64, 64, 128, 2, 2, 1, 1, 1},
-    {128, 64, 128, 128, 2, 2, 1, 1, 0},
+    {16, 16, 16, 512, 1, 1, 4, 1, 1, 2},      // 0
+    {32, 32, 32, 256, 1, 2, 2, 1, 1, 2},      // 1
+    {64, 64, 64, 128, 2, 2, 1, 1, 1, 2},      // 2
+    {128, 64, 128, 128, 2, 2, 1, 1, 0, 2},    // 3
+    {256, 128, 256, 64, 2, 4, 1, 1, 0, 1},    // 4: the wide class
+    {16, 32, 32, 256, 1, 2, 2, 1, 1, 2},      // 5: 0 with twice the columns
+    {32, 16, 32, 512, 1, 1, 4, 1, 1, 2},      // 6: 1 with half the gate/up columns
+    {64, 32, 64, 256, 2, 2, 1, 1, 1, 2},      // 7: 2 with half the gate/up columns
+    {32, 64, 64, 128, 1, 4, 1, 1, 1, 2},      // 8: 1 with twice the columns
+    {64, 64, 64, 128, 2, 2, 1, 1, 0, 2},      // 9: 2 with cached weight loads
+    {128, 64, 128, 128, 2, 2, 1, 1, 1, 2},    // 10: 3 with streaming weight loads
+    {32, 32, 32, 256, 1, 2, 2, 1, 0, 2},      // 11: 1 with cached weight loads
 };
 
 constexpr int kMinBlockM = 16;
-constexpr int kMaxBlockM = 128;
+constexpr int kMaxBlockM = 256;
 
-// workgroups per CU of the persistent grouped-FFN launch
+// workgroups per CU of the streaming class's persistent launch
 constexpr int kWgPerCu = 2;
 
-// The persistent grouped-FFN grid is min(CUs * kWgPerCu, kMaxGrid) workgroups
-// (MI355X: 256 CUs, so 512).  Each may leave up to two partial tiles of at most
-// kPieceMax fp32 sums in the workspace (the split tail tiles), so the workspace
-// size does not depend on the device.
+// The streaming class's persistent grid is min(CUs * kWgPerCu, kMaxGrid)
+// workgroups (MI355X: 256 CUs, so 512); the wide class's is min(CUs, kMaxGrid).
+// In the streaming class each workgroup may leave up to two partial tiles of at
+// most kPieceMax fp32 sums in the workspace (the split tail tiles; the wide class
+// never splits a tile), so the workspace size does not depend on the device.
 constexpr int kMaxGrid = 512;
 constexpr int piece_floats(const VariantDesc& d) {
   return 2 * d.bm * d.bn1 > d.bm * d.bn2 ? 2 * d.bm * d.bn1 : d.bm * d.bn2;
 }
 constexpr int piece_max() {
   int m = 0;
-  for (int v = 0; v < kNumVariants; ++v) m = piece_floats(kVariants[v]) > m ? piece_floats(kVariants[v]) : m;
+  for (int v = 0; v < kNumVariants; ++v)
+    if (kVariants[v].wgcu == kWgPerCu) m = piece_floats(kVariants[v]) > m ? piece_floats(kVariants[v]) : m;
   return m;
 }
 constexpr int kPieceMax = piece_max();

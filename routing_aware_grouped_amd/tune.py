@@ -221,13 +221,25 @@ def collect(shape_name: str, reps: int = 9, n_rep_loads: int = 1, log=print) -> 
     return dict(shape=shape_name, cost_constants=ccj, loads=loads, variants=V)
 
 
-def fit(data: dict) -> dict:
-    """theta per configuration from collected timings, with diagnostics."""
+# prediction of a configuration outside the served menu: larger than any real one,
+# so the device's argmin never takes it (finite, so the fp32 chain stays exact)
+OFF_MENU_THETA0 = 1.0e30
+
+
+def fit(data: dict, menu_size: int | None = None) -> dict:
+    """theta per configuration from collected timings, with diagnostics.
+
+    The served menu (RaMP section 3.1) is the first `menu_size` configurations of
+    the greedy order on the fit loads' forced times; the others get theta =
+    (OFF_MENU_THETA0, 0, 0, 0), which the device's argmin never picks."""
     V = data["variants"]
     cc = data["cost_constants"]
     F = np.stack([features(ld["counts"], cc) for ld in data["loads"]])  # [n][V][4]
     t = np.array([ld["times_us"] for ld in data["loads"]], dtype=np.float64)  # [n][V]
-    theta = np.stack([fit_nnls(F[:, v, :], t[:, v]) for v in range(V)]).astype(np.float32)
+    order = greedy_menu(t, V)
+    menu = sorted(order[: (menu_size or V)])
+    theta = np.stack([fit_nnls(F[:, v, :], t[:, v]) if v in menu else
+                      np.array([OFF_MENU_THETA0, 0.0, 0.0, 0.0]) for v in range(V)]).astype(np.float32)
     # diagnostics in float64 (the device's own fp32 choice is what the benchmark reports)
     pred = np.einsum("nvk,vk->nv", F, theta.astype(np.float64))
     pick = pred.argmin(axis=1)
@@ -239,9 +251,13 @@ def fit(data: dict) -> dict:
         fit_loads=len(t),
         fit_geomean_gap=float(np.exp(np.mean(np.log1p(gaps))) - 1.0),
         fit_worst_gap=float(gaps.max()),
-        spearman_mean=float(np.mean([spearman(pred[i], t[i]) for i in range(len(t))])),
+        spearman_mean=float(np.mean([spearman(pred[i][menu], t[i][menu]) for i in range(len(t))])),
         picked_rel_err_median=float(np.median(rel_err)),
-        greedy_menu=greedy_menu(t, V),
+        greedy_menu=order,
+        menu=menu,
+        # cost of serving the menu instead of every compiled configuration, on
+        # the fit loads: geomean of best-in-menu / best-overall - 1
+        menu_geomean_loss=float(np.exp(np.mean(np.log(t[:, menu].min(axis=1) / best))) - 1.0),
     )
 
 
@@ -251,6 +267,8 @@ def main(argv=None):
     ap.add_argument("--out", default=THETA_DIR, help="directory for <workload>.json")
     ap.add_argument("--reps", type=int, default=9, help="timed replays per configuration and load")
     ap.add_argument("--rep-loads", type=int, default=1, help="loads per (tokens, alpha)")
+    ap.add_argument("--menu", type=int, default=6,
+                    help="configurations in the served menu (greedy on the fit loads)")
     args = ap.parse_args(argv)
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
@@ -259,7 +277,7 @@ def main(argv=None):
         t0 = time.perf_counter()
         data = collect(shp, args.reps, args.rep_loads,
                        log=lambda m: print(m, file=sys.stderr, flush=True))
-        res = fit(data)
+        res = fit(data, args.menu)
         res.update(shape=shp, kernel_source_sha=kernel_source_hash(),
                    fit_alphas=FIT_ALPHAS, fit_tokens=FIT_TOKENS[shp], fit_rep0=FIT_REP0,
                    cost_constants=data["cost_constants"], loads=data["loads"],
@@ -267,7 +285,8 @@ def main(argv=None):
         path = os.path.join(args.out, f"{shp}.json")
         with open(path, "w") as f:
             json.dump(res, f, indent=1)
-        print(f"[tune] {shp}: theta {res['theta']} fit gap {res['fit_geomean_gap']:.4f} "
+        print(f"[tune] {shp}: menu {res['menu']} (greedy order {res['greedy_menu']}, menu loss "
+              f"{res['menu_geomean_loss']:.4f}) fit gap {res['fit_geomean_gap']:.4f} "
               f"(worst {res['fit_worst_gap']:.4f}) spearman {res['spearman_mean']:.3f} -> {path}",
               flush=True)
 

@@ -4,26 +4,35 @@ are checked against it, and the oracle's cost-model inputs come from here (never
 from the library)."""
 
 # BLOCK_M, BLOCK_N gate/up, BLOCK_N down, BLOCK_K, waves M, N, K-split, split-K,
-# streaming (non-temporal) weight loads
+# streaming (non-temporal) weight loads, workgroups per CU, threads per workgroup
 MENU = [
-    (16, 16, 16, 256, 1, 1, 4, 1, 1),
-    (32, 32, 32, 128, 1, 2, 2, 1, 1),
-    (64, 64, 64, 64, 2, 2, 1, 1, 1),
-    (128, 64, 128, 64, 2, 2, 1, 1, 0),
+    (16, 16, 16, 256, 1, 1, 4, 1, 1, 2, 256),
+    (32, 32, 32, 128, 1, 2, 2, 1, 1, 2, 256),
+    (64, 64, 64, 64, 2, 2, 1, 1, 1, 2, 256),
+    (128, 64, 128, 64, 2, 2, 1, 1, 0, 2, 256),
+    (256, 128, 256, 32, 2, 4, 1, 1, 0, 1, 512),
+    (16, 32, 32, 128, 1, 2, 2, 1, 1, 2, 256),
+    (32, 16, 32, 256, 1, 1, 4, 1, 1, 2, 256),
+    (64, 32, 64, 128, 2, 2, 1, 1, 1, 2, 256),
+    (32, 64, 64, 64, 1, 4, 1, 1, 1, 2, 256),
+    (64, 64, 64, 64, 2, 2, 1, 1, 0, 2, 256),
+    (128, 64, 128, 64, 2, 2, 1, 1, 1, 2, 256),
+    (32, 32, 32, 128, 1, 2, 2, 1, 0, 2, 256),
 ]
-# workgroups per compute unit of the persistent grouped-FFN launch (both phases)
+# workgroups per compute unit of the streaming class's persistent launch
 WG_PER_CU = (2, 2)
 
 
 def cost_constants(hidden: int, inter: int, num_cus: int) -> dict:
-    """b, q1, q2, S1, S2 per configuration, per the definitions in include/moe.h."""
-    grid = min(num_cus * WG_PER_CU[0], MAX_GRID)
+    """b, q1, q2, S1, S2 per configuration, per the definitions in include/moe.h:
+    S = the persistent grid of the configuration's class."""
+    grid = [min(num_cus * m[9], MAX_GRID) for m in MENU]
     return {
         "b": [m[0] for m in MENU],
-        "q1": [inter // m[1] for m in MENU],
-        "q2": [(hidden // m[2]) * m[7] for m in MENU],
-        "S1": [grid] * len(MENU),
-        "S2": [grid] * len(MENU),
+        "q1": [-(-inter // m[1]) for m in MENU],
+        "q2": [-(-hidden // m[2]) * m[7] for m in MENU],
+        "S1": grid,
+        "S2": grid,
     }
 
 
@@ -32,10 +41,11 @@ MAX_GRID = 512
 
 
 def splits_tail(r: int, grid: int, stream: int, full_rounds: int = 0) -> bool:
-    """Whether a phase's last r (< grid) tiles are split by reduction stages across
-    the whole grid (hybrid Stream-K): for streaming configurations when fewer than
-    three quarters of the workgroups would be busy; for the cached one when the idle
-    share of an unsplit phase, (grid - r) / (grid (F + 1)), exceeds one tenth."""
+    """Whether a streaming-class phase's last r (< grid) tiles are split by
+    reduction stages across the whole grid (hybrid Stream-K): for streaming
+    configurations when fewer than three quarters of the workgroups would be busy;
+    for the cached one when the idle share of an unsplit phase,
+    (grid - r) / (grid (F + 1)), exceeds one tenth.  The wide class never splits."""
     if r <= 0:
         return False
     if stream:

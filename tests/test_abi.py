@@ -34,7 +34,7 @@ def test_binding_mirrors_names():
 
 
 def test_variant_menu_matches_spec():
-    assert moe.moe_abi_version() == 5
+    assert moe.moe_abi_version() == 6
     assert moe.moe_num_variants() == len(spec.MENU)
     for v, m in enumerate(spec.MENU):
         assert tuple(moe.moe_variant_info(v)) == m

@@ -414,7 +414,8 @@ def test_split_tail_tiles(B):
         G.say(f"  variant {v}: rel err {err:.3g}")
         for N, BN in ((I, spec.MENU[v][1]), (H, spec.MENU[v][2])):
             tiles = out["num_blocks"] * (N // BN)
-            if spec.splits_tail(tiles % grid, grid, spec.MENU[v][8], tiles // grid):
+            if spec.MENU[v][9] == spec.WG_PER_CU[0] and \
+                    spec.splits_tail(tiles % grid, grid, spec.MENU[v][8], tiles // grid):
                 split.add(v)
         first = b.y.clone()
         for _ in range(2):

@@ -67,3 +67,27 @@ def test_greedy_menu_matches_enumeration_for_one_and_two():
     assert two[0] == first and len(set(two)) == 2
     second = min((np.minimum(t[:, first], t[:, v]).sum(), v) for v in range(5) if v != first)[1]
     assert two[1] == second
+
+
+def test_served_menu_excludes_the_rest():
+    """fit() with a menu: the menu is the greedy order's head, the other
+    configurations get the off-menu prediction, and the oracle's argmin over the
+    resulting theta never picks one of them."""
+    import oracle
+    rng = np.random.default_rng(4)
+    V, El = len(spec.MENU), 16
+    cc = spec.cost_constants(2048, 768, 256)
+    loads = []
+    for i in range(30):
+        cnt = (rng.integers(0, 300, El) * (rng.random(El) < 0.7)).astype(int)
+        loads.append(dict(counts=cnt.tolist(), times_us=(rng.random(V) * 100 + 50).tolist()))
+    res = tune.fit(dict(variants=V, cost_constants=cc, loads=loads), menu_size=4)
+    assert res["menu"] == sorted(res["greedy_menu"][:4])
+    th = np.asarray(res["theta"], np.float32)
+    off = [v for v in range(V) if v not in res["menu"]]
+    assert np.all(th[off, 0] == np.float32(tune.OFF_MENU_THETA0)) and np.all(th[off, 1:] == 0)
+    assert res["menu_geomean_loss"] >= 0
+    for ld in loads:
+        v, _, _ = oracle.select(np.asarray(ld["counts"], np.int32), cc["b"], cc["q1"], cc["q2"],
+                                cc["S1"], cc["S2"], th)
+        assert v in res["menu"]
