@@ -120,19 +120,49 @@ def spearman(a, b) -> float:
     return float(np.corrcoef(ra, rb)[0, 1])
 
 
-def greedy_menu(times: np.ndarray, size: int) -> list[int]:
+def greedy_menu(times: np.ndarray, size: int, relative: bool = False) -> list[int]:
     """Greedy order of configurations: each step adds the one that most lowers the
     summed time of the loads when each load runs the best configuration chosen so
-    far (RaMP section 3.1's offline menu choice)."""
+    far (RaMP section 3.1's offline menu choice).  relative=True sums log times
+    instead, so that every fit load weighs by its relative loss (the chooser is
+    judged per load, by the geometric mean of its gaps) rather than a few long
+    loads deciding the menu."""
     times = np.asarray(times, dtype=np.float64)
+    cost = np.log(times) if relative else times
     chosen: list[int] = []
     best = np.full(times.shape[0], np.inf)
     for _ in range(min(size, times.shape[1])):
-        cand = [(np.minimum(best, times[:, v]).sum(), v) for v in range(times.shape[1]) if v not in chosen]
-        tot, v = min(cand)
+        tot, v = min((np.minimum(best, cost[:, v]).sum(), v) for v in range(times.shape[1])
+                     if v not in chosen)
         chosen.append(v)
-        best = np.minimum(best, times[:, v])
+        best = np.minimum(best, cost[:, v])
     return chosen
+
+
+def greedy_menu_served(pred: np.ndarray, times: np.ndarray, size: int) -> list[int]:
+    """Greedy served menu judged by the chooser itself: each step adds the
+    configuration that most lowers the geometric mean, over the fit loads, of the
+    time of the configuration the cost model would pick within the menu (argmin of
+    pred over the menu's entries, ties to the lower index).  RaMP section 3.1 picks
+    the menu that minimises the recorded workload's time; scoring what the fitted
+    model would serve, rather than the best entry of the menu, keeps out entries
+    the model cannot tell from one already in (equal cost-model constants)."""
+    pred = np.asarray(pred, dtype=np.float64)
+    logt = np.log(np.asarray(times, dtype=np.float64))
+    n, V = logt.shape
+    menu: list[int] = []
+    for _ in range(min(size, V)):
+        best = None
+        for v in range(V):
+            if v in menu:
+                continue
+            m = sorted(menu + [v])
+            pick = np.asarray(m)[np.argmin(pred[:, m], axis=1)]
+            obj = logt[np.arange(n), pick].mean()
+            if best is None or obj < best[0] - 1e-12:
+                best = (obj, v)
+        menu.append(best[1])
+    return menu
 
 
 # ------------------------------------------------------------------ timing -----
@@ -229,17 +259,20 @@ OFF_MENU_THETA0 = 1.0e30
 def fit(data: dict, menu_size: int | None = None) -> dict:
     """theta per configuration from collected timings, with diagnostics.
 
-    The served menu (RaMP section 3.1) is the first `menu_size` configurations of
-    the greedy order on the fit loads' forced times; the others get theta =
-    (OFF_MENU_THETA0, 0, 0, 0), which the device's argmin never picks."""
+    Every configuration's theta is fitted; the served menu (RaMP section 3.1) is
+    then `menu_size` configurations picked by greedy_menu_served on the fit loads;
+    the others get theta = (OFF_MENU_THETA0, 0, 0, 0), which the device's argmin
+    never picks."""
     V = data["variants"]
     cc = data["cost_constants"]
     F = np.stack([features(ld["counts"], cc) for ld in data["loads"]])  # [n][V][4]
     t = np.array([ld["times_us"] for ld in data["loads"]], dtype=np.float64)  # [n][V]
-    order = greedy_menu(t, V)
-    menu = sorted(order[: (menu_size or V)])
-    theta = np.stack([fit_nnls(F[:, v, :], t[:, v]) if v in menu else
-                      np.array([OFF_MENU_THETA0, 0.0, 0.0, 0.0]) for v in range(V)]).astype(np.float32)
+    order = greedy_menu(t, V, relative=True)  # best-entry order, for the record
+    theta_all = np.stack([fit_nnls(F[:, v, :], t[:, v]) for v in range(V)])
+    pred_all = np.einsum("nvk,vk->nv", F, theta_all)
+    menu = sorted(greedy_menu_served(pred_all, t, menu_size or V))
+    theta = np.stack([theta_all[v] if v in menu else np.array([OFF_MENU_THETA0, 0.0, 0.0, 0.0])
+                      for v in range(V)]).astype(np.float32)
     # diagnostics in float64 (the device's own fp32 choice is what the benchmark reports)
     pred = np.einsum("nvk,vk->nv", F, theta.astype(np.float64))
     pick = pred.argmin(axis=1)
@@ -269,20 +302,30 @@ def main(argv=None):
     ap.add_argument("--rep-loads", type=int, default=1, help="loads per (tokens, alpha)")
     ap.add_argument("--menu", type=int, default=6,
                     help="configurations in the served menu (greedy on the fit loads)")
+    ap.add_argument("--refit", action="store_true",
+                    help="no timing: refit theta and the menu from the loads stored in --out")
     args = ap.parse_args(argv)
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     os.makedirs(args.out, exist_ok=True)
     for shp in [s for s in args.shapes.split(",") if s]:
         t0 = time.perf_counter()
-        data = collect(shp, args.reps, args.rep_loads,
-                       log=lambda m: print(m, file=sys.stderr, flush=True))
+        path = os.path.join(args.out, f"{shp}.json")
+        if args.refit:  # the forced times already collected for this kernel build
+            with open(path) as f:
+                old = json.load(f)
+            if old.get("kernel_source_sha") != kernel_source_hash():
+                raise SystemExit(f"{path} was timed on another kernel build")
+            data = dict(shape=shp, cost_constants=old["cost_constants"], loads=old["loads"],
+                        variants=len(old["theta"]))
+        else:
+            data = collect(shp, args.reps, args.rep_loads,
+                           log=lambda m: print(m, file=sys.stderr, flush=True))
         res = fit(data, args.menu)
         res.update(shape=shp, kernel_source_sha=kernel_source_hash(),
                    fit_alphas=FIT_ALPHAS, fit_tokens=FIT_TOKENS[shp], fit_rep0=FIT_REP0,
                    cost_constants=data["cost_constants"], loads=data["loads"],
                    wall_s=round(time.perf_counter() - t0, 1))
-        path = os.path.join(args.out, f"{shp}.json")
         with open(path, "w") as f:
             json.dump(res, f, indent=1)
         print(f"[tune] {shp}: menu {res['menu']} (greedy order {res['greedy_menu']}, menu loss "

@@ -69,8 +69,48 @@ def test_greedy_menu_matches_enumeration_for_one_and_two():
     assert two[1] == second
 
 
+def test_served_greedy_matches_enumeration_for_one_and_two():
+    """greedy_menu_served: the first pick is the configuration with the lowest
+    geomean time when it alone is served; the second is the best pair holding the
+    first, scored by what the argmin of pred serves inside the pair."""
+    rng = np.random.default_rng(12)
+    t = rng.random((40, 6)) + 0.1
+    pred = t * (1 + 0.3 * rng.standard_normal(t.shape))
+    first = tune.greedy_menu_served(pred, t, 1)[0]
+    assert first == int(np.argmin(np.log(t).mean(axis=0)))
+    two = tune.greedy_menu_served(pred, t, 2)
+    assert two[0] == first
+
+    def served(m):
+        m = sorted(m)
+        pick = np.asarray(m)[np.argmin(pred[:, m], axis=1)]
+        return np.log(t[np.arange(len(t)), pick]).mean()
+    assert two[1] == min((served([first, v]), v) for v in range(6) if v != first)[1]
+
+
+def test_served_greedy_skips_a_configuration_the_model_cannot_serve():
+    """A configuration predicted exactly like one already in the menu (same cost
+    constants and fit) loses every tie to the lower index, so adding it serves
+    nothing: the served greedy takes the next useful one, while the best-entry
+    greedy would take it for its (unreachable) fast loads."""
+    n = 30
+    half = np.arange(n) < n // 2
+    t = np.empty((n, 4))
+    t[:, 0] = 0.5                          # best alone
+    t[:, 3] = np.where(half, 0.2, 2.0)     # fast on half the loads ...
+    t[:, 1] = np.where(half, 0.4, 1.5)
+    t[:, 2] = 1.5
+    pred = np.empty((n, 4))
+    pred[:, 0] = 0.5
+    pred[:, 3] = pred[:, 0]                # ... but indistinguishable from 0
+    pred[:, 1] = np.where(half, 0.3, 1.5)
+    pred[:, 2] = 1.5
+    assert tune.greedy_menu(t, 2, relative=True) == [0, 3]
+    assert tune.greedy_menu_served(pred, t, 2) == [0, 1]
+
+
 def test_served_menu_excludes_the_rest():
-    """fit() with a menu: the menu is the greedy order's head, the other
+    """fit() with a menu: the menu is greedy_menu_served's choice, the other
     configurations get the off-menu prediction, and the oracle's argmin over the
     resulting theta never picks one of them."""
     import oracle
@@ -82,7 +122,7 @@ def test_served_menu_excludes_the_rest():
         cnt = (rng.integers(0, 300, El) * (rng.random(El) < 0.7)).astype(int)
         loads.append(dict(counts=cnt.tolist(), times_us=(rng.random(V) * 100 + 50).tolist()))
     res = tune.fit(dict(variants=V, cost_constants=cc, loads=loads), menu_size=4)
-    assert res["menu"] == sorted(res["greedy_menu"][:4])
+    assert len(res["menu"]) == 4 and res["menu"] == sorted(set(res["menu"]))
     th = np.asarray(res["theta"], np.float32)
     off = [v for v in range(V) if v not in res["menu"]]
     assert np.all(th[off, 0] == np.float32(tune.OFF_MENU_THETA0)) and np.all(th[off, 1:] == 0)
