@@ -954,11 +954,10 @@ struct Tile {
     const int e_end = SH ? g.E_loc + g.n_shared : g.E_loc;
     const int ncol = (N + BN - 1) / BN;
     const int total = nb * ncol;
-    const int nst = K / BK;  // the caller checks K % BK == 0 and nst >= ND + 2
+    const int nst = K / BK;  // the caller checks K % (ND * BK) == 0 and nst >= 2 * ND
     const int F = total / G;
     const int nit = F + (slot < total - F * G ? 1 : 0);  // whole tiles of this workgroup
-    const int nv = nit * nst;
-    if (nv == 0) return;
+    if (nit == 0) return;
     const int tid = threadIdx.x;
     // wave coordinates in scalar registers: every row test below is then a scalar
     // branch, not an exec mask around each group of MFMAs
@@ -1073,7 +1072,7 @@ struct Tile {
     f32x4 acc[NMAT][FM][FN];
     const int lr = lane & 15, lg = lane >> 4;
     const int foff = lr * ROWB + ((lg ^ swz<C>(lr)) << 4);
-    // every row of this wave's part holds a slot: all reads first, then the MFMAs
+    // all fragment reads first, then the MFMAs
     auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
       const uint8_t* bufA = buf + wm * MW * ROWB + foff;
       const uint8_t* bufB = buf + (BM + wn * NW) * ROWB + foff;
@@ -1092,94 +1091,71 @@ struct Tile {
           for (int j = 0; j < FN; ++j)
             acc[mt][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[mt][j], acc[mt][i][j], 0, 0, 0);
     };
-    // the last row-block of an expert: 16-row groups past nvalid are skipped
-    auto compute_part = [&](const uint8_t* buf, int nvalid) __attribute__((always_inline)) {
-      const uint8_t* bufA = buf + wm * MW * ROWB + foff;
-      const uint8_t* bufB = buf + (BM + wn * NW) * ROWB + foff;
-      bf16x8 fb[NMAT][FN];
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[mt][j] = *(const bf16x8*)(bufB + (mt * BN + j * 16) * ROWB);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        if (wm * MW + i * 16 >= nvalid) continue;
-        const bf16x8 fa = *(const bf16x8*)(bufA + i * 16 * ROWB);
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[mt][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[mt][j], acc[mt][i][j], 0, 0, 0);
-      }
-    };
-
     // ---- the pipeline ----
-    // item j's metadata: fetched at step j * nst - ND - 1 and stored at step
-    // j * nst - ND (before that step's barrier), so that it is published before
-    // step j * nst - ND + 1 issues the first loads of item j; items whose first
-    // loads come earlier are described before the loop.
+    // Tile loop around a stage loop unrolled by ND, the tile's stores after it: the
+    // accumulators live across the stage loop only, so they stay in place (MFMA
+    // destination = accumulator input) and nothing spills.  Every tile has nst
+    // stages and the caller checks nst % ND == 0, so stage s of any tile sits in
+    // buffer s % ND and each unrolled step names its buffer at compile time.  The
+    // loads run ND - 1 stages ahead across tile boundaries: the last steps of tile
+    // j issue the first stages of tile j + 1, whose metadata is fetched at its
+    // stage -ND - 1 and stored at its stage -ND (before that step's barrier), so it
+    // is published before the step that issues its first loads.
     auto buf_of = [&](int u) __attribute__((always_inline)) {
       return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : b3));
     };
-    for (int j = 0; j < nit && j * nst - ND <= 0; ++j) {
-      fetch_meta(j);
-      store_meta(j);
-    }
+    fetch_meta(0);
+    store_meta(0);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < ND - 1; ++u) issue(buf_of(u));
-    int c_j = 0, c_s = 0;
-    bool after_store = false;
-    auto step = [&](int v, auto U) __attribute__((always_inline)) {
-      constexpr int u = decltype(U)::value;
-      const int jn = (v + ND + 1) / nst;  // item whose metadata this step fetches
-      if ((v + ND + 1) % nst == 0 && jn < nit && jn * nst - ND > 0) fetch_meta(jn);
-      if ((v + ND) % nst == 0 && (v + ND) / nst < nit && v + ND > ND) store_meta((v + ND) / nst);
-      // this stage's loads are the oldest but (ND - 2) stages of this wave's loads;
-      // after tile stores (counted in the same counter) wait for everything
-      if (after_store)
-        wait_vm_lgkm0<0, true>();
-      else
+    for (int j = 0; j < nit; ++j) {
+      const int* m = meta3 + (j % kMetaSlots) * META;
+      const bool live = (unsigned)__builtin_amdgcn_readfirstlane(m[BM + 1]) < (unsigned)e_end;
+      const int nvalid = __builtin_amdgcn_readfirstlane(m[BM]);
+      const bool more = j + 1 < nit;
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // One stage: wait until this stage's loads are the oldest but (ND - 2)
+      // stages of this wave's loads, barrier, issue the loads of the stage ND - 1
+      // ahead into the buffer computed in the previous step, then the MFMAs.  A
+      // wave with some valid rows runs all its MFMAs: rows with no slot were
+      // loaded with an out-of-range offset and their sums are never stored, so
+      // the accumulators see one straight-line update per stage.
+      auto step = [&](int s0, auto U, auto Cmp) __attribute__((always_inline)) {
+        constexpr int u = decltype(U)::value;
+        const int s = s0 + u;
+        if (more && s == nst - ND - 1) fetch_meta(j + 1);
+        if (more && s == nst - ND) store_meta(j + 1);
         wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
-      after_store = false;
-      issue(buf_of((u + ND - 1) % ND));  // the buffer computed in the previous step
-      const int* m = meta3 + (c_j % kMetaSlots) * META;
-      if (c_s == 0) {
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int jn2 = 0; jn2 < FN; ++jn2) acc[mt][i][jn2] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      const bool live = c_j < nit && (unsigned)m[BM + 1] < (unsigned)e_end;
-      const int nvalid = m[BM];
-      if (live && wm * MW < nvalid) {
-        if (wm * MW + MW <= nvalid)
-          compute_full(buf_of(u));
-        else
-          compute_part(buf_of(u), nvalid);
-      }
-      if (c_s == nst - 1) {
-        int rb, nt;
-        tile_rc(slot + c_j * G, nb, ncol, rb, nt);
-        if (live) {
-          store_acc(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane);
-          after_store = true;
+        issue(buf_of((u + ND - 1) % ND));
+        if constexpr (decltype(Cmp)::value) compute_full(buf_of(u));
+      };
+      // the whole-wave test is taken once per tile (two copies of the stage loop)
+      auto stages = [&](auto Cmp) __attribute__((always_inline)) {
+        for (int s0 = 0; s0 < nst; s0 += ND) {
+          step(s0, std::integral_constant<int, 0>{}, Cmp);
+          step(s0, std::integral_constant<int, 1>{}, Cmp);
+          step(s0, std::integral_constant<int, 2>{}, Cmp);
+          step(s0, std::integral_constant<int, 3>{}, Cmp);
         }
-        ++c_j;
-        c_s = 0;
-      } else {
-        ++c_s;
+      };
+      if (live && wm * MW < nvalid)
+        stages(std::true_type{});
+      else
+        stages(std::false_type{});
+      if (live) {
+        int rb, nt;
+        tile_rc(slot + j * G, nb, ncol, rb, nt);
+        store_acc(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane);
+        // the stores count in the same counter as the loads: let them finish, so
+        // the next stage's wait counts loads only
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-    };
-    // every step of the unrolled loop runs (steps past nv compute nothing and load
-    // out of range), so the compiler can count the loads in flight at each read
-    for (int v0 = 0; v0 < nv; v0 += ND) {
-      step(v0, std::integral_constant<int, 0>{});
-      step(v0 + 1, std::integral_constant<int, 1>{});
-      step(v0 + 2, std::integral_constant<int, 2>{});
-      step(v0 + 3, std::integral_constant<int, 3>{});
     }
     // every load of this workgroup has landed before it exits (the last steps'
     // loads were out of range, so this costs nothing)
@@ -1430,9 +1406,10 @@ __global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
       __shared__ __attribute__((aligned(16))) uint8_t s3[R::STAGE];
       const int K = PHASE == 1 ? g.H : g.I;
       const int slot = xcd_slot(blockIdx.x, gridDim.x);
-      if (K % R::BK == 0 && K / R::BK >= 6)
+      if (K % (4 * R::BK) == 0 && K / R::BK >= 8)
         R::template run_dma<SH, 4>(g, s0, s1, s2, s3, meta3, nb, nbr, slot, gridDim.x);
-      else  // a reduction too short for the four-stage pipeline
+      else  // a reduction too short for the four-stage pipeline, or not in whole
+            // groups of four stages
         R::template run_all<SH>(g, s0, s1, meta3, nb, nbr, slot, gridDim.x);
     } else {
       run_phase<kWideVariant, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr);
