@@ -222,6 +222,9 @@ struct FfnArgs {
 
 // ring slots of per-tile metadata (see Tile::run_all)
 constexpr int kMetaSlots = 4;
+// entries of the wide class's first-row-block-per-expert table (local plus shared
+// experts, and one past the last); more experts fall back to tile_rc's order
+constexpr int kRunTable = 1088;
 
 // slot of workgroup wg so that consecutive slots share an XCD (workgroup wg runs
 // on XCD wg % 8)
@@ -302,9 +305,10 @@ struct Tile {
   };
 
   // Tile metadata kept in LDS, in a ring of kMetaSlots slots: the BM slot ids of
-  // the tile's rows, the number of leading rows that hold a slot, and the local
-  // expert.  A slot is refilled at least one barrier after its last reader.
-  static constexpr int META = BM + 2;
+  // the tile's rows, the number of leading rows that hold a slot, the local
+  // expert, and (wide class) the tile's row-block and column tile.  A slot is
+  // refilled at least one barrier after its last reader.
+  static constexpr int META = BM + 4;
 
   // Stores one tile's sums (lane holds rows 4*(lane/16)+c, column lane%16 of each
   // 16x16 block): h = silu(gate) * up in the gate/up phase, y_slots in the down
@@ -939,8 +943,8 @@ struct Tile {
 
   template <bool SH, int ND>
   __device__ __forceinline__ static void run_dma(const FfnArgs& g, uint8_t* b0, uint8_t* b1,
-                                                 uint8_t* b2, uint8_t* b3, int* meta3, int nb,
-                                                 int nbr, int slot, int G) {
+                                                 uint8_t* b2, uint8_t* b3, int* meta3, int* pexp,
+                                                 int nb, int nbr, int slot, int G) {
     static_assert(WKIND == W_BF16 && NT == kThreadsWide && WK == 1 && KSTEPS == 1 && C == 4,
                   "the direct-load pipeline serves the wide class's bf16 tiles");
     static_assert(ND == 4, "four stage buffers");
@@ -969,11 +973,59 @@ struct Tile {
     const Wt* wmat0 = (const Wt*)(PHASE == 1 ? g.w1 : g.w2);
     const Wt* wmat1 = (const Wt*)(PHASE == 1 ? g.w3 : g.w2);
 
+    // ---- tile order: expert-major, row-block fastest ----
+    // pexp[e] (e = 0..e_end) = the first row-block of local expert e, from a pass
+    // over the block experts: the experts in (expert of block b - 1, expert of
+    // block b] start at block b (each entry written by exactly one thread).  Tile
+    // t then lies in the run of row-blocks [pexp[e], pexp[e + 1]) that holds block
+    // t / ncol, and the run's tiles go column tile by column tile, its row-blocks
+    // fastest: the G / 8 consecutive slots that share an XCD then hold every
+    // row-block of a few weight tiles, and that L2 serves each weight slice to all
+    // of its row-blocks.  Block experts out of range or not in ascending order
+    // (not what the alignment step writes) fall back to tile_rc's order.
+    auto bexp = [&](int b) __attribute__((always_inline)) {
+      return SH && b >= nbr ? g.E_loc + (b - nbr) / nbs : g.block_expert[b];
+    };
+    int bad = e_end > kRunTable - 1;
+    if (!bad) {
+      for (int b = tid; b <= nb; b += NT) {
+        const int e1 = b < nb ? bexp(b) : e_end;
+        const int e0 = b > 0 ? bexp(b - 1) : -1;
+        if ((b < nb && (unsigned)e1 >= (unsigned)e_end) || e1 < e0) {
+          bad = 1;
+        } else {
+          for (int e = e0 + 1 > 0 ? e0 + 1 : 0; e <= e1; ++e) pexp[e] = b;
+        }
+      }
+    }
+    bad = __syncthreads_or(bad);
+    auto tile_map = [&](int t, int& rb, int& nt) __attribute__((always_inline)) {
+      if (bad) {
+        tile_rc(t, nb, ncol, rb, nt);
+        return;
+      }
+      const int b = t / ncol;
+      int lo = 0, hi = e_end;  // pexp[lo] <= b < pexp[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pexp[mid] <= b)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      const int s0 = pexp[lo], n = pexp[lo + 1] - s0;
+      const int local = t - s0 * ncol;
+      nt = local / n;
+      rb = s0 + (local - nt * n);
+    };
+
     // ---- tile metadata (as run_all: a ring of kMetaSlots slots in LDS) ----
-    int ms0 = -1, ms1 = -1, me = -1;
+    int ms0 = -1, ms1 = -1, me = -1, m_rb = 0, m_nt = 0;
     auto fetch_meta = [&](int j) __attribute__((always_inline)) {
       int rb, nt;
-      tile_rc(slot + j * G, nb, ncol, rb, nt);
+      tile_map(slot + j * G, rb, nt);
+      m_rb = rb;
+      m_nt = nt;
       const int64_t row0 = (int64_t)rb * BM;
       if (SH && rb >= nbr) {
         const int t0 = ((rb - nbr) % nbs) * BM + tid;
@@ -999,7 +1051,11 @@ struct Tile {
         if (v0 && !v1) m[BM] = tid + 1;
         if (tid == 0 && !v0) m[BM] = 0;
       }
-      if (tid == 0) m[BM + 1] = me;
+      if (tid == 0) {
+        m[BM + 1] = me;
+        m[BM + 2] = m_rb;
+        m[BM + 3] = m_nt;
+      }
     };
 
     // ---- the loads of one stage ----
@@ -1023,8 +1079,8 @@ struct Tile {
     bool l_new = true;
     auto enter_load_tile = [&](int j) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
-      int rb, nt;
-      tile_rc(slot + j * G, nb, ncol, rb, nt);
+      const int rb = __builtin_amdgcn_readfirstlane(m[BM + 2]);
+      const int nt = __builtin_amdgcn_readfirstlane(m[BM + 3]);
       int e = __builtin_amdgcn_readfirstlane(m[BM + 1]);
       int n0 = nt * BN;
       const bool eok = j < nit && (unsigned)e < (unsigned)e_end;
@@ -1068,51 +1124,72 @@ struct Tile {
       }
     };
 
-    // ---- MFMAs of one stage (one 32-deep step) ----
+    // ---- accumulators and the fragment layout ----
     f32x4 acc[NMAT][FM][FN];
     const int lr = lane & 15, lg = lane >> 4;
     const int foff = lr * ROWB + ((lg ^ swz<C>(lr)) << 4);
-    // all fragment reads first, then the MFMAs
-    auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
+
+    // ---- the pipeline ----
+    // Tile loop around a stage loop unrolled by ND, the tile's stores after it: the
+    // accumulators live across the stage loop only, so they stay in place and
+    // nothing spills.  Every tile has nst stages and the caller checks
+    // nst % ND == 0, so stage s of any tile sits in buffer s % ND and each unrolled
+    // step names its buffer at compile time.  The loads run ND - 1 stages ahead
+    // across tile boundaries: the last steps of tile j issue the first stages of
+    // tile j + 1, whose metadata is fetched at its stage -ND - 1 and stored at its
+    // stage -ND (before that step's barrier), so it is published before the step
+    // that issues its first loads.
+    //
+    // Ping-pong between the two waves of each SIMD.  Waves w and w + 4 share a
+    // SIMD and hold opposite row halves (wm = 0 and 1).  Every wave runs the same
+    // steps, each two halves long: barrier, issue the loads of stage s + ND - 1
+    // and read stage s's fragments from LDS; barrier, the MFMAs of stage s.  The
+    // wm = 1 waves take one extra barrier before the first step (and the wm = 0
+    // waves one after the last), and barriers pair up by count, so the wm = 1
+    // waves run half a step behind: while one wave of a SIMD reads LDS, the other
+    // runs its MFMAs, instead of both waiting for their fragments at the start of
+    // every stage.  Waits before each barrier: every wave has its own LDS reads
+    // done (so a buffer is refilled only after all waves have read it) and its
+    // loads of the next stage that any wave reads after the barrier: stage s
+    // before the first barrier of step s for the leading waves, stage s + 1
+    // before the second barrier of step s for the trailing ones.  A wave with any
+    // valid row runs all its MFMAs (rows with no slot were loaded out of range
+    // and their sums are never stored); the all-padding test is taken per tile.
+    auto buf_of = [&](int u) __attribute__((always_inline)) {
+      return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : b3));
+    };
+    bf16x8 fb[NMAT][FN], fa[FM];
+    auto read_frags = [&](const uint8_t* buf) __attribute__((always_inline)) {
       const uint8_t* bufA = buf + wm * MW * ROWB + foff;
       const uint8_t* bufB = buf + (BM + wn * NW) * ROWB + foff;
-      bf16x8 fb[NMAT][FN], fa[FM];
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[mt][j] = *(const bf16x8*)(bufB + (mt * BN + j * 16) * ROWB);
+        for (int jn = 0; jn < FN; ++jn) fb[mt][jn] = *(const bf16x8*)(bufB + (mt * BN + jn * 16) * ROWB);
 #pragma unroll
       for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(bufA + i * 16 * ROWB);
+    };
+    auto mfmas = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[mt][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[mt][j], acc[mt][i][j], 0, 0, 0);
+          for (int jn = 0; jn < FN; ++jn)
+            acc[mt][i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[mt][jn], acc[mt][i][jn], 0, 0, 0);
     };
-    // ---- the pipeline ----
-    // Tile loop around a stage loop unrolled by ND, the tile's stores after it: the
-    // accumulators live across the stage loop only, so they stay in place (MFMA
-    // destination = accumulator input) and nothing spills.  Every tile has nst
-    // stages and the caller checks nst % ND == 0, so stage s of any tile sits in
-    // buffer s % ND and each unrolled step names its buffer at compile time.  The
-    // loads run ND - 1 stages ahead across tile boundaries: the last steps of tile
-    // j issue the first stages of tile j + 1, whose metadata is fetched at its
-    // stage -ND - 1 and stored at its stage -ND (before that step's barrier), so it
-    // is published before the step that issues its first loads.
-    auto buf_of = [&](int u) __attribute__((always_inline)) {
-      return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : b3));
-    };
+    const bool late = wm != 0;  // wave-uniform
     fetch_meta(0);
     store_meta(0);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < ND - 1; ++u) issue(buf_of(u));
+    if (late) wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
     for (int j = 0; j < nit; ++j) {
       const int* m = meta3 + (j % kMetaSlots) * META;
       const bool live = (unsigned)__builtin_amdgcn_readfirstlane(m[BM + 1]) < (unsigned)e_end;
       const int nvalid = __builtin_amdgcn_readfirstlane(m[BM]);
+      const bool run = live && wm * MW < nvalid;
       const bool more = j + 1 < nit;
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
@@ -1120,43 +1197,39 @@ struct Tile {
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // One stage: wait until this stage's loads are the oldest but (ND - 2)
-      // stages of this wave's loads, barrier, issue the loads of the stage ND - 1
-      // ahead into the buffer computed in the previous step, then the MFMAs.  A
-      // wave with some valid rows runs all its MFMAs: rows with no slot were
-      // loaded with an out-of-range offset and their sums are never stored, so
-      // the accumulators see one straight-line update per stage.
-      auto step = [&](int s0, auto U, auto Cmp) __attribute__((always_inline)) {
+      auto step = [&](int s0, auto U) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
         const int s = s0 + u;
         if (more && s == nst - ND - 1) fetch_meta(j + 1);
         if (more && s == nst - ND) store_meta(j + 1);
+        // this stage's loads are the oldest but (ND - 2) stages of this wave's loads
         wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
         issue(buf_of((u + ND - 1) % ND));
-        if constexpr (decltype(Cmp)::value) compute_full(buf_of(u));
+        read_frags(buf_of(u));
+        // the trailing waves' next stage is the oldest but (ND - 2) of theirs now;
+        // the leading waves need nothing new here
+        if (late)
+          wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
+        else
+          wait_vm_lgkm0<(ND - 1) * kDmaInstr, true>();
+        if (run) mfmas();
       };
-      // the whole-wave test is taken once per tile (two copies of the stage loop)
-      auto stages = [&](auto Cmp) __attribute__((always_inline)) {
-        for (int s0 = 0; s0 < nst; s0 += ND) {
-          step(s0, std::integral_constant<int, 0>{}, Cmp);
-          step(s0, std::integral_constant<int, 1>{}, Cmp);
-          step(s0, std::integral_constant<int, 2>{}, Cmp);
-          step(s0, std::integral_constant<int, 3>{}, Cmp);
-        }
-      };
-      if (live && wm * MW < nvalid)
-        stages(std::true_type{});
-      else
-        stages(std::false_type{});
+      for (int s0 = 0; s0 < nst; s0 += ND) {
+        step(s0, std::integral_constant<int, 0>{});
+        step(s0, std::integral_constant<int, 1>{});
+        step(s0, std::integral_constant<int, 2>{});
+        step(s0, std::integral_constant<int, 3>{});
+      }
       if (live) {
-        int rb, nt;
-        tile_rc(slot + j * G, nb, ncol, rb, nt);
+        const int rb = __builtin_amdgcn_readfirstlane(m[BM + 2]);
+        const int nt = __builtin_amdgcn_readfirstlane(m[BM + 3]);
         store_acc(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane);
         // the stores count in the same counter as the loads: let them finish, so
         // the next stage's wait counts loads only
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
     }
+    if (!late) wait_vm_lgkm0<0, true>();  // the barrier the trailing waves took first
     // every load of this workgroup has landed before it exits (the last steps'
     // loads were out of range, so this costs nothing)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1367,7 +1440,7 @@ __device__ __forceinline__ void report_status(const FfnArgs& g, int v, int nbr) 
 template <int PHASE, int WKIND, bool SH>
 __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int meta3[kMetaSlots * (kMaxBlockM + 2)];
+  __shared__ int meta3[kMetaSlots * (kMaxBlockM + 4)];
   const int v = *g.variant;
   report_status<SH>(g, v, *g.num_blocks);
   int nb, nbr;
@@ -1391,7 +1464,7 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
 template <int PHASE, int WKIND, bool SH>
 __global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int meta3[kMetaSlots * (kMaxBlockM + 2)];
+  __shared__ int meta3[kMetaSlots * (kMaxBlockM + 4)];
   const int v = *g.variant;
   int nb, nbr;
   if (!block_counts<SH>(g, v, nb, nbr)) return;
@@ -1404,10 +1477,11 @@ __global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
       __shared__ __attribute__((aligned(16))) uint8_t s1[R::STAGE];
       __shared__ __attribute__((aligned(16))) uint8_t s2[R::STAGE];
       __shared__ __attribute__((aligned(16))) uint8_t s3[R::STAGE];
+      __shared__ int pexp[kRunTable];
       const int K = PHASE == 1 ? g.H : g.I;
       const int slot = xcd_slot(blockIdx.x, gridDim.x);
       if (K % (4 * R::BK) == 0 && K / R::BK >= 8)
-        R::template run_dma<SH, 4>(g, s0, s1, s2, s3, meta3, nb, nbr, slot, gridDim.x);
+        R::template run_dma<SH, 4>(g, s0, s1, s2, s3, meta3, pexp, nb, nbr, slot, gridDim.x);
       else  // a reduction too short for the four-stage pipeline, or not in whole
             // groups of four stages
         R::template run_all<SH>(g, s0, s1, meta3, nb, nbr, slot, gridDim.x);
