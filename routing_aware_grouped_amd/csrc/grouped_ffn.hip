@@ -140,19 +140,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // LDS row swizzle in 16-byte units for rows of C chunks: chunk c of row r sits at
-// c ^ ((r >> 2) & 3) for 64-byte rows, c ^ (r & 7) for 128-byte rows and
-// c ^ (r & 15) for longer ones.  A quarter wave's MFMA fragment read (16
-// consecutive rows, one logical chunk) then hits every one of the 64 banks once:
-// 64-byte rows cover the banks four rows at a time and the four such groups take
-// four distinct chunks, 128-byte rows alternate between the two bank halves and
-// take 8 distinct chunks each, longer rows all start on bank 0 and take 16
-// distinct chunks.  A stage write covers each row's chunks once.
-// Measured with rocprofv3 on gfx950 for 128-byte rows: a fragment read costs 4
-// LDS cycles and no bank-conflict cycles, against 8 cycles (half of them
-// conflicts) for the swizzle c ^ ((r & 7) ^ ((r >> 3) & 1)) and 16 without one.
+// c ^ ((r >> 1) & 3) for 64-byte rows, c ^ (r & 7) for 128-byte rows and
+// c ^ (r & 15) for longer ones.  A stage write covers each row's chunks once.
+// The choice is measured, not derived: with rocprofv3 on gfx950, fragment reads
+// (ds_read_b128, 16 consecutive rows per quarter wave, one logical chunk) show no
+// bank-conflict cycles with these swizzles.  For 64-byte rows the swizzles on
+// row bits 2-3 or 0-1, or none, double the LDS cycles of a read (half of them
+// conflicts); for 256-byte rows c ^ ((r >> 1) & 15) does the same and no swizzle
+// makes 87% of the cycles conflicts.
 template <int C>
 __device__ __forceinline__ int swz(int row) {
-  return C == 4 ? (row >> 2) & 3 : row & (C >= 16 ? 15 : 7);
+  return C == 4 ? (row >> 1) & 3 : row & (C >= 16 ? 15 : 7);
 }
 
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
@@ -1063,7 +1061,7 @@ struct Tile {
     // buffer: row (i * NT + tid) / 4, physical chunk tid % 4, which holds logical
     // chunk c = (tid % 4) ^ swz(row) (the swizzle of read_frag).  Instructions 0-1
     // take A rows 0-255, 2-3 weight rows 0-255 (gate/up: W1 then W3; down: W2).
-    const int c_log = (tid & 3) ^ ((tid >> 4) & 3);
+    const int c_log = (tid & 3) ^ ((tid >> 3) & 3);  // swz<4> of row i * NT / 4 + tid / 4
     const uint32_t a_bytes = PHASE == 1 ? (uint32_t)Btok * (uint32_t)K * ASZ
                                         : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
