@@ -399,7 +399,8 @@ def sweep_shape(torch, np, synth, L, T, shape, V, reps, density="grid"):
                       [r["us_per_variant"][v] for r in out for v in menu])
     # gap to the best served-menu configuration: the chooser's own error, apart
     # from what the menu leaves out
-    mgaps = [max(r["us"] / min(r["us_per_variant"][v] for v in menu) - 1.0, 0.0) for r in out]
+    mgaps = [max(r["us_per_variant"][r["variant"]] / min(r["us_per_variant"][v] for v in menu) - 1.0, 0.0)
+             for r in out]
     worst = max(out, key=lambda r: r["gap_to_exhaustive"])
     chooser = dict(geomean_gap=round(math.exp(statistics.fmean([math.log1p(x) for x in gaps])) - 1, 4),
                    worst_gap=round(max(gaps), 4),
@@ -546,9 +547,11 @@ def main():
     else:
         achieved, peak, unit = w["gate_up_flops"] / t_gu / 1e12, gu_peak / 1e12, "TFLOP/s"
     wl_key = f"{args.shape}:B{args.tokens}:a{args.alpha:g}:v{head['variant']}"
+    # the chosen configuration's class: 512-thread workgroups run in the wide kernel
+    gu_kernel = "ffn_wide_kernel" if moe.moe_variant_info(head["variant"])[10] == 512 else "ffn_kernel"
     roofline = dict(bound=bound, achieved=round(achieved, 2), peak=round(peak, 1), unit=unit,
                     frac=round(achieved / peak, 4), traffic=measured_traffic(wl_key),
-                    kernel="ffn_kernel<1,*> (moe_grouped_gate_up)",
+                    kernel=f"{gu_kernel}<1,*> (moe_grouped_gate_up)",
                     alg_bytes=int(w["gate_up_bytes"]), alg_flops=int(w["gate_up_flops"]),
                     avg_launch_us=round(seg["grouped_gate_up"], 3))
 
