@@ -1284,8 +1284,11 @@ struct Tile {
       }
     };
     const int npieces = Ut >= G ? w1 - w0 + 1 : nst;
-    f32x4 acc[NMAT][FM][FN];
-    auto load_piece = [&](int q, bool add) __attribute__((always_inline)) {
+    // A piece's fragments are loaded into their own registers, one piece ahead of
+    // the additions: all of a piece's loads are in flight together, instead of one
+    // wait per 16-byte load.  The pieces are still added in reduction order.
+    f32x4 acc[NMAT][FM][FN], nxt[NMAT][FM][FN];
+    auto fetch_piece = [&](int q) __attribute__((always_inline)) {
       int w, pc;
       piece_of(q, w, pc);
       const float* src = g.part + ((int64_t)w * 2 + pc) * PIECE + (wm * WN + wn) * NFRAG * 256;
@@ -1294,12 +1297,10 @@ struct Tile {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int jn = 0; jn < FN; ++jn) {
-            const f32x4 v = *(const f32x4*)(src + (((mt * FM + i) * FN + jn) * 64 + lane) * 4);
-            acc[mt][i][jn] = add ? acc[mt][i][jn] + v : v;
-          }
+          for (int jn = 0; jn < FN; ++jn)
+            nxt[mt][i][jn] = *(const f32x4*)(src + (((mt * FM + i) * FN + jn) * 64 + lane) * 4);
     };
-    if (act && wk == 0) load_piece(0, false);
+    if (act && wk == 0) fetch_piece(0);
     if (SH && rb >= nbr) {  // a shared expert's row-block (see run_all)
       const int Btok = g.slots / g.k;
       const int nbs = (Btok + BM - 1) / BM;
@@ -1317,7 +1318,29 @@ struct Tile {
     }
     __syncthreads();
     if (!act || wk != 0) return;
-    for (int q = 1; q < npieces; ++q) load_piece(q, true);
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = nxt[mt][i][jn];
+    if (npieces > 1) fetch_piece(1);
+    for (int q = 1; q < npieces; ++q) {
+      f32x4 cur[NMAT][FM][FN];
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) cur[mt][i][jn] = nxt[mt][i][jn];
+      if (q + 1 < npieces) fetch_piece(q + 1);
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = acc[mt][i][jn] + cur[mt][i][jn];
+    }
     store_acc(g, acc, meta, row0, n0, wm, wn, lane);
   }
 };
