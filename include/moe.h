@@ -264,10 +264,16 @@ moe_status moe_quant_act(const moe_problem* p, const void* x, uint8_t* xq, float
  * [rows_max][H] (act dtype).  workspace: >= workspace_bytes, 256-byte aligned;
  * holds h and the fp32 partial sums of the tiles that a phase's last round splits
  * across workgroups.  The call enqueues, for the gate/up phase and then the down
- * phase (moe_grouped_gate_up followed by moe_grouped_down), one launch of a
- * persistent polymorphic kernel and one of its fix-up kernel, which adds the
- * split tiles' partial sums; each reads *variant and *num_blocks from device
- * memory, so every compiled configuration runs under one fixed launch shape. */
+ * phase (moe_grouped_gate_up followed by moe_grouped_down), two launches of
+ * persistent polymorphic kernels, one per occupancy class of the compiled
+ * configurations (2 workgroups of 256 threads per CU; 1 of 512): each runs the
+ * chosen configuration if it belongs to its class, and the second also adds the
+ * partial sums of the tiles the first class split.  With bf16 weights and
+ * activations the down phase adds a third launch when the problem's row-block
+ * bound lets the 512-thread configuration split its last round (more tiles than
+ * one round of its grid): it adds that configuration's split tiles.  Every launch
+ * reads *variant and *num_blocks from device memory, so every compiled
+ * configuration runs under one fixed launch shape. */
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
                            const void* w2, const float* s1, const float* s3, const float* s2,
                            const int32_t* sorted_slots, const int32_t* block_expert,

@@ -939,6 +939,72 @@ struct Tile {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N_) : "memory");
   }
 
+  // ---- the wide class's tile order and tail split ----
+  // pexp[e] (e = 0..e_end) = the first row-block of local expert e, from a pass
+  // over the block experts: the experts in (expert of block b - 1, expert of
+  // block b] start at block b (each entry written by exactly one thread).  Tile t
+  // then lies in the run of row-blocks [pexp[e], pexp[e + 1]) that holds block
+  // t / ncol, and the run's tiles go column tile by column tile, its row-blocks
+  // fastest: the G / 8 consecutive slots that share an XCD then hold every
+  // row-block of a few weight tiles, and that L2 serves each weight slice to all
+  // of its row-blocks.  Block experts out of range or not in ascending order (not
+  // what the alignment step writes) fall back to tile_rc's order: the return
+  // value is then nonzero.  Every thread of the workgroup calls this (barrier).
+  template <bool SH>
+  __device__ __forceinline__ static int expert_runs(const FfnArgs& g, int* pexp, int nb, int nbr,
+                                                   int nbs, int e_end) {
+    auto bexp = [&](int b) __attribute__((always_inline)) {
+      return SH && b >= nbr ? g.E_loc + (b - nbr) / nbs : g.block_expert[b];
+    };
+    int bad = e_end > kRunTable - 1;
+    if (!bad) {
+      for (int b = threadIdx.x; b <= nb; b += NT) {
+        const int e1 = b < nb ? bexp(b) : e_end;
+        const int e0 = b > 0 ? bexp(b - 1) : -1;
+        if ((b < nb && (unsigned)e1 >= (unsigned)e_end) || e1 < e0) {
+          bad = 1;
+        } else {
+          for (int e = e0 + 1 > 0 ? e0 + 1 : 0; e <= e1; ++e) pexp[e] = b;
+        }
+      }
+    }
+    return __syncthreads_or(bad);
+  }
+  __device__ __forceinline__ static void tile_map(const int* pexp, int bad, int e_end, int t, int nb,
+                                                  int ncol, int& rb, int& nt) {
+    if (bad) {
+      tile_rc(t, nb, ncol, rb, nt);
+      return;
+    }
+    const int b = t / ncol;
+    int lo = 0, hi = e_end;  // pexp[lo] <= b < pexp[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pexp[mid] <= b)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int s0 = pexp[lo], n = pexp[lo + 1] - s0;
+    const int local = t - s0 * ncol;
+    nt = local / n;
+    rb = s0 + (local - nt * n);
+  }
+  // Tail split of the wide class's down phase (hybrid Stream-K): after F >= 1 full
+  // rounds, a last round of r <= G / 2 tiles would leave most of the grid idle
+  // for a whole tile of the longest reduction in the layer.  Each tail tile is
+  // then cut into P pieces of whole four-stage groups, one piece per workgroup
+  // (workgroup slot w < r * P takes piece w % P of tail tile w / P), so that
+  // every stage loop still starts on buffer 0 and each workgroup leaves at most
+  // one partial tile.  Pieces hold at least two groups (the next item's metadata
+  // is fetched five stages before its first load).  Returns P, or 0: no split.
+  __device__ __forceinline__ static int wide_pieces(int r, int G, int F, int nst) {
+    if (PHASE != 2 || F < 1 || r <= 0 || 2 * r > G || (int64_t)G * PIECE > kPartBytes / 4) return 0;
+    int P = G / r;
+    if (P > nst / 8) P = nst / 8;
+    return P >= 2 ? P : 0;
+  }
+
   template <bool SH, int ND>
   __device__ __forceinline__ static void run_dma(const FfnArgs& g, uint8_t* b0, uint8_t* b1,
                                                  uint8_t* b2, uint8_t* b3, int* meta3, int* pexp,
@@ -958,8 +1024,22 @@ struct Tile {
     const int total = nb * ncol;
     const int nst = K / BK;  // the caller checks K % (ND * BK) == 0 and nst >= 2 * ND
     const int F = total / G;
-    const int nit = F + (slot < total - F * G ? 1 : 0);  // whole tiles of this workgroup
+    const int r = total - F * G;
+    // work items: whole tiles slot, slot + G, ..., then at most one tail piece
+    const int P = wide_pieces(r, G, F, nst);
+    const int nwhole = F + (P == 0 && slot < r ? 1 : 0);
+    const bool has_piece = P > 0 && slot < r * P;
+    const int nit = nwhole + (has_piece ? 1 : 0);
     if (nit == 0) return;
+    const int ngr = nst / ND;
+    const int pq = has_piece ? slot % P : 0;
+    const int psb = has_piece ? ND * (pq * ngr / P) : 0;
+    const int pse = has_piece ? ND * ((pq + 1) * ngr / P) : nst;
+    auto item_tile = [&](int j) __attribute__((always_inline)) {
+      return j < nwhole ? slot + j * G : F * G + (has_piece ? slot / P : 0);
+    };
+    auto item_sb = [&](int j) __attribute__((always_inline)) { return j == nwhole ? psb : 0; };
+    auto item_se = [&](int j) __attribute__((always_inline)) { return j == nwhole ? pse : nst; };
     const int tid = threadIdx.x;
     // wave coordinates in scalar registers: every row test below is then a scalar
     // branch, not an exec mask around each group of MFMAs
@@ -971,57 +1051,14 @@ struct Tile {
     const Wt* wmat0 = (const Wt*)(PHASE == 1 ? g.w1 : g.w2);
     const Wt* wmat1 = (const Wt*)(PHASE == 1 ? g.w3 : g.w2);
 
-    // ---- tile order: expert-major, row-block fastest ----
-    // pexp[e] (e = 0..e_end) = the first row-block of local expert e, from a pass
-    // over the block experts: the experts in (expert of block b - 1, expert of
-    // block b] start at block b (each entry written by exactly one thread).  Tile
-    // t then lies in the run of row-blocks [pexp[e], pexp[e + 1]) that holds block
-    // t / ncol, and the run's tiles go column tile by column tile, its row-blocks
-    // fastest: the G / 8 consecutive slots that share an XCD then hold every
-    // row-block of a few weight tiles, and that L2 serves each weight slice to all
-    // of its row-blocks.  Block experts out of range or not in ascending order
-    // (not what the alignment step writes) fall back to tile_rc's order.
-    auto bexp = [&](int b) __attribute__((always_inline)) {
-      return SH && b >= nbr ? g.E_loc + (b - nbr) / nbs : g.block_expert[b];
-    };
-    int bad = e_end > kRunTable - 1;
-    if (!bad) {
-      for (int b = tid; b <= nb; b += NT) {
-        const int e1 = b < nb ? bexp(b) : e_end;
-        const int e0 = b > 0 ? bexp(b - 1) : -1;
-        if ((b < nb && (unsigned)e1 >= (unsigned)e_end) || e1 < e0) {
-          bad = 1;
-        } else {
-          for (int e = e0 + 1 > 0 ? e0 + 1 : 0; e <= e1; ++e) pexp[e] = b;
-        }
-      }
-    }
-    bad = __syncthreads_or(bad);
-    auto tile_map = [&](int t, int& rb, int& nt) __attribute__((always_inline)) {
-      if (bad) {
-        tile_rc(t, nb, ncol, rb, nt);
-        return;
-      }
-      const int b = t / ncol;
-      int lo = 0, hi = e_end;  // pexp[lo] <= b < pexp[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pexp[mid] <= b)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      const int s0 = pexp[lo], n = pexp[lo + 1] - s0;
-      const int local = t - s0 * ncol;
-      nt = local / n;
-      rb = s0 + (local - nt * n);
-    };
+    // ---- tile order: expert-major, row-block fastest (expert_runs) ----
+    const int bad = expert_runs<SH>(g, pexp, nb, nbr, nbs, e_end);
 
     // ---- tile metadata (as run_all: a ring of kMetaSlots slots in LDS) ----
     int ms0 = -1, ms1 = -1, me = -1, m_rb = 0, m_nt = 0;
     auto fetch_meta = [&](int j) __attribute__((always_inline)) {
       int rb, nt;
-      tile_map(slot + j * G, rb, nt);
+      tile_map(pexp, bad, e_end, item_tile(j), nb, ncol, rb, nt);
       m_rb = rb;
       m_nt = nt;
       const int64_t row0 = (int64_t)rb * BM;
@@ -1073,7 +1110,7 @@ struct Tile {
       l_boff[i] = (uint32_t)(rr * K + c_log * 8) * WSZ;
     }
     __amdgpu_buffer_rsrc_t l_b_rsrc[2];
-    int l_j = 0, l_s = 0;
+    int l_j = 0, l_s = item_sb(0), l_se = item_se(0);
     bool l_new = true;
     auto enter_load_tile = [&](int j) __attribute__((always_inline)) {
       const int* m = meta3 + (j % kMetaSlots) * META;
@@ -1115,9 +1152,10 @@ struct Tile {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(l_b_rsrc[NMAT == 2 ? i - 2 : 0], dst, 16,
                                                    l_boff[i - 2], soff, 0, 0);
       }
-      if (++l_s == nst) {  // past the last tile the offsets are out of range
+      if (++l_s == l_se) {  // past the last item the offsets are out of range
         ++l_j;
-        l_s = 0;
+        l_s = item_sb(l_j);
+        l_se = item_se(l_j);
         l_new = true;
       }
     };
@@ -1185,6 +1223,7 @@ struct Tile {
     if (late) wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
     for (int j = 0; j < nit; ++j) {
       const int* m = meta3 + (j % kMetaSlots) * META;
+      const int sb = item_sb(j), se = item_se(j);
       const bool live = (unsigned)__builtin_amdgcn_readfirstlane(m[BM + 1]) < (unsigned)e_end;
       const int nvalid = __builtin_amdgcn_readfirstlane(m[BM]);
       const bool run = live && wm * MW < nvalid;
@@ -1198,8 +1237,8 @@ struct Tile {
       auto step = [&](int s0, auto U) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
         const int s = s0 + u;
-        if (more && s == nst - ND - 1) fetch_meta(j + 1);
-        if (more && s == nst - ND) store_meta(j + 1);
+        if (more && s == se - ND - 1) fetch_meta(j + 1);
+        if (more && s == se - ND) store_meta(j + 1);
         // this stage's loads are the oldest but (ND - 2) stages of this wave's loads
         wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
         issue(buf_of((u + ND - 1) % ND));
@@ -1212,16 +1251,29 @@ struct Tile {
           wait_vm_lgkm0<(ND - 1) * kDmaInstr, true>();
         if (run) mfmas();
       };
-      for (int s0 = 0; s0 < nst; s0 += ND) {
+      for (int s0 = sb; s0 < se; s0 += ND) {
         step(s0, std::integral_constant<int, 0>{});
         step(s0, std::integral_constant<int, 1>{});
         step(s0, std::integral_constant<int, 2>{});
         step(s0, std::integral_constant<int, 3>{});
       }
       if (live) {
-        const int rb = __builtin_amdgcn_readfirstlane(m[BM + 2]);
-        const int nt = __builtin_amdgcn_readfirstlane(m[BM + 3]);
-        store_acc(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane);
+        if (j < nwhole) {
+          const int rb = __builtin_amdgcn_readfirstlane(m[BM + 2]);
+          const int nt = __builtin_amdgcn_readfirstlane(m[BM + 3]);
+          store_acc(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane);
+        } else {
+          // this workgroup's piece: its fp32 sums in MFMA fragment order, 16 bytes
+          // per lane, wave-contiguous (wide_fixup adds the pieces)
+          float* dst = g.part + (int64_t)slot * PIECE + wave * NFRAG * 256;
+#pragma unroll
+          for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int jn = 0; jn < FN; ++jn)
+                *(f32x4*)(dst + (((mt * FM + i) * FN + jn) * 64 + lane) * 4) = acc[mt][i][jn];
+        }
         // the stores count in the same counter as the loads: let them finish, so
         // the next stage's wait counts loads only
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1231,6 +1283,73 @@ struct Tile {
     // every load of this workgroup has landed before it exits (the last steps'
     // loads were out of range, so this costs nothing)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // The fix-up of the wide class's split tail tile tq (see wide_pieces): adds its
+  // P pieces in reduction order (piece q, workgroup slot tq * P + q, holds stages
+  // [4 (q ngr / P), 4 ((q + 1) ngr / P)) ) and stores the tile.  Each of the eight
+  // waves adds its own fragment region, half of it at a time, with all of a
+  // piece's loads for that half in flight together.
+  template <bool SH>
+  __device__ __forceinline__ static void wide_fixup(const FfnArgs& g, int* meta, int* pexp, int nb,
+                                                    int nbr, int G, int tq) {
+    const int N = PHASE == 1 ? g.I : g.H;
+    const int K = PHASE == 1 ? g.H : g.I;
+    const int ncol = (N + BN - 1) / BN;
+    const int total = nb * ncol;
+    const int nst = K / BK;
+    const int F = total / G;
+    const int r = total - F * G;
+    const int P = wide_pieces(r, G, F, nst);
+    if (P == 0 || tq >= r) return;  // uniform over the workgroup
+    const int Btok = g.slots / g.k;
+    const int nbs = SH ? (Btok + BM - 1) / BM : 1;
+    const int slot_end = SH ? g.slots + Btok : g.slots;
+    const int e_end = SH ? g.E_loc + g.n_shared : g.E_loc;
+    const int bad = expert_runs<SH>(g, pexp, nb, nbr, nbs, e_end);
+    int rb, nt;
+    tile_map(pexp, bad, e_end, F * G + tq, nb, ncol, rb, nt);
+    const int e = SH && rb >= nbr ? g.E_loc + (rb - nbr) / nbs : g.block_expert[rb];
+    if ((unsigned)e >= (unsigned)e_end) return;  // uniform: the pieces were not stored
+    const int tid = threadIdx.x;
+    if (tid < BM) {
+      int sl;
+      if (SH && rb >= nbr) {
+        const int t0 = ((rb - nbr) % nbs) * BM + tid;
+        sl = t0 < Btok ? g.slots + t0 : -1;
+      } else {
+        sl = g.sorted_slots[(int64_t)rb * BM + tid];
+      }
+      meta[tid] = sl >= 0 && sl < slot_end ? sl : -1;
+    }
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wn = wave % WN, wm = wave / WN;
+    f32x4 acc[NMAT][FM][FN];
+    constexpr int FH = FM / 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      for (int q = 0; q < P; ++q) {
+        const float* src = g.part + (int64_t)(tq * P + q) * PIECE + wave * NFRAG * 256;
+        f32x4 v[NMAT][FH][FN];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int i = 0; i < FH; ++i)
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn)
+              v[mt][i][jn] = *(const f32x4*)(src + (((mt * FM + h * FH + i) * FN + jn) * 64 + lane) * 4);
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int i = 0; i < FH; ++i)
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn)
+              acc[mt][h * FH + i][jn] = q == 0 ? v[mt][i][jn] : acc[mt][h * FH + i][jn] + v[mt][i][jn];
+      }
+    }
+    store_acc(g, acc, meta, (int64_t)rb * BM, nt * BN, wm, wn, lane);
   }
 
   // The fix-up of tail tile tq (the tile F * G + tq of the schedule in run_all):
@@ -1526,14 +1645,48 @@ __global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
   }
 }
 
+// The fix-up launch of the wide class's split down-phase tail (Tile::wide_fixup):
+// one 512-thread workgroup per possible split tile (at most half the wide grid).
+// It follows the wide launch on the stream, so the pieces are complete.
+template <int PHASE, bool SH>
+__global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_fixup_kernel(FfnArgs g, int grid_wide) {
+  __shared__ int meta[kMaxBlockM + 4];
+  __shared__ int pexp[kRunTable];
+  const int v = *g.variant;
+  if (v != kWideVariant) return;
+  int nb, nbr;
+  if (!block_counts<SH>(g, v, nb, nbr)) return;
+  using R = typename Cfg<kWideVariant, PHASE, W_BF16>::R;
+  const int K = PHASE == 1 ? g.H : g.I;
+  if (K % (4 * R::BK) != 0 || K / R::BK < 8) return;  // the register-staged path never splits
+  R::template wide_fixup<SH>(g, meta, pexp, nb, nbr, grid_wide, blockIdx.x);
+}
+
+// Whether the wide class can split the down phase's tail for this problem: the
+// row-block count of its BLOCK_M is at most ceil(slots / BM) + min(E_loc, slots)
+// (one partial block per active expert) plus the shared experts' blocks, and a
+// split needs more tiles than one round.  Small problems skip the launch.
+inline bool wide_split_possible(const FfnArgs& g, int grid_wide) {
+  using R = Cfg<kWideVariant, 2, W_BF16>::R;
+  const int64_t bm = kVariants[kWideVariant].bm;
+  if (g.I % (4 * R::BK) != 0 || g.I / R::BK < 8) return false;
+  const int64_t slots = g.slots;
+  int64_t nb = (slots + bm - 1) / bm + (g.E_loc < slots ? g.E_loc : slots);
+  if (nb > g.rows_max / bm) nb = g.rows_max / bm;
+  if (g.n_shared > 0) nb += (int64_t)g.n_shared * ((slots / g.k + bm - 1) / bm);
+  const int64_t bn = kVariants[kWideVariant].bn2;
+  const int64_t ncol = (g.H + bn - 1) / bn;
+  return nb * ncol > grid_wide && (int64_t)grid_wide * R::PIECE <= kPartBytes / 4;
+}
+
 template <int PHASE, int WKIND, bool SH>
 hipError_t launch_phase_sh(const FfnArgs& g, int grid_wide, hipStream_t s) {
-  constexpr int meta_bytes = kMetaSlots * (kMaxBlockM + 2) * 4;
+  constexpr int meta_bytes = kMetaSlots * (kMaxBlockM + 4) * 4;
   constexpr int lds = lds_bytes_stream<PHASE, WKIND>();
   static_assert((lds + meta_bytes) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
   constexpr int ldsw = lds_bytes_wide<PHASE, WKIND>();
   constexpr int ldsw_static = WKIND == W_BF16 ? 4 * Cfg<kWideVariant, PHASE, W_BF16>::R::STAGE : 0;
-  static_assert(ldsw + ldsw_static + meta_bytes <= 160 * 1024,
+  static_assert(ldsw + ldsw_static + meta_bytes + kRunTable * 4 <= 160 * 1024,
                 "LDS budget of one wide workgroup per CU");
   hipError_t e = opt_in_lds((const void*)ffn_kernel<PHASE, WKIND, SH>, lds);
   if (e != hipSuccess) return e;
@@ -1543,7 +1696,15 @@ hipError_t launch_phase_sh(const FfnArgs& g, int grid_wide, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   ffn_wide_kernel<PHASE, WKIND, SH><<<grid_wide, kThreadsWide, ldsw, s>>>(g);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (PHASE == 2 && WKIND == W_BF16) {
+    if (wide_split_possible(g, grid_wide)) {
+      ffn_wide_fixup_kernel<PHASE, SH><<<(grid_wide + 1) / 2, kThreadsWide, 0, s>>>(g, grid_wide);
+      e = hipGetLastError();
+    }
+  }
+  return e;
 }
 
 // the launch with shared experts is a separate instance, so that the routed-only

@@ -51,3 +51,34 @@ def splits_tail(r: int, grid: int, stream: int, full_rounds: int = 0) -> bool:
     if stream:
         return 4 * r < 3 * grid
     return 10 * (grid - r) > grid * (full_rounds + 1)
+
+
+# The wide configuration (512-thread workgroups): BLOCK_M 256, BLOCK_N 256 in the
+# down phase, 32-deep stages.  Its down phase splits the last round's tiles
+# (include/moe.h, moe_grouped_down): after F >= 1 full rounds of the wide grid, a
+# tail of 0 < r <= grid / 2 tiles is cut into P = min(grid // r, nst // 8) pieces
+# per tile (no split when P < 2), nst = I / 32 stages per tile, which must be a
+# multiple of 4 and at least 8.
+WIDE = next(v for v, m in enumerate(MENU) if m[10] == 512)
+
+
+def wide_pieces(total: int, grid: int, nst: int) -> int:
+    F, r = divmod(total, grid)
+    if F < 1 or r <= 0 or 2 * r > grid or nst % 4 or nst < 8:
+        return 0
+    P = min(grid // r, nst // 8)
+    return P if P >= 2 else 0
+
+
+def expert_major_tile(t: int, block_expert, ncol: int):
+    """(row-block, column tile) of the wide configuration's tile t: the row-blocks
+    of one expert form a run, and a run's tiles go column tile by column tile with
+    its row-blocks fastest (block experts ascending, as the alignment step writes
+    them)."""
+    be = list(block_expert)
+    b = t // ncol
+    e = be[b]
+    s0 = be.index(e)
+    n = sum(1 for x in be if x == e)
+    local = t - s0 * ncol
+    return s0 + local % n, local // n
