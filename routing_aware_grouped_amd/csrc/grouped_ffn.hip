@@ -302,6 +302,15 @@ struct Tile {
     float xs, ws;  // FP8 activation path: one x scale and one weight scale
   };
 
+  // The LDS swizzle of this tile's rows: swz<C>, except for the fp8 x fp8 tiles'
+  // 128-byte rows.  Their fragment read takes two consecutive 16-byte chunks per
+  // lane, and with c ^ (r & 7) it measured a quarter of its LDS cycles in bank
+  // conflicts on gfx950; c ^ (((r & 3) << 1) | ((r >> 3) & 1)) measured none (the
+  // 256- and 512-byte rows' swizzle measured none for this read either).
+  __device__ __forceinline__ static int tswz(int row) {
+    return (FP8A && C == 8) ? (((row & 3) << 1) | ((row >> 3) & 1)) : swz<C>(row);
+  }
+
   // Tile metadata kept in LDS, in a ring of kMetaSlots slots: the BM slot ids of
   // the tile's rows, the number of leading rows that hold a slot, the local
   // expert, and (wide class) the tile's row-block and column tile.  A slot is
@@ -597,14 +606,14 @@ struct Tile {
       for (int i = 0; i < NA; ++i) {
         const int q = i * NT + tid;
         const int row = q / GCA, c = q % GCA;
-        *(u32x4*)(buf + row * ROWB + ((c ^ swz<C>(row)) << 4)) = R.a[i];
+        *(u32x4*)(buf + row * ROWB + ((c ^ tswz(row)) << 4)) = R.a[i];
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int q = i * NT + tid;
         const int c = q % GCB;
         const int row = BM + q / GCB;  // LDS row: matrices follow each other
-        const int sw = swz<C>(row);
+        const int sw = tswz(row);
         uint8_t* rp = buf + row * ROWB;
         if constexpr (FP8) {
           u32x4 o0, o1;
@@ -632,7 +641,7 @@ struct Tile {
     // immediate offsets instead of one live address per fragment.
     auto frag_off = [&](int step, int half) __attribute__((always_inline)) {
       const int c0 = (FP8A || F32) ? step * 8 + 2 * lg + half : step * 4 + lg;
-      return lr * ROWB + ((c0 ^ swz<C>(lr)) << 4);
+      return lr * ROWB + ((c0 ^ tswz(lr)) << 4);
     };
     auto read_frag = [&](const uint8_t* buf, int row16, int step, FragT& f) __attribute__((always_inline)) {
       const uint8_t* rp = buf + row16 * ROWB;
