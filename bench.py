@@ -547,8 +547,8 @@ def main():
     else:
         achieved, peak, unit = w["gate_up_flops"] / t_gu / 1e12, gu_peak / 1e12, "TFLOP/s"
     wl_key = f"{args.shape}:B{args.tokens}:a{args.alpha:g}:v{head['variant']}"
-    # the chosen configuration's class: 512-thread workgroups run in the wide kernel
-    gu_kernel = "ffn_wide_kernel" if moe.moe_variant_info(head["variant"])[10] == 512 else "ffn_kernel"
+    # the chosen configuration's class: one workgroup per CU runs in the wide kernel
+    gu_kernel = "ffn_wide_kernel" if moe.moe_variant_info(head["variant"])[9] == 1 else "ffn_kernel"
     roofline = dict(bound=bound, achieved=round(achieved, 2), peak=round(peak, 1), unit=unit,
                     frac=round(achieved / peak, 4), traffic=measured_traffic(wl_key),
                     kernel=f"{gu_kernel}<1,*> (moe_grouped_gate_up)",

@@ -171,12 +171,13 @@ int32_t moe_num_variants(void);
  *                problem uses half of it; fp8 weights are staged as bf16; in the
  *                wide class the fp32 and fp8 tiles stage twice the bytes)
  *   [4] waves along M, [5] waves along N, [6] waves splitting K inside a tile
+ *       (of the bf16 tiles: the wide class's fp32 and fp8 tiles run twice the
+ *       waves along N)
  *   [7] split-K of the down phase across tiles (1 = none)
  *   [8] 1 if weights are read with non-temporal (streaming) loads, 0 if cached
  *   [9] workgroups per compute unit of its persistent launch (its occupancy
- *       class: 2 for the 256-thread streaming class, 1 for the 512-thread wide
- *       class)
- *   [10] threads per workgroup
+ *       class: 2 for the streaming class, 1 for the wide class)
+ *   [10] threads per workgroup of the bf16 tiles, 64 x [4] x [5] x [6]
  * Errors: MOE_ERR_INVALID_ARG for v outside [0, V) or out == NULL. */
 #define MOE_VARIANT_FIELDS 11
 moe_status moe_variant_info(int32_t v, int32_t* out);
@@ -266,11 +267,12 @@ moe_status moe_quant_act(const moe_problem* p, const void* x, uint8_t* xq, float
  * across workgroups.  The call enqueues, for the gate/up phase and then the down
  * phase (moe_grouped_gate_up followed by moe_grouped_down), two launches of
  * persistent polymorphic kernels, one per occupancy class of the compiled
- * configurations (2 workgroups of 256 threads per CU; 1 of 512): each runs the
+ * configurations (2 workgroups of 256 threads per CU; 1 workgroup per CU, of 256
+ * threads for bf16 and 512 for fp32 and fp8): each runs the
  * chosen configuration if it belongs to its class, and the second also adds the
  * partial sums of the tiles the first class split.  With bf16 weights and
  * activations the down phase adds a third launch when the problem's row-block
- * bound lets the 512-thread configuration split its last round (more tiles than
+ * bound lets the one-per-CU configuration split its last round (more tiles than
  * one round of its grid): it adds that configuration's split tiles.  Every launch
  * reads *variant and *num_blocks from device memory, so every compiled
  * configuration runs under one fixed launch shape. */

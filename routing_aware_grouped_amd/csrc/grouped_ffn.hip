@@ -235,11 +235,11 @@ __device__ __forceinline__ int xcd_slot(int wg, int grid) {
 // one tile configuration of one phase
 //   BM x BN tile (BN weight rows per matrix; the gate/up phase has two matrices),
 //   ROWB = LDS bytes per tile row per stage, waves WM x WN x WK, RS register
-//   stages in flight, NT threads per workgroup (256: streaming class, two
-//   workgroups per CU; 512: wide class, one per CU).
+//   stages in flight, NT = 64 WM WN WK threads per workgroup; WIDE: the wide
+//   class (one workgroup per CU), else the streaming class (two per CU).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int WK, int ROWB, int RS, int STREAM, int PHASE, int WKIND,
-          int NT>
+          int NT, bool WIDE>
 struct Tile {
   using T = Types<WKIND>;
   using Act = typename T::Act;
@@ -277,6 +277,7 @@ struct Tile {
   static constexpr int NFRAG = NMAT * FM * FN;   // 16x16 accumulator blocks per wave
   static constexpr int PIECE = NMAT * BM * BN;   // floats of one partial tile
   static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int THREADS = NT;
   static_assert(RED_FLOATS * 4 <= STAGE, "the K-split sums reuse one stage buffer");
   static_assert(WM * WN * WK * 64 == NT, "waves must cover the workgroup");
   static_assert(FM >= 1 && FN >= 1 && MW % 16 == 0 && NW % 16 == 0, "wave tile too small");
@@ -290,8 +291,9 @@ struct Tile {
                                                                              : BN % 128 == 0) &&
                           (BN / WN) <= 128 && 128 % (BN / WN) == 0),
                 "one scale load per thread; a wave's columns share one 128-row weight block");
-  // the wide class never splits a tile, so its pieces need no workspace
-  static constexpr bool SPLITS = NT == kThreads;
+  // run_all splits the streaming class's tail tiles only (the wide class's bf16
+  // down phase splits its own way, in run_dma)
+  static constexpr bool SPLITS = !WIDE;
   static_assert(WM * WN * NFRAG * 256 == PIECE && (!SPLITS || PIECE <= kPieceMax),
                 "partial tile layout");
 
@@ -320,28 +322,55 @@ struct Tile {
   // Stores one tile's sums (lane holds rows 4*(lane/16)+c, column lane%16 of each
   // 16x16 block): h = silu(gate) * up in the gate/up phase, y_slots in the down
   // phase.  Rows without a slot (m[r] < 0) are not stored.
-  __device__ __forceinline__ static void store_acc(const FfnArgs& g, const f32x4 (&acc)[NMAT][FM][FN],
-                                                  const int* m, int64_t row0, int n0, int wm,
-                                                  int wn, int lane) {
+  // Component c of an accumulator block that inline-asm MFMAs wrote (run_dma),
+  // read by an inline-asm v_accvgpr_read (see store_rows).
+  __device__ __forceinline__ static float acc_read(const f32x4& v, int c) {
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(v[c]));
+    return x;
+  }
+  // store_rows: the same for the NI 16-row groups i0 .. i0 + NI - 1 of the wave.
+  // AGPR: the sums are in accumulation registers written by inline-asm MFMAs
+  // (run_dma); each is then read by an inline-asm v_accvgpr_read, whose "a"
+  // operand keeps every use of the sums in those registers (the compiler makes
+  // no copies of them elsewhere, e.g. all 256 at the loop exit), and volatile
+  // asm keeps each read after the MFMAs' padding.
+  template <int NI, bool AGPR = false>
+  __device__ __forceinline__ static void store_rows(const FfnArgs& g, const f32x4 (&acc)[NMAT][NI][FN],
+                                                   const int* m, int64_t row0, int n0, int wm,
+                                                   int wn, int lane, int i0) {
+    auto rd = [&](const f32x4& v, int c) __attribute__((always_inline)) {
+      if constexpr (AGPR)
+        return acc_read(v, c);
+      else
+        return v[c];
+    };
     const int N = PHASE == 1 ? g.I : g.H;
-    Out* out = (Out*)(PHASE == 1 ? g.h : g.y_slots);
     const int lr = lane & 15;
+    // this lane's first row: one 64-bit base, then wave-uniform row offsets
+    const int rl = wm * MW + (lane >> 4) * 4;
+    Out* obase = (Out*)(PHASE == 1 ? g.h : g.y_slots) + (row0 + rl) * N + n0 + wn * NW + lr;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int r = wm * MW + i * 16 + (lane >> 4) * 4 + c;
-        if (m[r] < 0) continue;
-        Out* orow = out + (row0 + r) * N + n0 + wn * NW + lr;
+        const int ro = (i0 + i) * 16 + c;
+        if (m[rl + ro] < 0) continue;
+        Out* orow = obase + ro * N;
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn) {
           // a tile of the wide class may reach past N (ragged last column tile)
           if (BN > 128 && n0 + wn * NW + jn * 16 + lr >= N) continue;
-          const float v = PHASE == 1 ? silu_mul(acc[0][i][jn][c], acc[NMAT - 1][i][jn][c])
-                                     : acc[0][i][jn][c];
+          const float v = PHASE == 1 ? silu_mul(rd(acc[0][i][jn], c), rd(acc[NMAT - 1][i][jn], c))
+                                     : rd(acc[0][i][jn], c);
           store_out<Out>(orow + jn * 16, v);
         }
       }
+  }
+  __device__ __forceinline__ static void store_acc(const FfnArgs& g, const f32x4 (&acc)[NMAT][FM][FN],
+                                                  const int* m, int64_t row0, int n0, int wm,
+                                                  int wn, int lane) {
+    store_rows<FM>(g, acc, m, row0, n0, wm, wn, lane, 0);
   }
 
   // Tile t of a phase -> row-block rb and column tile nt.  Column tiles come in
@@ -664,7 +693,7 @@ struct Tile {
     auto compute_full = [&](const uint8_t* buf) __attribute__((always_inline)) {
      const uint8_t* bufA = buf + wm * MW * ROWB;         // this wave's A rows
      const uint8_t* bufB = buf + (BM + wn * NW) * ROWB;  // its weight rows (matrix mt: + mt * BN rows)
-     if constexpr (!FP8A && NT == kThreadsWide) {
+     if constexpr (!FP8A && WIDE) {
       // wide class: the B fragments of a step stay in registers and the A
       // fragments are read one at a time, which keeps the 128 accumulators, two
       // register stages and the fragments within 256 registers
@@ -761,7 +790,7 @@ struct Tile {
         compute_full(buf);
         return;
       }
-      if constexpr (NT == kThreadsWide) {  // as compute_full, one A fragment at a time
+      if constexpr (WIDE) {  // as compute_full, one A fragment at a time
 #pragma unroll
         for (int jj = 0; jj < KSTEPS / WK; ++jj) {
           const int step = jj * WK + wk;
@@ -928,24 +957,25 @@ struct Tile {
   // ---------------------------------------------------------------------------
   // The wide class's bf16 tiles with direct global -> LDS loads.  Each stage's A
   // rows and weight rows go from HBM (or L2) straight into one of ND LDS stage
-  // buffers with the buffer-load LDS form of gfx950, ND - 1 stages ahead of the
+  // buffers with the buffer-load LDS form of gfx950, ND stages ahead of the
   // MFMAs and with no register staging, so the loads in flight are bounded by LDS
-  // (ND x 32 KiB) instead of by registers.  The buffers are distinct LDS arrays, so
-  // the compiler tracks which stage each fragment read depends on and waits for
-  // exactly that stage's loads.  Each step waits until this wave's loads of the
-  // stage are in LDS, then a barrier makes every wave's loads of the stage visible
-  // and releases the buffer computed in the previous step, which takes the loads
-  // of the stage ND - 1 ahead.  Loads past the last stage (and of rows that hold
-  // no slot) use an offset past the buffer's range: no memory is read.  The
-  // schedule is run_all's for a class that never splits: whole tiles, F or F + 1
-  // per workgroup.
+  // (ND x 32 KiB) instead of by registers.  Four waves, one per SIMD, each own a
+  // 128 x 128 block of the tile: its 256 fp32 sums per lane stay in the
+  // accumulation registers for the whole reduction, and the fragments of the next
+  // stage are read from LDS into a second register set while the MFMAs of this
+  // stage run, so one wave per SIMD keeps its matrix unit fed.  Loads past the
+  // last stage (and of rows that hold no slot) use an offset past the buffer's
+  // range: no memory is read.
   static constexpr int kDmaInstr = ROWS * C / NT;  // 16-byte loads per thread per stage
-  template <int N_, bool Q>
-  __device__ __forceinline__ static void wait_vm_lgkm0() {
-    // vmcnt(N_) and lgkmcnt(0) (the LDS writes of this wave done), then the barrier
+  // s_waitcnt vmcnt(N_) lgkmcnt(0), then s_barrier, as builtins: the compiler
+  // then knows which of its loads and LDS reads are complete (an inline-asm wait
+  // is opaque to it, and it would add waits of its own after it).  gfx9 encoding:
+  // vmcnt in bits 3:0 and 15:14, expcnt (7: none) in 6:4, lgkmcnt in 11:8.
+  template <int N_>
+  __device__ __forceinline__ static void wait_vm_bar() {
     static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
-    if constexpr (Q)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N_) : "memory");
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | ((N_ >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
   }
 
   // ---- the wide class's tile order and tail split ----
@@ -1018,11 +1048,12 @@ struct Tile {
   __device__ __forceinline__ static void run_dma(const FfnArgs& g, uint8_t* b0, uint8_t* b1,
                                                  uint8_t* b2, uint8_t* b3, int* meta3, int* pexp,
                                                  int nb, int nbr, int slot, int G) {
-    static_assert(WKIND == W_BF16 && NT == kThreadsWide && WK == 1 && KSTEPS == 1 && C == 4,
+    static_assert(WKIND == W_BF16 && WIDE && WM == 2 && WN == 2 && WK == 1 && KSTEPS == 1 && C == 4,
                   "the direct-load pipeline serves the wide class's bf16 tiles");
     static_assert(ND == 4, "four stage buffers");
-    static_assert((NT / C) * 2 == BM && (BN % (NT / C)) == 0 && kDmaInstr == 4,
-                  "each load instruction covers 128 rows of one operand");
+    static_assert(NT == BM && ROWS == 2 * NT && NMAT * BN == BM && kDmaInstr == 8,
+                  "load instruction i covers stage rows 64 i .. 64 i + 63: A rows, then weight rows");
+    static_assert(FM == 8 && NMAT * FN == 8, "a wave owns 8 x 8 accumulator blocks");
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
     const int Btok = g.slots / g.k;
@@ -1031,7 +1062,7 @@ struct Tile {
     const int e_end = SH ? g.E_loc + g.n_shared : g.E_loc;
     const int ncol = (N + BN - 1) / BN;
     const int total = nb * ncol;
-    const int nst = K / BK;  // the caller checks K % (ND * BK) == 0 and nst >= 2 * ND
+    const int nst = K / BK;  // the caller checks K % (ND * BK) == 0 and nst >= ND
     const int F = total / G;
     const int r = total - F * G;
     // work items: whole tiles slot, slot + G, ..., then at most one tail piece
@@ -1073,28 +1104,22 @@ struct Tile {
       const int64_t row0 = (int64_t)rb * BM;
       if (SH && rb >= nbr) {
         const int t0 = ((rb - nbr) % nbs) * BM + tid;
-        if (tid < BM) {
-          ms0 = t0 < Btok ? g.slots + t0 : -1;
-          ms1 = tid + 1 < BM && t0 + 1 < Btok ? g.slots + t0 + 1 : -1;
-        }
+        ms0 = t0 < Btok ? g.slots + t0 : -1;
+        ms1 = tid + 1 < BM && t0 + 1 < Btok ? g.slots + t0 + 1 : -1;
         if (tid == 0) me = g.E_loc + (rb - nbr) / nbs;
       } else {
-        if (tid < BM) {
-          ms0 = g.sorted_slots[row0 + tid];
-          ms1 = tid + 1 < BM ? g.sorted_slots[row0 + tid + 1] : -1;
-        }
+        ms0 = g.sorted_slots[row0 + tid];
+        ms1 = tid + 1 < BM ? g.sorted_slots[row0 + tid + 1] : -1;
         if (tid == 0) me = g.block_expert[rb];
       }
     };
     auto store_meta = [&](int j) __attribute__((always_inline)) {
       int* m = meta3 + (j % kMetaSlots) * META;
-      if (tid < BM) {
-        const bool v0 = ms0 >= 0 && ms0 < slot_end;
-        const bool v1 = ms1 >= 0 && ms1 < slot_end;
-        m[tid] = v0 ? ms0 : -1;
-        if (v0 && !v1) m[BM] = tid + 1;
-        if (tid == 0 && !v0) m[BM] = 0;
-      }
+      const bool v0 = ms0 >= 0 && ms0 < slot_end;
+      const bool v1 = ms1 >= 0 && ms1 < slot_end;
+      m[tid] = v0 ? ms0 : -1;
+      if (v0 && !v1) m[BM] = tid + 1;
+      if (tid == 0 && !v0) m[BM] = 0;
       if (tid == 0) {
         m[BM + 1] = me;
         m[BM + 2] = m_rb;
@@ -1104,18 +1129,19 @@ struct Tile {
 
     // ---- the loads of one stage ----
     // Load instruction i of thread tid fills LDS chunk i * NT + tid of the stage
-    // buffer: row (i * NT + tid) / 4, physical chunk tid % 4, which holds logical
-    // chunk c = (tid % 4) ^ swz(row) (the swizzle of read_frag).  Instructions 0-1
-    // take A rows 0-255, 2-3 weight rows 0-255 (gate/up: W1 then W3; down: W2).
-    const int c_log = (tid & 3) ^ ((tid >> 3) & 3);  // swz<4> of row i * NT / 4 + tid / 4
+    // buffer: row 64 i + tid / 4, physical chunk tid % 4, which holds logical
+    // chunk (tid % 4) ^ swz(row) (the swizzle of the fragment reads).
+    // Instructions 0-3 take A rows 0-255, 4-7 weight rows 0-255 (gate/up: W1 rows
+    // n0 .. n0 + 127, then the same rows of W3; down: W2).
+    const int c_log = (tid & 3) ^ ((tid >> 3) & 3);  // swz<4>(64 i + tid / 4)
     const uint32_t a_bytes = PHASE == 1 ? (uint32_t)Btok * (uint32_t)K * ASZ
                                         : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
-    uint32_t l_aoff[2] = {kOob, kOob};
-    uint32_t l_boff[2];
+    uint32_t l_aoff[4] = {kOob, kOob, kOob, kOob};
+    uint32_t l_boff[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rr = NMAT == 2 ? (tid >> 2) : i * (NT / C) + (tid >> 2);
+    for (int i = 0; i < 4; ++i) {
+      const int rr = NMAT == 2 ? (i & 1) * 64 + (tid >> 2) : i * 64 + (tid >> 2);
       l_boff[i] = (uint32_t)(rr * K + c_log * 8) * WSZ;
     }
     __amdgpu_buffer_rsrc_t l_b_rsrc[2];
@@ -1137,8 +1163,8 @@ struct Tile {
       l_b_rsrc[0] = make_rsrc(wmat0 + wrow0, wbytes);
       l_b_rsrc[1] = make_rsrc(wmat1 + wrow0, wbytes);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = i * (NT / C) + (tid >> 2);
+      for (int i = 0; i < 4; ++i) {
+        const int row = i * 64 + (tid >> 2);
         const int sl = m[row];
         l_aoff[i] = kOob;
         if (eok && sl >= 0 && sl < slot_end) {
@@ -1147,20 +1173,25 @@ struct Tile {
         }
       }
     };
-    auto issue = [&](uint8_t* buf) __attribute__((always_inline)) {
+    // A stage's loads in three parts, so that a step can spread its load
+    // instructions among its MFMAs: issue_begin (the item's offsets when a new
+    // item starts), issue_one(buf, i) for i = 0 .. kDmaInstr - 1, issue_end.
+    int l_soff = 0;
+    auto issue_begin = [&]() __attribute__((always_inline)) {
       if (l_new) enter_load_tile(l_j);
       l_new = false;
-      const int soff = l_s * BK * ASZ;
+      l_soff = l_s * BK * ASZ;
+    };
+    auto issue_one = [&](uint8_t* buf, int i) __attribute__((always_inline)) {
       typedef __attribute__((address_space(3))) void lds_void;
-#pragma unroll
-      for (int i = 0; i < kDmaInstr; ++i) {
-        lds_void* dst = (lds_void*)(buf + (i * NT + wave * 64) * 16);
-        if (i < 2)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, l_aoff[i], soff, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(l_b_rsrc[NMAT == 2 ? i - 2 : 0], dst, 16,
-                                                   l_boff[i - 2], soff, 0, 0);
-      }
+      lds_void* dst = (lds_void*)(buf + (i * NT + wave * 64) * 16);
+      if (i < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, l_aoff[i], l_soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(l_b_rsrc[NMAT == 2 ? (i - 4) >> 1 : 0], dst, 16,
+                                                 l_boff[i - 4], l_soff, 0, 0);
+    };
+    auto issue_end = [&]() __attribute__((always_inline)) {
       if (++l_s == l_se) {  // past the last item the offsets are out of range
         ++l_j;
         l_s = item_sb(l_j);
@@ -1168,71 +1199,102 @@ struct Tile {
         l_new = true;
       }
     };
+    auto issue = [&](uint8_t* buf) __attribute__((always_inline)) {
+      issue_begin();
+#pragma unroll
+      for (int i = 0; i < kDmaInstr; ++i) issue_one(buf, i);
+      issue_end();
+    };
 
-    // ---- accumulators and the fragment layout ----
+    // ---- accumulators, fragments and MFMAs ----
+    // The MFMAs are written as inline asm with the accumulator tied in place
+    // ("+a"): the sums then stay in the same accumulation registers from stage to
+    // stage (with the builtin, the register allocator rotated them through copies).
+    // The compiler does not see these as MFMAs, so it inserts no hazard padding
+    // for them: after an item's last MFMAs, an explicit s_nop of 19 wait states
+    // covers the longest MFMA-result-to-read requirement before any read of the
+    // sums; the zeroing before the first MFMAs of an item is separated from them
+    // by the stage loop's barrier, loads and LDS reads.  Fragment operands come
+    // from LDS reads, which the compiler's own counter waits cover.
     f32x4 acc[NMAT][FM][FN];
     const int lr = lane & 15, lg = lane >> 4;
     const int foff = lr * ROWB + ((lg ^ swz<C>(lr)) << 4);
-
-    // ---- the pipeline ----
-    // Tile loop around a stage loop unrolled by ND, the tile's stores after it: the
-    // accumulators live across the stage loop only, so they stay in place and
-    // nothing spills.  Every tile has nst stages and the caller checks
-    // nst % ND == 0, so stage s of any tile sits in buffer s % ND and each unrolled
-    // step names its buffer at compile time.  The loads run ND - 1 stages ahead
-    // across tile boundaries: the last steps of tile j issue the first stages of
-    // tile j + 1, whose metadata is fetched at its stage -ND - 1 and stored at its
-    // stage -ND (before that step's barrier), so it is published before the step
-    // that issues its first loads.
-    //
-    // Ping-pong between the two waves of each SIMD.  Waves w and w + 4 share a
-    // SIMD and hold opposite row halves (wm = 0 and 1).  Every wave runs the same
-    // steps, each two halves long: barrier, issue the loads of stage s + ND - 1
-    // and read stage s's fragments from LDS; barrier, the MFMAs of stage s.  The
-    // wm = 1 waves take one extra barrier before the first step (and the wm = 0
-    // waves one after the last), and barriers pair up by count, so the wm = 1
-    // waves run half a step behind: while one wave of a SIMD reads LDS, the other
-    // runs its MFMAs, instead of both waiting for their fragments at the start of
-    // every stage.  Waits before each barrier: every wave has its own LDS reads
-    // done (so a buffer is refilled only after all waves have read it) and its
-    // loads of the next stage that any wave reads after the barrier: stage s
-    // before the first barrier of step s for the leading waves, stage s + 1
-    // before the second barrier of step s for the trailing ones.  A wave with any
-    // valid row runs all its MFMAs (rows with no slot were loaded out of range
-    // and their sums are never stored); the all-padding test is taken per tile.
     auto buf_of = [&](int u) __attribute__((always_inline)) {
       return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : b3));
     };
-    bf16x8 fb[NMAT][FN], fa[FM];
-    auto read_frags = [&](const uint8_t* buf) __attribute__((always_inline)) {
-      const uint8_t* bufA = buf + wm * MW * ROWB + foff;
-      const uint8_t* bufB = buf + (BM + wn * NW) * ROWB + foff;
+    bf16x8 fa0[FM], fb0[NMAT * FN], fa1[FM], fb1[NMAT * FN];
+    // fragment k of a stage: k < NMAT FN the weight fragments, then the A ones
+    auto read_one = [&](const uint8_t* buf, int k, bf16x8(&fa)[FM], bf16x8(&fb)[NMAT * FN])
+        __attribute__((always_inline)) {
+      if (k < NMAT * FN)
+        fb[k] = *(const bf16x8*)(buf + (BM + wn * NW + (k / FN) * BN + (k % FN) * 16) * ROWB + foff);
+      else
+        fa[k - NMAT * FN] = *(const bf16x8*)(buf + (wm * MW + (k - NMAT * FN) * 16) * ROWB + foff);
+    };
+    auto read_frags = [&](const uint8_t* buf, bf16x8(&fa)[FM], bf16x8(&fb)[NMAT * FN])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < NMAT * FN + FM; ++k) read_one(buf, k, fa, fb);
+    };
+    // the MFMAs of A fragment row i (all of its weight fragments)
+    auto mfma_row = [&](int i, const bf16x8(&fa)[FM], const bf16x8(&fb)[NMAT * FN])
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-        for (int jn = 0; jn < FN; ++jn) fb[mt][jn] = *(const bf16x8*)(bufB + (mt * BN + jn * 16) * ROWB);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(bufA + i * 16 * ROWB);
+        for (int jn = 0; jn < FN; ++jn)
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                       : "+a"(acc[mt][i][jn])
+                       : "v"(fa[i]), "v"(fb[mt * FN + jn]));
     };
-    auto mfmas = [&]() __attribute__((always_inline)) {
+    // One step's work after its barrier, in FM groups, each: one load instruction
+    // of the stage ND ahead, two fragment reads of the next stage and the MFMAs of
+    // one A fragment row of this stage.  A wave per SIMD issues everything itself,
+    // so spreading the loads and LDS reads among the MFMAs keeps the matrix unit
+    // busy while they queue (issued all before the MFMAs, they left it idle for
+    // about half of each step).  Memory operations keep their program order
+    // around the volatile MFMA asm.
+    static_assert(FM == kDmaInstr && 2 * FM == NMAT * FN + FM, "one load and two reads per group");
+    auto groups = [&](uint8_t* dbuf, const uint8_t* rbuf, bf16x8(&nfa)[FM], bf16x8(&nfb)[NMAT * FN],
+                      const bf16x8(&cfa)[FM], const bf16x8(&cfb)[NMAT * FN], bool run)
+        __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-          for (int jn = 0; jn < FN; ++jn)
-            acc[mt][i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[mt][jn], acc[mt][i][jn], 0, 0, 0);
+      for (int gi = 0; gi < FM; ++gi) {
+        issue_one(dbuf, gi);
+        read_one(rbuf, 2 * gi, nfa, nfb);
+        read_one(rbuf, 2 * gi + 1, nfa, nfb);
+        if (run) mfma_row(gi, cfa, cfb);
+      }
     };
-    const bool late = wm != 0;  // wave-uniform
+
+    // ---- the pipeline ----
+    // Tile loop around a stage loop unrolled by ND, the tile's stores after it: the
+    // accumulators live across the stage loop only.  Every item has a multiple of
+    // ND stages and starts at a multiple of ND (the caller checks nst % ND == 0),
+    // so stage s of any item sits in buffer s % ND, its fragments in register set
+    // s % 2, and each unrolled step names both at compile time.  Step s: wait until
+    // this wave's loads of stage s + 1 are in LDS and its LDS reads of stage s are
+    // in registers, then a barrier (every wave's loads of stage s + 1 are visible,
+    // and every wave holds stage s's fragments, so stage s's buffer is free); issue
+    // the loads of stage s + ND into that buffer, read stage s + 1's fragments
+    // (the next item's first stage after an item's last), and run stage s's MFMAs.
+    // Each stage's loads so have ND - 1 steps to land.  The loads run ND stages
+    // ahead across items: item j + 1's metadata is fetched at stage se - ND - 1
+    // of item j and stored at stage se - ND, before the barrier of the step that
+    // issues its first loads (an item of only ND stages fetches it at that step
+    // too).  A wave with any valid row runs all its MFMAs (rows with no slot were
+    // loaded out of range and their sums are never stored); the all-padding test
+    // is taken per item.
     fetch_meta(0);
     store_meta(0);
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < ND - 1; ++u) issue(buf_of(u));
-    if (late) wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
+    for (int u = 0; u < ND; ++u) issue(buf_of(u));
+    wait_vm_bar<(ND - 1) * kDmaInstr>();  // stage 0 in LDS
+    read_frags(b0, fa0, fb0);
     for (int j = 0; j < nit; ++j) {
       const int* m = meta3 + (j % kMetaSlots) * META;
-      const int sb = item_sb(j), se = item_se(j);
+      const int len = item_se(j) - item_sb(j);
       const bool live = (unsigned)__builtin_amdgcn_readfirstlane(m[BM + 1]) < (unsigned)e_end;
       const int nvalid = __builtin_amdgcn_readfirstlane(m[BM]);
       const bool run = live && wm * MW < nvalid;
@@ -1243,65 +1305,78 @@ struct Tile {
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int jn = 0; jn < FN; ++jn) acc[mt][i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto step = [&](int s0, auto U) __attribute__((always_inline)) {
+      // step c of the item: its stage sb + c (the loop counts from the item's
+      // start, so that every item runs the same loop)
+      auto step = [&](int c0, auto U) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
-        const int s = s0 + u;
-        if (more && s == se - ND - 1) fetch_meta(j + 1);
-        if (more && s == se - ND) store_meta(j + 1);
-        // this stage's loads are the oldest but (ND - 2) stages of this wave's loads
-        wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
-        issue(buf_of((u + ND - 1) % ND));
-        read_frags(buf_of(u));
-        // the trailing waves' next stage is the oldest but (ND - 2) of theirs now;
-        // the leading waves need nothing new here
-        if (late)
-          wait_vm_lgkm0<(ND - 2) * kDmaInstr, true>();
+        const int c = c0 + u;
+        // (an item of only ND stages fetches at its first step, just before storing)
+        if (more && c == (len - ND - 1 > 0 ? len - ND - 1 : 0)) fetch_meta(j + 1);
+        if (more && c == len - ND) store_meta(j + 1);
+        // stage s + 1 is the oldest but ND - 2 stages of this wave's loads
+        wait_vm_bar<(ND - 2) * kDmaInstr>();
+        issue_begin();
+        if constexpr ((u & 1) == 0)
+          groups(buf_of(u), buf_of((u + 1) % ND), fa1, fb1, fa0, fb0, run);
         else
-          wait_vm_lgkm0<(ND - 1) * kDmaInstr, true>();
-        if (run) mfmas();
+          groups(buf_of(u), buf_of((u + 1) % ND), fa0, fb0, fa1, fb1, run);
+        issue_end();
+        // after the item's last MFMAs, the padding before any read of the sums:
+        // inside the loop, so every read after it (wherever the compiler places
+        // it) follows in execution order
+        if constexpr (u == ND - 1)
+          if (c0 + ND >= len) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
       };
-      for (int s0 = sb; s0 < se; s0 += ND) {
-        step(s0, std::integral_constant<int, 0>{});
-        step(s0, std::integral_constant<int, 1>{});
-        step(s0, std::integral_constant<int, 2>{});
-        step(s0, std::integral_constant<int, 3>{});
-      }
+      // every item has at least ND stages: a loop with no path around it
+      int c0 = 0;
+      do {
+        step(c0, std::integral_constant<int, 0>{});
+        step(c0, std::integral_constant<int, 1>{});
+        step(c0, std::integral_constant<int, 2>{});
+        step(c0, std::integral_constant<int, 3>{});
+        c0 += ND;
+      } while (c0 < len);
       if (live) {
         if (j < nwhole) {
           const int rb = __builtin_amdgcn_readfirstlane(m[BM + 2]);
           const int nt = __builtin_amdgcn_readfirstlane(m[BM + 3]);
-          store_acc(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane);
+          store_rows<FM, true>(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane, 0);
         } else {
           // this workgroup's piece: its fp32 sums in MFMA fragment order, 16 bytes
-          // per lane, wave-contiguous (wide_fixup adds the pieces)
-          float* dst = g.part + (int64_t)slot * PIECE + wave * NFRAG * 256;
+          // per lane, wave-contiguous (wide_fixup adds the pieces).  Buffer
+          // stores with the fragment's offset as a constant: no per-fragment
+          // address is formed (or kept live across the stage loop)
+          const __amdgpu_buffer_rsrc_t prs =
+              make_rsrc(g.part + (int64_t)slot * PIECE + wave * NFRAG * 256, NFRAG * 256 * 4);
 #pragma unroll
           for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
               for (int jn = 0; jn < FN; ++jn)
-                *(f32x4*)(dst + (((mt * FM + i) * FN + jn) * 64 + lane) * 4) = acc[mt][i][jn];
+              {
+                const f32x4& a = acc[mt][i][jn];
+                const f32x4 v = {acc_read(a, 0), acc_read(a, 1), acc_read(a, 2), acc_read(a, 3)};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prs, lane * 16,
+                                                       ((mt * FM + i) * FN + jn) * 1024, 0);
+              }
         }
-        // the stores count in the same counter as the loads: let them finish, so
-        // the next stage's wait counts loads only
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
     }
-    if (!late) wait_vm_lgkm0<0, true>();  // the barrier the trailing waves took first
     // every load of this workgroup has landed before it exits (the last steps'
     // loads were out of range, so this costs nothing)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // The fix-up of the wide class's split tail tile tq (see wide_pieces): adds its
   // P pieces in reduction order (piece q, workgroup slot tq * P + q, holds stages
-  // [4 (q ngr / P), 4 ((q + 1) ngr / P)) ) and stores the tile.  Each of the eight
-  // waves adds its own fragment region, half of it at a time, with all of a
-  // piece's loads for that half in flight together.
+  // [4 (q ngr / P), 4 ((q + 1) ngr / P)) ) and stores the tile.  Two workgroups
+  // share a tile, one per half of each wave's rows (half = 0, 1); each wave adds
+  // its fragment region two 16-row groups at a time, with all of a piece's loads
+  // for those rows in flight together.
   template <bool SH>
   __device__ __forceinline__ static void wide_fixup(const FfnArgs& g, int* meta, int* pexp, int nb,
-                                                    int nbr, int G, int tq) {
+                                                    int nbr, int G, int tq, int half) {
     const int N = PHASE == 1 ? g.I : g.H;
     const int K = PHASE == 1 ? g.H : g.I;
     const int ncol = (N + BN - 1) / BN;
@@ -1321,44 +1396,45 @@ struct Tile {
     const int e = SH && rb >= nbr ? g.E_loc + (rb - nbr) / nbs : g.block_expert[rb];
     if ((unsigned)e >= (unsigned)e_end) return;  // uniform: the pieces were not stored
     const int tid = threadIdx.x;
-    if (tid < BM) {
+    for (int row = tid; row < BM; row += NT) {
       int sl;
       if (SH && rb >= nbr) {
-        const int t0 = ((rb - nbr) % nbs) * BM + tid;
+        const int t0 = ((rb - nbr) % nbs) * BM + row;
         sl = t0 < Btok ? g.slots + t0 : -1;
       } else {
-        sl = g.sorted_slots[(int64_t)rb * BM + tid];
+        sl = g.sorted_slots[(int64_t)rb * BM + row];
       }
-      meta[tid] = sl >= 0 && sl < slot_end ? sl : -1;
+      meta[row] = sl >= 0 && sl < slot_end ? sl : -1;
     }
     __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int wn = wave % WN, wm = wave / WN;
-    f32x4 acc[NMAT][FM][FN];
-    constexpr int FH = FM / 2;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    constexpr int FG = 2;
+    static_assert(FM % (2 * FG) == 0, "each half is whole groups of FG row groups");
+#pragma unroll 1
+    for (int i0 = half * (FM / 2); i0 < (half + 1) * (FM / 2); i0 += FG) {
+      f32x4 acc[NMAT][FG][FN];
       for (int q = 0; q < P; ++q) {
         const float* src = g.part + (int64_t)(tq * P + q) * PIECE + wave * NFRAG * 256;
-        f32x4 v[NMAT][FH][FN];
+        f32x4 v[NMAT][FG][FN];
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int i = 0; i < FH; ++i)
+          for (int i = 0; i < FG; ++i)
 #pragma unroll
             for (int jn = 0; jn < FN; ++jn)
-              v[mt][i][jn] = *(const f32x4*)(src + (((mt * FM + h * FH + i) * FN + jn) * 64 + lane) * 4);
+              v[mt][i][jn] = *(const f32x4*)(src + (((mt * FM + i0 + i) * FN + jn) * 64 + lane) * 4);
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-          for (int i = 0; i < FH; ++i)
+          for (int i = 0; i < FG; ++i)
 #pragma unroll
             for (int jn = 0; jn < FN; ++jn)
-              acc[mt][h * FH + i][jn] = q == 0 ? v[mt][i][jn] : acc[mt][h * FH + i][jn] + v[mt][i][jn];
+              acc[mt][i][jn] = q == 0 ? v[mt][i][jn] : acc[mt][i][jn] + v[mt][i][jn];
       }
+      store_rows<FG>(g, acc, meta, (int64_t)rb * BM, nt * BN, wm, wn, lane, i0);
     }
-    store_acc(g, acc, meta, (int64_t)rb * BM, nt * BN, wm, wn, lane);
   }
 
   // The fix-up of tail tile tq (the tile F * G + tq of the schedule in run_all):
@@ -1476,24 +1552,28 @@ struct Tile {
 // ---------------------------------------------------------------------------
 // configuration table: must match kVariants in moe_common.h
 //   Cfg<V, PHASE, WKIND>::R is the tile runner of configuration V in that phase.
-//   NT threads per workgroup; RX multiplies the LDS row bytes of the fp32, fp8 and
-//   fp8 x fp8 tiles (their fragments, decode or load shapes need 128-byte rows
-//   where the bf16 tile of the wide class uses 64).
+//   WIDE: the one-workgroup-per-CU class (else two per CU, 256 threads each); RX
+//   multiplies the LDS row bytes of the fp32, fp8 and fp8 x fp8 tiles (their
+//   fragments, decode or load shapes need 128-byte rows where the bf16 tile of the
+//   wide class uses 64).
 // ---------------------------------------------------------------------------
 template <int V, int PHASE, int WKIND>
 struct Cfg;
-#define MOE_CFG(V, BM, BN1, BN2, ROWB1, ROWB2, WM, WN, WK, RS, STREAM, NT, RX)                 \
+#define MOE_CFG(V, BM, BN1, BN2, ROWB1, ROWB2, WM, WN, WK, RS, STREAM, WIDE, RX)               \
   template <int PHASE, int WKIND>                                                             \
   struct Cfg<V, PHASE, WKIND> {                                                               \
     static constexpr int BN = PHASE == 1 ? BN1 : BN2;                                         \
     static constexpr int ROWB = (PHASE == 1 ? ROWB1 : ROWB2) * (WKIND == W_BF16 ? 1 : RX);    \
-    using R = Tile<BM, BN, WM, WN, WK, ROWB, RS, STREAM, PHASE, WKIND, NT>;                   \
+    static constexpr int WNX = (WIDE) && WKIND != W_BF16 ? 2 * (WN) : (WN);                   \
+    using R = Tile<BM, BN, WM, WNX, WK, ROWB, RS, STREAM, PHASE, WKIND, 64 * (WM) * WNX * (WK), \
+                   (WIDE) != 0>;                                                              \
   };                                                                                          \
   static_assert(kVariants[V].bm == BM && kVariants[V].bn1 == BN1 && kVariants[V].bn2 == BN2 && \
                     kVariants[V].rowb == ROWB1 && kVariants[V].wm == WM &&                    \
                     kVariants[V].wn == WN && kVariants[V].wk == WK && kVariants[V].splitk == 1 && \
                     kVariants[V].stream == STREAM &&                                          \
-                    kVariants[V].wgcu == (NT == kThreads ? kWgPerCu : 1),                     \
+                    kVariants[V].wgcu == ((WIDE) ? 1 : kWgPerCu) &&                           \
+                    ((WIDE) || 64 * (WM) * (WN) * (WK) == kThreads),                          \
                 "kernel configuration table out of sync with kVariants");
 // Streaming class: two workgroups share a compute unit, so each stage buffer
 // holds at most 32 KiB: every stage carries 16 KiB of weights (the down phase has
@@ -1502,24 +1582,27 @@ struct Cfg;
 // common case), so they stream the weights with non-temporal loads, which sustain
 // a markedly higher HBM rate; the largest one serves many row-blocks per expert
 // that re-read each weight tile from L2, so it keeps cached loads.
-MOE_CFG(0, 16, 16, 16, 512, 1024, 1, 1, 4, 2, 1, kThreads, 1)
-MOE_CFG(1, 32, 32, 32, 256, 512, 1, 2, 2, 2, 1, kThreads, 1)
-MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2, 1, kThreads, 1)
-MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2, 0, kThreads, 1)
-// Wide class: one 512-thread workgroup per compute unit computes a 256 x 256
-// output tile (gate/up: 128 gate and 128 up columns), eight waves of 128 x 64
-// each.  Per byte staged it does twice the MFMA work of the 128-row streaming
-// tile, which halves the L2 and fabric traffic per FLOP where the matrix units
-// bound the layer.  bf16 stages are 32 deep (64-byte LDS rows, 32 KiB a stage).
-MOE_CFG(4, 256, 128, 256, 64, 64, 2, 4, 1, 2, 0, kThreadsWide, 2)
+MOE_CFG(0, 16, 16, 16, 512, 1024, 1, 1, 4, 2, 1, 0, 1)
+MOE_CFG(1, 32, 32, 32, 256, 512, 1, 2, 2, 2, 1, 0, 1)
+MOE_CFG(2, 64, 64, 64, 128, 256, 2, 2, 1, 2, 1, 0, 1)
+MOE_CFG(3, 128, 64, 128, 128, 128, 2, 2, 1, 2, 0, 0, 1)
+// Wide class: one workgroup per compute unit computes a 256 x 256 output tile
+// (gate/up: 128 gate and 128 up columns).  Per byte staged it does twice the MFMA
+// work of the 128-row streaming tile, which halves the L2 and fabric traffic per
+// FLOP where the matrix units bound the layer.  bf16 tiles: four waves, one per
+// SIMD, of 128 x 128 each (their 256 fp32 sums per lane live in the accumulation
+// registers), 32-deep stages (64-byte LDS rows, 32 KiB a stage).  fp32 and fp8
+// tiles: eight waves of 128 x 64 (their register-staged path needs the second
+// wave per SIMD to hide its loads), with 128-byte rows.
+MOE_CFG(4, 256, 128, 256, 64, 64, 2, 2, 1, 2, 0, 1, 2)
 // more of the streaming class: other column widths, stage depths and load policies
-MOE_CFG(5, 16, 32, 32, 256, 512, 1, 2, 2, 2, 1, kThreads, 1)
-MOE_CFG(6, 32, 16, 32, 512, 512, 1, 1, 4, 2, 1, kThreads, 1)
-MOE_CFG(7, 64, 32, 64, 256, 256, 2, 2, 1, 2, 1, kThreads, 1)
-MOE_CFG(8, 32, 64, 64, 128, 256, 1, 4, 1, 2, 1, kThreads, 1)
-MOE_CFG(9, 64, 64, 64, 128, 256, 2, 2, 1, 2, 0, kThreads, 1)
-MOE_CFG(10, 128, 64, 128, 128, 128, 2, 2, 1, 2, 1, kThreads, 1)
-MOE_CFG(11, 32, 32, 32, 256, 512, 1, 2, 2, 2, 0, kThreads, 1)
+MOE_CFG(5, 16, 32, 32, 256, 512, 1, 2, 2, 2, 1, 0, 1)
+MOE_CFG(6, 32, 16, 32, 512, 512, 1, 1, 4, 2, 1, 0, 1)
+MOE_CFG(7, 64, 32, 64, 256, 256, 2, 2, 1, 2, 1, 0, 1)
+MOE_CFG(8, 32, 64, 64, 128, 256, 1, 4, 1, 2, 1, 0, 1)
+MOE_CFG(9, 64, 64, 64, 128, 256, 2, 2, 1, 2, 0, 0, 1)
+MOE_CFG(10, 128, 64, 128, 128, 128, 2, 2, 1, 2, 1, 0, 1)
+MOE_CFG(11, 32, 32, 32, 256, 512, 1, 2, 2, 2, 0, 0, 1)
 #undef MOE_CFG
 // the streaming class's entries, for the dispatch switches
 #define MOE_STREAM_VARIANTS(X) X(0) X(1) X(2) X(3) X(5) X(6) X(7) X(8) X(9) X(10) X(11)
@@ -1533,6 +1616,13 @@ constexpr int lds_bytes_stream() {
 #undef MOE_LDS
   return m;
 }
+// threads per workgroup of the wide launch (and of the bf16 wide fix-up launch)
+template <int WKIND>
+constexpr int wide_threads() {
+  return Cfg<kWideVariant, 1, WKIND>::R::THREADS;
+}
+static_assert(wide_threads<W_BF16>() == 64 * kVariants[kWideVariant].wm * kVariants[kWideVariant].wn,
+              "the wide configuration's table entry describes its bf16 tiles");
 // dynamic LDS of the wide launch; its bf16 tiles use four static stage buffers
 template <int PHASE, int WKIND>
 constexpr int lds_bytes_wide() {
@@ -1605,13 +1695,13 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) ffn_kernel(FfnArgs g) {
   }
 }
 
-// The launch that follows the streaming one in each phase: one 512-thread
-// workgroup per CU.  With the wide configuration chosen it computes all of the
-// phase's tiles; otherwise it is the streaming class's fix-up, adding the
-// partial sums of each split tail tile (Tile::fixup; tail tile tq for tq =
-// workgroup, workgroup + grid, ...).
+// The launch that follows the streaming one in each phase: one workgroup per CU
+// (256 threads for bf16, 512 for fp32 and fp8).  With the wide configuration
+// chosen it computes all of the phase's tiles; otherwise it is the streaming
+// class's fix-up, adding the partial sums of each split tail tile (Tile::fixup;
+// tail tile tq for tq = workgroup, workgroup + grid, ...).
 template <int PHASE, int WKIND, bool SH>
-__global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
+__global__ void __launch_bounds__(wide_threads<WKIND>(), 1) ffn_wide_kernel(FfnArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int meta3[kMetaSlots * (kMaxBlockM + 4)];
   const int v = *g.variant;
@@ -1629,11 +1719,10 @@ __global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
       __shared__ int pexp[kRunTable];
       const int K = PHASE == 1 ? g.H : g.I;
       const int slot = xcd_slot(blockIdx.x, gridDim.x);
-      if (K % (4 * R::BK) == 0 && K / R::BK >= 8)
+      // H and I are multiples of 128 (the API checks), so every reduction is whole
+      // groups of four 32-deep stages
+      if (K % (4 * R::BK) == 0 && K >= 4 * R::BK)
         R::template run_dma<SH, 4>(g, s0, s1, s2, s3, meta3, pexp, nb, nbr, slot, gridDim.x);
-      else  // a reduction too short for the four-stage pipeline, or not in whole
-            // groups of four stages
-        R::template run_all<SH>(g, s0, s1, meta3, nb, nbr, slot, gridDim.x);
     } else {
       run_phase<kWideVariant, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr);
     }
@@ -1655,10 +1744,11 @@ __global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_kernel(FfnArgs g) {
 }
 
 // The fix-up launch of the wide class's split down-phase tail (Tile::wide_fixup):
-// one 512-thread workgroup per possible split tile (at most half the wide grid).
-// It follows the wide launch on the stream, so the pieces are complete.
+// two workgroups per possible split tile (at most half the wide grid), one per
+// half of the tile's rows.  It follows the wide launch on the stream, so the
+// pieces are complete.
 template <int PHASE, bool SH>
-__global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_fixup_kernel(FfnArgs g, int grid_wide) {
+__global__ void __launch_bounds__(wide_threads<W_BF16>(), 1) ffn_wide_fixup_kernel(FfnArgs g, int grid_wide) {
   __shared__ int meta[kMaxBlockM + 4];
   __shared__ int pexp[kRunTable];
   const int v = *g.variant;
@@ -1667,8 +1757,8 @@ __global__ void __launch_bounds__(kThreadsWide, 1) ffn_wide_fixup_kernel(FfnArgs
   if (!block_counts<SH>(g, v, nb, nbr)) return;
   using R = typename Cfg<kWideVariant, PHASE, W_BF16>::R;
   const int K = PHASE == 1 ? g.H : g.I;
-  if (K % (4 * R::BK) != 0 || K / R::BK < 8) return;  // the register-staged path never splits
-  R::template wide_fixup<SH>(g, meta, pexp, nb, nbr, grid_wide, blockIdx.x);
+  if (K % (4 * R::BK) != 0 || K / R::BK < 8) return;  // no split below two four-stage groups
+  R::template wide_fixup<SH>(g, meta, pexp, nb, nbr, grid_wide, blockIdx.x >> 1, blockIdx.x & 1);
 }
 
 // Whether the wide class can split the down phase's tail for this problem: the
@@ -1704,12 +1794,13 @@ hipError_t launch_phase_sh(const FfnArgs& g, int grid_wide, hipStream_t s) {
   ffn_kernel<PHASE, WKIND, SH><<<g.grid_stream, kThreads, lds, s>>>(g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ffn_wide_kernel<PHASE, WKIND, SH><<<grid_wide, kThreadsWide, ldsw, s>>>(g);
+  ffn_wide_kernel<PHASE, WKIND, SH><<<grid_wide, wide_threads<WKIND>(), ldsw, s>>>(g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (PHASE == 2 && WKIND == W_BF16) {
     if (wide_split_possible(g, grid_wide)) {
-      ffn_wide_fixup_kernel<PHASE, SH><<<(grid_wide + 1) / 2, kThreadsWide, 0, s>>>(g, grid_wide);
+      ffn_wide_fixup_kernel<PHASE, SH><<<2 * ((grid_wide + 1) / 2), wide_threads<W_BF16>(), 0, s>>>(
+          g, grid_wide);
       e = hipGetLastError();
     }
   }

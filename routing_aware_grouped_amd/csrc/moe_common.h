@@ -39,17 +39,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // LDS allocation and one register budget for all its entries (RaMP, section 3.3:
 // one shared-memory buffer and one register count for every entry of a
 // polymorphic kernel):
-//   - the streaming class: 256 threads, two workgroups per CU (entries 0-3);
-//   - the wide class: 512 threads, one workgroup per CU, a 256 x 256 output tile
-//     whose larger per-workgroup reuse of every staged byte suits the loads where
-//     the matrix units, not HBM, bound the time (entry 4).
+//   - the streaming class: 256 threads, two workgroups per CU;
+//   - the wide class: one workgroup per CU, a 256 x 256 output tile whose larger
+//     per-workgroup reuse of every staged byte suits the loads where the matrix
+//     units, not HBM, bound the time (entry 4).  Its bf16 tiles run four waves
+//     (the wave counts below); its fp32 and fp8 tiles run eight, twice the waves
+//     along N.
 //   bm    token rows per tile (b_c of RaMP Eq. 1)
 //   bn1   weight rows per tile of W1 and of W3 in the gate/up phase
 //   bn2   weight rows per tile of W2 in the down phase
 //   rowb  LDS bytes per tile row per pipeline stage for bf16 operands (BLOCK_K =
 //         rowb / 2; fp32 operands use half the depth, and in the wide class the
 //         fp32 and fp8 x fp8 tiles use twice the row bytes)
-//   wm, wn, wk  waves along M, along N, and splitting K inside a tile
+//   wm, wn, wk  waves along M, along N, and splitting K inside a tile (bf16)
 //   splitk      tiles splitting K of the down phase (1 = none)
 //   stream      1: weights are read with non-temporal (streaming) loads, for the
 //               small-M configurations where each weight tile is read once;
@@ -61,8 +63,7 @@ struct VariantDesc {
 };
 
 constexpr int kNumVariants = 12;
-constexpr int kThreads = 256;      // streaming class
-constexpr int kThreadsWide = 512;  // wide class
+constexpr int kThreads = 256;  // streaming class
 constexpr int kWideVariant = 4;
 
 // The compiled configuration space.  The served menu of a workload is chosen
@@ -73,7 +74,7 @@ constexpr VariantDesc kVariants[kNumVariants] = {
     {32, 32, 32, 256, 1, 2, 2, 1, 1, 2},      // 1
     {64, 64, 64, 128, 2, 2, 1, 1, 1, 2},      // 2
     {128, 64, 128, 128, 2, 2, 1, 1, 0, 2},    // 3
-    {256, 128, 256, 64, 2, 4, 1, 1, 0, 1},    // 4: the wide class
+    {256, 128, 256, 64, 2, 2, 1, 1, 0, 1},    // 4: the wide class (bf16 waves)
     {16, 32, 32, 256, 1, 2, 2, 1, 1, 2},      // 5: 0 with twice the columns
     {32, 16, 32, 512, 1, 1, 4, 1, 1, 2},      // 6: 1 with half the gate/up columns
     {64, 32, 64, 256, 2, 2, 1, 1, 1, 2},      // 7: 2 with half the gate/up columns

@@ -10,7 +10,7 @@ MENU = [
     (32, 32, 32, 128, 1, 2, 2, 1, 1, 2, 256),
     (64, 64, 64, 64, 2, 2, 1, 1, 1, 2, 256),
     (128, 64, 128, 64, 2, 2, 1, 1, 0, 2, 256),
-    (256, 128, 256, 32, 2, 4, 1, 1, 0, 1, 512),
+    (256, 128, 256, 32, 2, 2, 1, 1, 0, 1, 256),
     (16, 32, 32, 128, 1, 2, 2, 1, 1, 2, 256),
     (32, 16, 32, 256, 1, 1, 4, 1, 1, 2, 256),
     (64, 32, 64, 128, 2, 2, 1, 1, 1, 2, 256),
@@ -53,13 +53,13 @@ def splits_tail(r: int, grid: int, stream: int, full_rounds: int = 0) -> bool:
     return 10 * (grid - r) > grid * (full_rounds + 1)
 
 
-# The wide configuration (512-thread workgroups): BLOCK_M 256, BLOCK_N 256 in the
+# The wide configuration (one workgroup per CU): BLOCK_M 256, BLOCK_N 256 in the
 # down phase, 32-deep stages.  Its down phase splits the last round's tiles
 # (include/moe.h, moe_grouped_down): after F >= 1 full rounds of the wide grid, a
 # tail of 0 < r <= grid / 2 tiles is cut into P = min(grid // r, nst // 8) pieces
 # per tile (no split when P < 2), nst = I / 32 stages per tile, which must be a
 # multiple of 4 and at least 8.
-WIDE = next(v for v, m in enumerate(MENU) if m[10] == 512)
+WIDE = next(v for v, m in enumerate(MENU) if m[9] == 1)
 
 
 def wide_pieces(total: int, grid: int, nst: int) -> int:

@@ -193,7 +193,7 @@ def test_select_config_bit_exact():
     ("qwen3", 1, 0.3, None), ("qwen3", 37, 1.0, None), ("qwen3", 130, 0.05, None),
     ("mixtral", 1, 1.0, None), ("mixtral", 5, 0.1, None),
     ("dsv3_share", 8, 1.0, None), ("dsv3_share", 96, 0.1, 24),
-    ("kimi_share", 64, 0.05, 24)])
+    ("kimi_share", 64, 0.05, 24), ("tiny_bf16", 37, 0.1, None), ("tiny_bf16", 700, 1.0, None)])
 def test_layer_every_variant(shape, B, alpha, sample):
     G.say(f"layer {shape} B={B} alpha={alpha}")
     wdev, whost = G.weights(shape)

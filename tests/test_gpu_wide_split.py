@@ -49,10 +49,13 @@ def test_wide_split_tail(shape, B, alpha, P_expected):
     rng = np.random.default_rng([B, 5])
     picked = set()
     for rb in split_rbs:
-        rows = ss[rb * bm:(rb + 1) * bm]
-        rows = rows[rows >= 0]
-        if len(rows):
-            picked.add(int(rng.choice(rows)) // sh.top_k)
+        # one token in each 64-row quarter of the row-block (each quarter is added
+        # by its own wave and fix-up workgroup)
+        for q in range(bm // 64):
+            rows = ss[rb * bm + q * 64:rb * bm + (q + 1) * 64]
+            rows = rows[rows >= 0]
+            if len(rows):
+                picked.add(int(rng.choice(rows)) // sh.top_k)
     toks = np.array(sorted(picked | set(rng.choice(B, 12, replace=False).tolist())), dtype=np.int32)
     out = G.fetch(G.run(layer, variant=spec.WIDE, wdev=wdev))
     G.check_routing(layer, out)
