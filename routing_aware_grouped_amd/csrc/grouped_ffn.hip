@@ -177,7 +177,13 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& q, float s, u32x4& o
   }
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u = g / (1 + e^-g) * u, with the hardware reciprocal (about 1 ulp):
+// the IEEE divide took about ten instructions per output, a large share of the
+// tile epilogue, for accuracy far below the bf16 output's rounding.  Large
+// negative g: e^-g -> inf, its reciprocal 0, the product 0 (the limit).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 template <typename T>
 __device__ __forceinline__ void store_out(T* p, float v);
@@ -366,6 +372,48 @@ struct Tile {
           store_out<Out>(orow + jn * 16, v);
         }
       }
+  }
+  // The direct-load path's tile stores (bf16 out), staged through this wave's
+  // LDS tile ost of OSTAGE bytes: each 16-row group of the wave's block is
+  // written there row-major (rows padded by 16 bytes), then read back 16 bytes
+  // per lane and stored as contiguous row segments.  Direct from the MFMA layout
+  // a store instruction wrote 2 bytes per lane to four rows.  The sums are read
+  // with acc_read (see store_rows); rows without a slot are not stored, nor
+  // columns past N.  The wave's own LDS operations run in order, so the staging
+  // tile is rewritten only after the previous group's reads.
+  static constexpr int OSTR = NW * 2 + 16;  // staging row stride, bytes
+  static constexpr int OSTAGE = 16 * OSTR;  // staging bytes per wave
+  __device__ __forceinline__ static void store_staged(const FfnArgs& g, const f32x4 (&acc)[NMAT][FM][FN],
+                                                     const int* m, int64_t row0, int n0, int wm,
+                                                     int wn, int lane, uint8_t* ost) {
+    static_assert(WKIND == W_BF16 && sizeof(Out) == 2 && (NW * 2) % 16 == 0 && 64 % (NW * 2 / 16) == 0,
+                  "bf16 rows of whole 16-byte chunks");
+    const int N = PHASE == 1 ? g.I : g.H;
+    const int lr = lane & 15, lq = lane >> 4;
+    constexpr int CPR = NW * 2 / 16;  // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPR;     // rows per read instruction
+    const int rr0 = lane / CPR, ch = lane % CPR;
+    Out* obase = (Out*)(PHASE == 1 ? g.h : g.y_slots) + row0 * N + n0 + wn * NW + ch * 8;
+    const bool col_ok = BN <= 128 || n0 + wn * NW + ch * 8 < N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) {
+          const float v = PHASE == 1 ? silu_mul(acc_read(acc[0][i][jn], c), acc_read(acc[NMAT - 1][i][jn], c))
+                                     : acc_read(acc[0][i][jn], c);
+          *(uint16_t*)(ost + (lq * 4 + c) * OSTR + (jn * 16 + lr) * 2) =
+              __builtin_bit_cast(uint16_t, (__bf16)v);
+        }
+#pragma unroll
+      for (int k = 0; k < 16 / RPI; ++k) {
+        const int r = k * RPI + rr0;
+        const u32x4 d = *(const u32x4*)(ost + r * OSTR + ch * 16);
+        const int rr = wm * MW + i * 16 + r;
+        if (m[rr] >= 0 && col_ok) *(u32x4*)(obase + rr * N) = d;
+      }
+    }
   }
   __device__ __forceinline__ static void store_acc(const FfnArgs& g, const f32x4 (&acc)[NMAT][FM][FN],
                                                   const int* m, int64_t row0, int n0, int wm,
@@ -1047,7 +1095,7 @@ struct Tile {
   template <bool SH, int ND>
   __device__ __forceinline__ static void run_dma(const FfnArgs& g, uint8_t* b0, uint8_t* b1,
                                                  uint8_t* b2, uint8_t* b3, int* meta3, int* pexp,
-                                                 int nb, int nbr, int slot, int G) {
+                                                 uint8_t* ostage, int nb, int nbr, int slot, int G) {
     static_assert(WKIND == W_BF16 && WIDE && WM == 2 && WN == 2 && WK == 1 && KSTEPS == 1 && C == 4,
                   "the direct-load pipeline serves the wide class's bf16 tiles");
     static_assert(ND == 4, "four stage buffers");
@@ -1176,15 +1224,20 @@ struct Tile {
     // A stage's loads in three parts, so that a step can spread its load
     // instructions among its MFMAs: issue_begin (the item's offsets when a new
     // item starts), issue_one(buf, i) for i = 0 .. kDmaInstr - 1, issue_end.
-    int l_soff = 0;
+    int l_soff = 0, l_woff = 0;
     auto issue_begin = [&]() __attribute__((always_inline)) {
       if (l_new) enter_load_tile(l_j);
       l_new = false;
       l_soff = l_s * BK * ASZ;
+      // this wave's LDS offset, opaque to the compiler at every step: each load's
+      // destination is then one scalar add (hoisted, the 32 destinations of the
+      // four buffers were kept in scalar registers, which spilled)
+      l_woff = wave * 64 * 16;
+      asm volatile("" : "+s"(l_woff));
     };
     auto issue_one = [&](uint8_t* buf, int i) __attribute__((always_inline)) {
       typedef __attribute__((address_space(3))) void lds_void;
-      lds_void* dst = (lds_void*)(buf + (i * NT + wave * 64) * 16);
+      lds_void* dst = (lds_void*)(buf + i * NT * 16 + l_woff);
       if (i < 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, l_aoff[i], l_soff, 0, 0);
       else
@@ -1236,34 +1289,38 @@ struct Tile {
 #pragma unroll
       for (int k = 0; k < NMAT * FN + FM; ++k) read_one(buf, k, fa, fb);
     };
-    // the MFMAs of A fragment row i (all of its weight fragments)
-    auto mfma_row = [&](int i, const bf16x8(&fa)[FM], const bf16x8(&fb)[NMAT * FN])
+    // MFMAs q0 .. q1 - 1 of A fragment row i (weight fragment q of each)
+    auto mfmas = [&](int i, int q0, int q1, const bf16x8(&fa)[FM], const bf16x8(&fb)[NMAT * FN])
         __attribute__((always_inline)) {
 #pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-        for (int jn = 0; jn < FN; ++jn)
+      for (int q = 0; q < NMAT * FN; ++q)
+        if (q >= q0 && q < q1)
           asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-                       : "+a"(acc[mt][i][jn])
-                       : "v"(fa[i]), "v"(fb[mt * FN + jn]));
+                       : "+a"(acc[q / FN][i][q % FN])
+                       : "v"(fa[i]), "v"(fb[q]));
     };
-    // One step's work after its barrier, in FM groups, each: one load instruction
-    // of the stage ND ahead, two fragment reads of the next stage and the MFMAs of
-    // one A fragment row of this stage.  A wave per SIMD issues everything itself,
-    // so spreading the loads and LDS reads among the MFMAs keeps the matrix unit
-    // busy while they queue (issued all before the MFMAs, they left it idle for
-    // about half of each step).  Memory operations keep their program order
-    // around the volatile MFMA asm.
-    static_assert(FM == kDmaInstr && 2 * FM == NMAT * FN + FM, "one load and two reads per group");
+    // One step's work after its barrier, in FM groups, each: the MFMAs of one A
+    // fragment row of this stage, with two fragment reads of the next stage and
+    // one load instruction of the stage ND ahead spread among them (read, two
+    // MFMAs, read, two MFMAs, load, four MFMAs).  A wave per SIMD issues
+    // everything itself, so spreading the loads and LDS reads among the MFMAs
+    // keeps the matrix unit busy while they queue: issued all before the MFMAs,
+    // they left it idle for about half of each step; among them, placed as here,
+    // measured fastest of the orders tried.  Memory operations keep their program
+    // order around the volatile MFMA asm.
+    static_assert(FM == kDmaInstr && 2 * FM == NMAT * FN + FM && NMAT * FN == 8,
+                  "one load, two reads and eight MFMAs per group");
     auto groups = [&](uint8_t* dbuf, const uint8_t* rbuf, bf16x8(&nfa)[FM], bf16x8(&nfb)[NMAT * FN],
-                      const bf16x8(&cfa)[FM], const bf16x8(&cfb)[NMAT * FN], bool run)
+                      const bf16x8(&cfa)[FM], const bf16x8(&cfb)[NMAT * FN])
         __attribute__((always_inline)) {
 #pragma unroll
       for (int gi = 0; gi < FM; ++gi) {
-        issue_one(dbuf, gi);
         read_one(rbuf, 2 * gi, nfa, nfb);
+        mfmas(gi, 0, 2, cfa, cfb);
         read_one(rbuf, 2 * gi + 1, nfa, nfb);
-        if (run) mfma_row(gi, cfa, cfb);
+        mfmas(gi, 2, 4, cfa, cfb);
+        issue_one(dbuf, gi);
+        mfmas(gi, 4, 8, cfa, cfb);
       }
     };
 
@@ -1282,9 +1339,10 @@ struct Tile {
     // ahead across items: item j + 1's metadata is fetched at stage se - ND - 1
     // of item j and stored at stage se - ND, before the barrier of the step that
     // issues its first loads (an item of only ND stages fetches it at that step
-    // too).  A wave with any valid row runs all its MFMAs (rows with no slot were
-    // loaded out of range and their sums are never stored); the all-padding test
-    // is taken per item.
+    // too).  Every wave runs all its MFMAs, also on rows with no slot (loaded out
+    // of range as zeros; their sums are never stored): the barrier paces a step
+    // by its slowest wave, so skipping them would save no time, and the test
+    // between MFMAs cost about a tenth of each step.
     fetch_meta(0);
     store_meta(0);
     __syncthreads();
@@ -1296,8 +1354,6 @@ struct Tile {
       const int* m = meta3 + (j % kMetaSlots) * META;
       const int len = item_se(j) - item_sb(j);
       const bool live = (unsigned)__builtin_amdgcn_readfirstlane(m[BM + 1]) < (unsigned)e_end;
-      const int nvalid = __builtin_amdgcn_readfirstlane(m[BM]);
-      const bool run = live && wm * MW < nvalid;
       const bool more = j + 1 < nit;
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
@@ -1317,9 +1373,9 @@ struct Tile {
         wait_vm_bar<(ND - 2) * kDmaInstr>();
         issue_begin();
         if constexpr ((u & 1) == 0)
-          groups(buf_of(u), buf_of((u + 1) % ND), fa1, fb1, fa0, fb0, run);
+          groups(buf_of(u), buf_of((u + 1) % ND), fa1, fb1, fa0, fb0);
         else
-          groups(buf_of(u), buf_of((u + 1) % ND), fa0, fb0, fa1, fb1, run);
+          groups(buf_of(u), buf_of((u + 1) % ND), fa0, fb0, fa1, fb1);
         issue_end();
         // after the item's last MFMAs, the padding before any read of the sums:
         // inside the loop, so every read after it (wherever the compiler places
@@ -1340,7 +1396,7 @@ struct Tile {
         if (j < nwhole) {
           const int rb = __builtin_amdgcn_readfirstlane(m[BM + 2]);
           const int nt = __builtin_amdgcn_readfirstlane(m[BM + 3]);
-          store_rows<FM, true>(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane, 0);
+          store_staged(g, acc, m, (int64_t)rb * BM, nt * BN, wm, wn, lane, ostage + wave * OSTAGE);
         } else {
           // this workgroup's piece: its fp32 sums in MFMA fragment order, 16 bytes
           // per lane, wave-contiguous (wide_fixup adds the pieces).  Buffer
@@ -1717,12 +1773,13 @@ __global__ void __launch_bounds__(wide_threads<WKIND>(), 1) ffn_wide_kernel(FfnA
       __shared__ __attribute__((aligned(16))) uint8_t s2[R::STAGE];
       __shared__ __attribute__((aligned(16))) uint8_t s3[R::STAGE];
       __shared__ int pexp[kRunTable];
+      __shared__ __attribute__((aligned(16))) uint8_t ostage[4 * R::OSTAGE];
       const int K = PHASE == 1 ? g.H : g.I;
       const int slot = xcd_slot(blockIdx.x, gridDim.x);
       // H and I are multiples of 128 (the API checks), so every reduction is whole
       // groups of four 32-deep stages
       if (K % (4 * R::BK) == 0 && K >= 4 * R::BK)
-        R::template run_dma<SH, 4>(g, s0, s1, s2, s3, meta3, pexp, nb, nbr, slot, gridDim.x);
+        R::template run_dma<SH, 4>(g, s0, s1, s2, s3, meta3, pexp, ostage, nb, nbr, slot, gridDim.x);
     } else {
       run_phase<kWideVariant, PHASE, WKIND, SH>(g, lds, meta3, nb, nbr);
     }
@@ -1784,7 +1841,9 @@ hipError_t launch_phase_sh(const FfnArgs& g, int grid_wide, hipStream_t s) {
   constexpr int lds = lds_bytes_stream<PHASE, WKIND>();
   static_assert((lds + meta_bytes) * kWgPerCu <= 160 * 1024, "LDS budget of kWgPerCu workgroups per CU");
   constexpr int ldsw = lds_bytes_wide<PHASE, WKIND>();
-  constexpr int ldsw_static = WKIND == W_BF16 ? 4 * Cfg<kWideVariant, PHASE, W_BF16>::R::STAGE : 0;
+  constexpr int ldsw_static =
+      WKIND == W_BF16 ? 4 * (Cfg<kWideVariant, PHASE, W_BF16>::R::STAGE + Cfg<kWideVariant, PHASE, W_BF16>::R::OSTAGE)
+                      : 0;
   static_assert(ldsw + ldsw_static + meta_bytes + kRunTable * 4 <= 160 * 1024,
                 "LDS budget of one wide workgroup per CU");
   hipError_t e = opt_in_lds((const void*)ffn_kernel<PHASE, WKIND, SH>, lds);
