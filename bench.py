@@ -482,6 +482,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size kernel that scales HBM byte counters) and exit")
+    ap.add_argument("--calibrate-gemm", type=int, default=0, metavar="N",
+                    help="only time a dense bf16 N x N x N torch.mm (the vendor GEMM library on the "
+                         "same GPU: a practical reference for the MFMA-bound rate) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -503,6 +506,26 @@ def main():
             dt = time.perf_counter() - t0
             print(f"copy {args.calibrate_copy} MiB: read {n} B + write {n} B in {dt * 1e6:.1f} us "
                   f"({2 * n / dt / 1e9:.1f} GB/s wall)", flush=True)
+        return
+
+    if args.calibrate_gemm:
+        import torch
+        n = args.calibrate_gemm
+        a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        c = torch.mm(a, b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(4):
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                torch.mm(a, b, out=c)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 10
+            tf = 2.0 * n ** 3 / us / 1e6
+            print(f"bf16 GEMM {n}^3: {us:.1f} us per call, {tf:.1f} TFLOP/s "
+                  f"({tf / (MFMA_BF16_PEAK / 1e12):.3f} of the dense bf16 peak)", flush=True)
         return
 
     import numpy as np
