@@ -1315,12 +1315,17 @@ struct Tile {
         __attribute__((always_inline)) {
 #pragma unroll
       for (int gi = 0; gi < FM; ++gi) {
-        read_one(rbuf, 2 * gi, nfa, nfb);
+        // fragment reads front-loaded: three in each of groups 0-3, two in 4-5
+        constexpr int kR[FM + 1] = {0, 3, 6, 9, 12, 14, 16, 16, 16};
+        const int r0 = kR[gi], nr = kR[gi + 1] - kR[gi];
+        if (nr > 0) read_one(rbuf, r0, nfa, nfb);
         mfmas(gi, 0, 2, cfa, cfb);
-        read_one(rbuf, 2 * gi + 1, nfa, nfb);
+        if (nr > 1) read_one(rbuf, r0 + 1, nfa, nfb);
         mfmas(gi, 2, 4, cfa, cfb);
+        if (nr > 2) read_one(rbuf, r0 + 2, nfa, nfb);
+        mfmas(gi, 4, 6, cfa, cfb);
         issue_one(dbuf, gi);
-        mfmas(gi, 4, 8, cfa, cfb);
+        mfmas(gi, 6, 8, cfa, cfb);
       }
     };
 
