@@ -113,6 +113,9 @@ def work(layer, ids_np):
                 counts=np.concatenate([cnt, np.full(nsh, B, dtype=cnt.dtype)]))
 
 
+PACK = None  # layer.allocate's pack argument (--pack)
+
+
 def roof_us(w):
     return max(w["layer_bytes"] / HBM_PEAK, w["mfma_s"]) * 1e6
 
@@ -223,7 +226,7 @@ def device_weights(wdev):
 def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, V, reps, warmup,
               exhaustive=True, rep=0, force=None):
     layer = synth.make_layer(shape, tokens, alpha, rep, weights=whost)
-    b = L.from_layer(layer, theta=theta, weights=device_weights(wdev))
+    b = L.from_layer(layer, theta=theta, weights=device_weights(wdev), pack=PACK)
     L.forward(b)
     torch.cuda.synchronize()
     ids = b.topk_ids.cpu().numpy()
@@ -482,10 +485,15 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size kernel that scales HBM byte counters) and exit")
+    ap.add_argument("--pack", type=int, default=1,
+                    help="1: bf16 layers give the wide configuration its packed weight copy "
+                         "(moe_pack_wide, written once per weight set before timing); 0: row-major")
     ap.add_argument("--calibrate-gemm", type=int, default=0, metavar="N",
                     help="only time a dense bf16 N x N x N torch.mm (the vendor GEMM library on the "
                          "same GPU: a practical reference for the MFMA-bound rate) and exit")
     args = ap.parse_args()
+    global PACK
+    PACK = None if args.pack else False
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the layer runs on one GPU "

@@ -132,6 +132,15 @@ typedef struct moe_problem {
                             lane of the combine).  Their weights follow the local
                             experts' in W1, W3, W2 (and s1, s3, s2): those arrays
                             hold E_loc + S_sh experts.                          */
+  const void* packed_weights; /* NULL (default), or a copy of W1, W3 and W2 that
+                            moe_pack_wide wrote for this problem's shapes (device
+                            memory, 256-byte aligned, owned by the caller, not
+                            modified by any call).  When set, the wide
+                            configuration's bf16 tiles read their weights from it
+                            instead of W1, W3, W2; every other configuration
+                            reads W1, W3, W2 as always, so those stay required.
+                            Only for act_dtype = weight_dtype = MOE_BF16
+                            (MOE_ERR_INVALID_ARG otherwise).                    */
 } moe_problem;
 
 /* Buffer sizes a caller must provide for one problem. */
@@ -307,6 +316,30 @@ moe_status moe_grouped_ffn_noalloc(const moe_problem* p, const void* x, const vo
 
 /* Size in bytes of the per-GPU array moe_grouped_ffn_noalloc works in. */
 int64_t moe_noalloc_workspace_limit(void);
+
+/* Weight prepack for the wide configuration (GC-MoE, arXiv 2611.04222, section
+ * 4: a weight transform, run once per weight set on the caller's stream, that
+ * makes each tile's reduction blocks contiguous and interleaves gate and up;
+ * RaMP appendix A.8 loads gate and up weights interleaved).  The copy holds, for
+ * every expert e (E_loc + S_sh of them), in this order:
+ *   gate/up: for each column tile n of ceil(I / 128), for each 32-deep block kb
+ *     of H: 256 rows of 64 bytes, rows 0-127 = W1_e[128 n + r][32 kb .. 32 kb + 31],
+ *     rows 128-255 = W3_e of the same rows (rows past I are zeros);
+ *   then down, for every expert: for each column tile n of ceil(H / 256), for each
+ *     32-deep block kb of I: 256 rows of 64 bytes, W2_e[256 n + r][32 kb ..]
+ *     (rows past H zeros).
+ * Each 16 KiB block is one pipeline stage of that configuration's tile, so a
+ * stage's weight loads read 16 KiB of consecutive bytes instead of 64 bytes of
+ * each of 256 rows.
+ * moe_pack_wide_bytes: *bytes = the copy's size (2 * E * ceil(I/128) * 128 * H + E *
+ * ceil(H/256) * 256 * I bf16 values).  moe_pack_wide: writes the copy to packed
+ * (device, 256-byte aligned, *bytes) from W1, W3, W2 ([E][I][H], [E][I][H],
+ * [E][H][I] bf16, device); enqueued on stream, asynchronous.  Errors:
+ * MOE_ERR_INVALID_ARG (NULL pointers, misalignment, p not bf16 or with
+ * packed_weights set), MOE_ERR_UNSUPPORTED, MOE_ERR_HIP. */
+moe_status moe_pack_wide_bytes(const moe_problem* p, int64_t* bytes);
+moe_status moe_pack_wide(const moe_problem* p, const void* w1, const void* w3, const void* w2,
+                         void* packed, void* stream);
 
 /* Step 4a alone: the grouped gate/up GEMM with the fused SwiGLU, writing h into
  * workspace (as moe_grouped_ffn's first launch; with act_quant = 1 it is preceded

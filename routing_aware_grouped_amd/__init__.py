@@ -36,7 +36,7 @@ class moe_problem(ctypes.Structure):  # noqa: N801  (C struct name)
                 ("local_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("act_quant", ctypes.c_int32),
-                ("shared_experts", ctypes.c_int32)]
+                ("shared_experts", ctypes.c_int32), ("packed_weights", ctypes.c_void_p)]
 
 
 class moe_sizes(ctypes.Structure):  # noqa: N801
@@ -47,10 +47,11 @@ class moe_sizes(ctypes.Structure):  # noqa: N801
 
 def problem(tokens, hidden, inter, num_experts, top_k, *, expert_begin=0, local_experts=None,
             act_dtype=MOE_BF16, weight_dtype=MOE_BF16, renormalize=1, act_quant=0,
-            shared_experts=0) -> moe_problem:
+            shared_experts=0, packed_weights=None) -> moe_problem:
     return moe_problem(tokens, hidden, inter, num_experts, expert_begin,
                        num_experts if local_experts is None else local_experts, top_k,
-                       act_dtype, weight_dtype, renormalize, act_quant, shared_experts)
+                       act_dtype, weight_dtype, renormalize, act_quant, shared_experts,
+                       _ptr(packed_weights))
 
 
 _lib = None
@@ -78,6 +79,8 @@ _SIGS = {
     "moe_grouped_ffn_noalloc": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P, P, P,
                                  P], ctypes.c_int),
     "moe_noalloc_workspace_limit": ([], ctypes.c_int64),
+    "moe_pack_wide_bytes": ([ctypes.POINTER(moe_problem), P], ctypes.c_int),
+    "moe_pack_wide": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
 }
 
 
@@ -201,6 +204,17 @@ def moe_grouped_ffn_noalloc(p, x, w1, w3, w2, s1, s3, s2, sorted_slots, block_ex
 
 def moe_noalloc_workspace_limit() -> int:
     return int(lib().moe_noalloc_workspace_limit())
+
+
+def moe_pack_wide_bytes(p: moe_problem) -> int:
+    out = ctypes.c_int64(0)
+    _check("moe_pack_wide_bytes", lib().moe_pack_wide_bytes(_pp(p), ctypes.byref(out)))
+    return int(out.value)
+
+
+def moe_pack_wide(p, w1, w3, w2, packed, stream=None):
+    _check("moe_pack_wide", lib().moe_pack_wide(_pp(p), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(packed),
+                                                _stream(stream)))
 
 
 def moe_grouped_gate_up(p, x, w1, w3, s1, s3, sorted_slots, block_expert, num_blocks, variant,

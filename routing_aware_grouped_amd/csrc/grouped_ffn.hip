@@ -222,6 +222,7 @@ struct FfnArgs {
   int n_shared;     // shared experts (row-blocks after the routed ones)
   int32_t* status;  // device status word (MOE_DEV_* bits)
   int grid_stream;  // workgroups of the streaming class's launch (its fix-up needs it)
+  const uint8_t* wpk;  // the wide configuration's packed bf16 weights (moe_pack_wide), or null
 };
 
 // ring slots of per-tile metadata (see Tile::run_all)
@@ -1186,12 +1187,22 @@ struct Tile {
                                         : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
     uint32_t l_aoff[4] = {kOob, kOob, kOob, kOob};
+    // Weights from the packed copy (moe_pack_wide): each stage of a tile is one
+    // 256-row block of 64-byte rows (gate/up: W1's 128 rows, then W3's), so
+    // instruction i reads block rows 64 i .. 64 i + 63; else from W1/W3/W2 rows.
+    const bool pk = g.wpk != nullptr;
     uint32_t l_boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = NMAT == 2 ? (i & 1) * 64 + (tid >> 2) : i * 64 + (tid >> 2);
-      l_boff[i] = (uint32_t)(rr * K + c_log * 8) * WSZ;
+      const int rr = pk || NMAT == 1 ? i * 64 + (tid >> 2) : (i & 1) * 64 + (tid >> 2);
+      l_boff[i] = (uint32_t)rr * (pk ? 64u : (uint32_t)K * WSZ) + c_log * 16;
     }
+    static_assert(ROWB == 64 && BM == 256 && NMAT * BN == 256, "packed blocks are 256 rows x 64 bytes");
+    constexpr uint32_t kPkBlock = 256 * 64;  // bytes of one packed stage
+    // this phase's region of the packed copy: gate/up first, then down
+    const int64_t pk_region = PHASE == 1 ? 0
+                                         : (int64_t)(g.E_loc + g.n_shared) * ((g.I + 127) / 128) *
+                                               (g.H / 32) * kPkBlock;
     __amdgpu_buffer_rsrc_t l_b_rsrc[2];
     int l_j = 0, l_s = item_sb(0), l_se = item_se(0);
     bool l_new = true;
@@ -1206,10 +1217,17 @@ struct Tile {
         e = 0;
         n0 = 0;
       }
-      const int64_t wrow0 = ((int64_t)e * N + n0) * K;
-      const uint32_t wbytes = eok ? (uint32_t)(N - n0) * (uint32_t)K * WSZ : 0u;
-      l_b_rsrc[0] = make_rsrc(wmat0 + wrow0, wbytes);
-      l_b_rsrc[1] = make_rsrc(wmat1 + wrow0, wbytes);
+      if (pk) {
+        // the tile's nst consecutive blocks; rows past N are zeros in the copy
+        const uint8_t* tb = g.wpk + pk_region + ((int64_t)e * ncol + (eok ? nt : 0)) * nst * kPkBlock;
+        l_b_rsrc[0] = make_rsrc(tb, eok ? (uint32_t)nst * kPkBlock : 0u);
+        l_b_rsrc[1] = l_b_rsrc[0];
+      } else {
+        const int64_t wrow0 = ((int64_t)e * N + n0) * K;
+        const uint32_t wbytes = eok ? (uint32_t)(N - n0) * (uint32_t)K * WSZ : 0u;
+        l_b_rsrc[0] = make_rsrc(wmat0 + wrow0, wbytes);
+        l_b_rsrc[1] = make_rsrc(wmat1 + wrow0, wbytes);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = i * 64 + (tid >> 2);
@@ -1224,11 +1242,12 @@ struct Tile {
     // A stage's loads in three parts, so that a step can spread its load
     // instructions among its MFMAs: issue_begin (the item's offsets when a new
     // item starts), issue_one(buf, i) for i = 0 .. kDmaInstr - 1, issue_end.
-    int l_soff = 0, l_woff = 0;
+    int l_soff = 0, l_bsoff = 0, l_woff = 0;
     auto issue_begin = [&]() __attribute__((always_inline)) {
       if (l_new) enter_load_tile(l_j);
       l_new = false;
       l_soff = l_s * BK * ASZ;
+      l_bsoff = pk ? l_s * (int)kPkBlock : l_soff;
       // this wave's LDS offset, opaque to the compiler at every step: each load's
       // destination is then one scalar add (hoisted, the 32 destinations of the
       // four buffers were kept in scalar registers, which spilled)
@@ -1242,7 +1261,7 @@ struct Tile {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, l_aoff[i], l_soff, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(l_b_rsrc[NMAT == 2 ? (i - 4) >> 1 : 0], dst, 16,
-                                                 l_boff[i - 4], l_soff, 0, 0);
+                                                 l_boff[i - 4], l_bsoff, 0, 0);
     };
     auto issue_end = [&]() __attribute__((always_inline)) {
       if (++l_s == l_se) {  // past the last item the offsets are out of range
@@ -1889,7 +1908,52 @@ hipError_t launch_w(const FfnArgs& g, int phases, int grid, hipStream_t s) {
   return hipSuccess;
 }
 
+// Writes the wide configuration's packed weight copy (include/moe.h,
+// moe_pack_wide): chunk q (16 bytes) of a region is bytes 16 (q % 4) .. of row
+// (q / 4) % 256 of block q / 1024; a block is one 32-deep stage of one expert's
+// column tile (gate/up: rows 0-127 from W1, 128-255 from W3; down: W2), and rows
+// past the matrix's end are zeros.
+__global__ void __launch_bounds__(256) pack_wide_kernel(const uint16_t* w1, const uint16_t* w3,
+                                                        const uint16_t* w2, u32x4* out, int E, int H,
+                                                        int I) {
+  const int64_t ncol1 = (I + 127) / 128, nst1 = H / 32, ncol2 = (H + 255) / 256, nst2 = I / 32;
+  const int64_t n1 = (int64_t)E * ncol1 * nst1 * 1024;
+  const int64_t n2 = (int64_t)E * ncol2 * nst2 * 1024;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n1 + n2;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const bool gu = q < n1;
+    const int64_t qq = gu ? q : q - n1;
+    const int64_t blk = qq >> 10;
+    const int r = (int)((qq >> 2) & 255), c = (int)(qq & 3);
+    const int64_t nst = gu ? nst1 : nst2, ncol = gu ? ncol1 : ncol2;
+    const int64_t kb = blk % nst, nt = (blk / nst) % ncol, e = blk / (nst * ncol);
+    const uint16_t* src = gu ? (r < 128 ? w1 : w3) : w2;
+    const int64_t row = gu ? nt * 128 + (r & 127) : nt * 256 + r;
+    const int64_t N = gu ? I : H, K = gu ? H : I;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < N) v = *(const u32x4*)(src + (e * N + row) * K + kb * 32 + c * 8);
+    out[q] = v;
+  }
+}
+
 }  // namespace
+
+int64_t pack_wide_bytes(const moe_problem& p) {
+  const int64_t E = (int64_t)p.local_experts + p.shared_experts;
+  const int64_t H = p.hidden, I = p.inter;
+  return 2 * E * ((I + 127) / 128 * 128) * H * 2 + E * ((H + 255) / 256 * 256) * I * 2;
+}
+
+hipError_t launch_pack_wide(const moe_problem& p, const void* w1, const void* w3, const void* w2,
+                            void* packed, hipStream_t s) {
+  const int64_t chunks = pack_wide_bytes(p) / 16;
+  const int64_t want = (chunks + 255) / 256;
+  const int grid = (int)(want < 4096 ? want : 4096);
+  pack_wide_kernel<<<grid, 256, 0, s>>>((const uint16_t*)w1, (const uint16_t*)w3, (const uint16_t*)w2,
+                                        (u32x4*)packed, p.local_experts + p.shared_experts, p.hidden,
+                                        p.inter);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, const uint8_t* xq,
                               const float* xs, const uint8_t* hq, const float* hs, const void* w1,
@@ -1902,7 +1966,8 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
   const int grid = num_cus < kMaxGrid ? num_cus : kMaxGrid;  // the wide class's launch
   FfnArgs g{x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks, variant,
             h, y_slots, part, p.hidden, p.inter, p.top_k, p.local_experts,
-            p.tokens * p.top_k, rows_max, nullptr, p.shared_experts, status, grid_stream};
+            p.tokens * p.top_k, rows_max, nullptr, p.shared_experts, status, grid_stream,
+            (const uint8_t*)p.packed_weights};
   switch (p.weight_dtype) {
     case MOE_F32: return launch_w<W_F32>(g, phases, grid, s);
     case MOE_BF16: return launch_w<W_BF16>(g, phases, grid, s);

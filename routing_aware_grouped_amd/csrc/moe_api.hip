@@ -90,6 +90,9 @@ moe_status validate(const moe_problem* p) {
   if (!ok) return MOE_ERR_UNSUPPORTED;
   // the FP8 activation path: bf16 activations quantized for fp8-weight GEMMs
   if (p->act_quant && !(a == MOE_BF16 && w == MOE_FP8_E4M3)) return MOE_ERR_UNSUPPORTED;
+  // the wide configuration's packed weight copy: bf16 problems only
+  if (p->packed_weights && (!(a == MOE_BF16 && w == MOE_BF16) || !aligned(p->packed_weights, 256)))
+    return MOE_ERR_INVALID_ARG;
   // 32-bit slot and row indices
   const int64_t slots = (int64_t)p->tokens * p->top_k;
   if (slots >= (1ll << 30)) return MOE_ERR_UNSUPPORTED;
@@ -186,7 +189,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 6; }
+int32_t moe_abi_version(void) { return 7; }
 
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
@@ -403,6 +406,26 @@ moe_status moe_grouped_ffn_noalloc(const moe_problem* p, const void* x, const vo
 }
 
 int64_t moe_noalloc_workspace_limit(void) { return kScratchBytes; }
+
+moe_status moe_pack_wide_bytes(const moe_problem* p, int64_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->act_dtype != MOE_BF16 || p->weight_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  *bytes = pack_wide_bytes(*p);
+  return MOE_OK;
+}
+
+moe_status moe_pack_wide(const moe_problem* p, const void* w1, const void* w3, const void* w2,
+                         void* packed, void* stream) {
+  const moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->act_dtype != MOE_BF16 || p->weight_dtype != MOE_BF16 || p->packed_weights) return MOE_ERR_INVALID_ARG;
+  if (!w1 || !w3 || !w2 || !packed || !aligned(packed, 256) || !aligned(w1, 16) || !aligned(w3, 16) ||
+      !aligned(w2, 16))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack_wide(*p, w1, w3, w2, packed, (hipStream_t)stream));
+}
 
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x, const void* w1, const void* w3,
                            const void* w2, const float* s1, const float* s3, const float* s2,

@@ -164,6 +164,11 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
                               const int32_t* block_expert, const int32_t* num_blocks,
                               const int32_t* variant, void* y_slots, void* h, float* part,
                               int32_t* status, int num_cus, int64_t rows_max, hipStream_t s);
+// The wide configuration's packed weight copy (include/moe.h, moe_pack_wide):
+// its size in bytes, and the launch that writes it from W1, W3, W2.
+int64_t pack_wide_bytes(const moe_problem& p);
+hipError_t launch_pack_wide(const moe_problem& p, const void* w1, const void* w3, const void* w2,
+                            void* packed, hipStream_t s);
 // num_blocks / variant: device values of the sort, needed with shared experts only
 hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
                           const float* w, const int32_t* num_blocks, const int32_t* variant,

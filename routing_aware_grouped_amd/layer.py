@@ -14,7 +14,8 @@ import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_combine_shared,
                moe_grouped_down,
-               moe_grouped_ffn, moe_grouped_gate_up, moe_num_variants, moe_problem,
+               moe_grouped_ffn, moe_grouped_gate_up, moe_num_variants, moe_pack_wide,
+               moe_pack_wide_bytes, moe_problem,
                moe_query_sizes, moe_route_select_align, moe_route_topk, moe_select_config)
 
 _TORCH_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
@@ -44,12 +45,35 @@ class Buffers:
     y_slots: torch.Tensor
     workspace: torch.Tensor
     y: torch.Tensor
+    packed: torch.Tensor | None = None  # the wide configuration's packed weights
+
+
+def packed_weights(p: moe_problem, w1, w3, w2, stream=None) -> torch.Tensor:
+    """The wide configuration's packed copy of bf16 device weights (moe_pack_wide),
+    written once per weight set: it is kept on w1 and reused while the problem's
+    shapes, the three tensors and their contents (in-place version counters) are
+    unchanged."""
+    key = (p.local_experts, p.shared_experts, p.hidden, p.inter, w3.data_ptr(), w2.data_ptr(),
+           w1._version, w3._version, w2._version)
+    cached = getattr(w1, "_moe_wide_pack", None)
+    if cached is not None and cached[0] == key:
+        return cached[1]
+    q = moe_problem.from_buffer_copy(p)
+    q.packed_weights = None
+    t = torch.empty(moe_pack_wide_bytes(q), dtype=torch.uint8, device=w1.device)
+    moe_pack_wide(q, w1, w3, w2, t, stream)
+    w1._moe_wide_pack = (key, t)
+    return t
 
 
 def allocate(p: moe_problem, logits, x, w1, w3, w2, s1=None, s3=None, s2=None, theta=None,
-             device="cuda") -> Buffers:
+             device="cuda", pack=None) -> Buffers:
     """Output/intermediate buffers sized by moe_query_sizes; inputs are moved to
-    the device as given (already dtype-encoded)."""
+    the device as given (already dtype-encoded).  pack (default: bf16 problems)
+    gives the wide configuration its packed weight copy (packed_weights)."""
+    p = moe_problem.from_buffer_copy(p)
+    if pack is None:
+        pack = p.act_dtype == MOE_BF16 and p.weight_dtype == MOE_BF16
     sz = moe_query_sizes(p)
     B, k, El = p.tokens, p.top_k, p.local_experts
     V = moe_num_variants()
@@ -61,8 +85,14 @@ def allocate(p: moe_problem, logits, x, w1, w3, w2, s1=None, s3=None, s2=None, t
 
     if theta is None:
         theta = torch.zeros(V, 4, dtype=torch.float32)
+    w1, w3, w2 = d(w1), d(w3), d(w2)
+    packed = None
+    if pack:
+        p.packed_weights = None
+        packed = packed_weights(p, w1, w3, w2)
+        p.packed_weights = packed.data_ptr()
     return Buffers(
-        p=p, logits=d(logits), x=d(x), w1=d(w1), w3=d(w3), w2=d(w2), s1=d(s1), s3=d(s3), s2=d(s2),
+        p=p, logits=d(logits), x=d(x), w1=w1, w3=w3, w2=w2, s1=d(s1), s3=d(s3), s2=d(s2),
         theta=d(theta),
         topk_ids=torch.empty(B, k, dtype=torch.int32, device=dev),
         topk_w=torch.empty(B, k, dtype=torch.float32, device=dev),
@@ -76,6 +106,7 @@ def allocate(p: moe_problem, logits, x, w1, w3, w2, s1=None, s3=None, s2=None, t
         y_slots=torch.empty(sz.rows_max, p.hidden, dtype=act, device=dev),
         workspace=torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=dev),
         y=torch.empty(B, p.hidden, dtype=act, device=dev),
+        packed=packed,
     )
 
 
@@ -168,15 +199,16 @@ def problem_of(layer, renormalize: int = 1) -> moe_problem:
     sh = layer.shape
     return moe_problem(layer.tokens, sh.hidden, sh.inter, sh.num_experts, layer.expert_begin,
                        sh.local_experts, sh.top_k, sh.act_dtype, sh.weight_dtype, renormalize,
-                       getattr(sh, "act_quant", 0), getattr(sh, "shared", 0))
+                       getattr(sh, "act_quant", 0), getattr(sh, "shared", 0), None)
 
 
-def from_layer(layer, theta=None, device="cuda", weights=None, renormalize: int = 1) -> Buffers:
+def from_layer(layer, theta=None, device="cuda", weights=None, renormalize: int = 1,
+               pack=None) -> Buffers:
     """Buffers for a synthetic layer (see synth.Layer); `weights` reuses device
-    weight tensors (w1, w3, w2, s1, s3, s2) across loads."""
+    weight tensors (w1, w3, w2, s1, s3, s2) across loads (and their packed copy)."""
     p = problem_of(layer, renormalize)
     if weights is None:
         weights = weight_tensors(layer)
     w1, w3, w2, s1, s3, s2 = weights
     return allocate(p, torch.from_numpy(layer.logits), act_tensor(layer, layer.x), w1, w3, w2, s1,
-                    s3, s2, theta=theta, device=device)
+                    s3, s2, theta=theta, device=device, pack=pack)

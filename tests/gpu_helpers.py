@@ -58,11 +58,13 @@ def device_weights(layer, wdev=None):
     return tuple(None if t is None else t.cuda() for t in L.weight_tensors(layer))
 
 
-def run(layer, variant: int | None = None, theta=None, wdev=None, renormalize: int = 1):
+def run(layer, variant: int | None = None, theta=None, wdev=None, renormalize: int = 1,
+        pack=None):
     """Whole layer on the GPU.  variant=None: the select step chooses with theta;
-    else configuration `variant` is forced."""
+    else configuration `variant` is forced.  pack: see layer.allocate (default:
+    bf16 layers give the wide configuration its packed weight copy)."""
     b = L.from_layer(layer, theta=theta if theta is not None else theta_forcing(0),
-                     weights=device_weights(layer, wdev), renormalize=renormalize)
+                     weights=device_weights(layer, wdev), renormalize=renormalize, pack=pack)
     if variant is not None:
         b.variant.fill_(variant)
     torch.cuda.synchronize()

@@ -82,3 +82,36 @@ def expert_major_tile(t: int, block_expert, ncol: int):
     n = sum(1 for x in be if x == e)
     local = t - s0 * ncol
     return s0 + local % n, local // n
+
+
+def pack_wide_bytes(E: int, H: int, I: int) -> int:
+    """Bytes of the wide configuration's packed weight copy (include/moe.h,
+    moe_pack_wide) for E experts: gate/up blocks of 128 W1 rows and 128 W3 rows,
+    then down blocks of 256 W2 rows, each 32 bf16 values deep."""
+    return 2 * E * (-(-I // 128) * 128) * H * 2 + E * (-(-H // 256) * 256) * I * 2
+
+
+def pack_wide(w1, w3, w2):
+    """The packed copy as uint16 words, written out from the header's description:
+    per expert, per column tile, per 32-deep block, 256 rows of 32 values (rows past
+    the matrix's end are zeros); gate/up for every expert first, then down."""
+    import numpy as np
+    E, I, H = w1.shape
+    out = []
+    for e in range(E):
+        for n in range(-(-I // 128)):
+            for kb in range(H // 32):
+                blk = np.zeros((256, 32), np.uint16)
+                r1 = w1[e, n * 128:(n + 1) * 128, kb * 32:(kb + 1) * 32]
+                r3 = w3[e, n * 128:(n + 1) * 128, kb * 32:(kb + 1) * 32]
+                blk[:r1.shape[0]] = r1
+                blk[128:128 + r3.shape[0]] = r3
+                out.append(blk)
+    for e in range(E):
+        for n in range(-(-H // 256)):
+            for kb in range(I // 32):
+                blk = np.zeros((256, 32), np.uint16)
+                r2 = w2[e, n * 256:(n + 1) * 256, kb * 32:(kb + 1) * 32]
+                blk[:r2.shape[0]] = r2
+                out.append(blk)
+    return np.concatenate([b.ravel() for b in out])

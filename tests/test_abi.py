@@ -34,7 +34,7 @@ def test_binding_mirrors_names():
 
 
 def test_variant_menu_matches_spec():
-    assert moe.moe_abi_version() == 6
+    assert moe.moe_abi_version() == 7
     assert moe.moe_num_variants() == len(spec.MENU)
     for v, m in enumerate(spec.MENU):
         assert tuple(moe.moe_variant_info(v)) == m
@@ -216,3 +216,52 @@ def test_noalloc_refuses_problems_beyond_its_array():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_grouped_ffn_noalloc(p, d, d, d, d, d, d, d, d, d, d, d, d, stream=0)
     assert ei.value.status == moe.MOE_ERR_WORKSPACE
+
+
+def test_packed_weights_only_for_bf16_problems():
+    """The wide configuration's packed copy: its size follows the header's layout;
+    problems that are not bf16, a misaligned copy, and packing a problem that
+    already names a copy are rejected before anything runs."""
+    p = _p(act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16, hidden=384, inter=256,
+           local_experts=5, shared_experts=1)
+    assert moe.moe_pack_wide_bytes(p) == spec.pack_wide_bytes(6, 384, 256)
+    q = _p()  # fp32
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_pack_wide_bytes(q)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    q.packed_weights = 1 << 20
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_query_sizes(q)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    p.packed_weights = (1 << 20) + 128  # not 256-byte aligned
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_query_sizes(p)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    p.packed_weights = 1 << 20
+    moe.moe_query_sizes(p)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_pack_wide(p, 1 << 20, 1 << 21, 1 << 22, 1 << 23, 0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_pack_layout_restatement_small():
+    """spec.pack_wide on a hand-checkable case: element (e, row, k) of W1 lands at
+    block (e, row // 128, k // 32), row row % 128, column k % 32."""
+    import numpy as np
+    E, I, H = 2, 256, 64
+    w1 = np.arange(E * I * H, dtype=np.uint16).reshape(E, I, H)
+    w3 = (w1 + 7).astype(np.uint16)
+    w2 = np.arange(E * H * I, dtype=np.uint16).reshape(E, H, I) ^ 0x5555
+    pk = spec.pack_wide(w1, w3, w2)
+    assert pk.size * 2 == spec.pack_wide_bytes(E, H, I)
+    nst, ncol = H // 32, I // 128
+    for (e, r, k) in ((0, 0, 0), (1, 200, 37), (0, 129, 63)):
+        blk = (e * ncol + r // 128) * nst + k // 32
+        assert pk[blk * 256 * 32 + (r % 128) * 32 + k % 32] == w1[e, r, k]
+        assert pk[blk * 256 * 32 + (128 + r % 128) * 32 + k % 32] == w3[e, r, k]
+    base = E * ncol * nst * 256 * 32
+    for (e, r, k) in ((1, 63, 255), (0, 5, 40)):
+        blk = e * 1 * (I // 32) + k // 32  # one down column tile (H = 64 < 256)
+        assert pk[base + blk * 256 * 32 + r * 32 + k % 32] == w2[e, r, k]
+    # rows 64..255 of each down block are zeros (H = 64)
+    assert not pk[base:].reshape(-1, 256, 32)[:, 64:].any()
