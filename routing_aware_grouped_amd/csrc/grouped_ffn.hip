@@ -382,6 +382,14 @@ struct Tile {
   // with acc_read (see store_rows); rows without a slot are not stored, nor
   // columns past N.  The wave's own LDS operations run in order, so the staging
   // tile is rewritten only after the previous group's reads.
+  // h of the wide configuration's bf16 tiles (written by the gate/up phase,
+  // read by the down phase; workspace only): per row-block rb, per 32-deep block
+  // kb of I, 256 rows of 64 bytes, so each down stage reads 16 KiB of
+  // consecutive bytes, as from the packed weights.  Byte offset of row-block rb's
+  // row 0 at column col (a multiple of 8); row r adds 64 r.
+  __device__ __forceinline__ static int64_t hblock_offset(const FfnArgs& g, int64_t rb, int col) {
+    return (rb * (g.I / 32) + col / 32) * (256 * 64) + (col % 32) * 2;
+  }
   static constexpr int OSTR = NW * 2 + 16;  // staging row stride, bytes
   static constexpr int OSTAGE = 16 * OSTR;  // staging bytes per wave
   __device__ __forceinline__ static void store_staged(const FfnArgs& g, const f32x4 (&acc)[NMAT][FM][FN],
@@ -394,8 +402,11 @@ struct Tile {
     constexpr int CPR = NW * 2 / 16;  // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;     // rows per read instruction
     const int rr0 = lane / CPR, ch = lane % CPR;
-    Out* obase = (Out*)(PHASE == 1 ? g.h : g.y_slots) + row0 * N + n0 + wn * NW + ch * 8;
-    const bool col_ok = BN <= 128 || n0 + wn * NW + ch * 8 < N;
+    // gate/up: h in 32-deep blocks per row-block (hblock_offset); down: y_slots rows
+    const int col = n0 + wn * NW + ch * 8;
+    Out* obase = (Out*)g.y_slots + row0 * N + col;
+    uint8_t* hbase = (uint8_t*)g.h + hblock_offset(g, row0 / BM, col);
+    const bool col_ok = BN <= 128 || col < N;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -412,7 +423,12 @@ struct Tile {
         const int r = k * RPI + rr0;
         const u32x4 d = *(const u32x4*)(ost + r * OSTR + ch * 16);
         const int rr = wm * MW + i * 16 + r;
-        if (m[rr] >= 0 && col_ok) *(u32x4*)(obase + rr * N) = d;
+        if (m[rr] >= 0 && col_ok) {
+          if constexpr (PHASE == 1)
+            *(u32x4*)(hbase + rr * 64) = d;
+          else
+            *(u32x4*)(obase + rr * N) = d;
+        }
       }
     }
   }
@@ -1183,9 +1199,9 @@ struct Tile {
     // Instructions 0-3 take A rows 0-255, 4-7 weight rows 0-255 (gate/up: W1 rows
     // n0 .. n0 + 127, then the same rows of W3; down: W2).
     const int c_log = (tid & 3) ^ ((tid >> 3) & 3);  // swz<4>(64 i + tid / 4)
-    const uint32_t a_bytes = PHASE == 1 ? (uint32_t)Btok * (uint32_t)K * ASZ
-                                        : (uint32_t)g.rows_max * (uint32_t)K * ASZ;
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, a_bytes);
+    // gate/up: x rows through one descriptor; down: the row-block's blocks of h
+    // (hblock_offset), a descriptor per item
+    __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(abase, PHASE == 1 ? (uint32_t)Btok * (uint32_t)K * ASZ : 0u);
     uint32_t l_aoff[4] = {kOob, kOob, kOob, kOob};
     // Weights from the packed copy (moe_pack_wide): each stage of a tile is one
     // 256-row block of 64-byte rows (gate/up: W1's 128 rows, then W3's), so
@@ -1228,14 +1244,21 @@ struct Tile {
         l_b_rsrc[0] = make_rsrc(wmat0 + wrow0, wbytes);
         l_b_rsrc[1] = make_rsrc(wmat1 + wrow0, wbytes);
       }
+      if constexpr (PHASE == 2)
+        a_rsrc = make_rsrc((const uint8_t*)g.h + hblock_offset(g, eok ? rb : 0, 0),
+                           eok ? (uint32_t)nst * 256u * 64u : 0u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = i * 64 + (tid >> 2);
         const int sl = m[row];
         l_aoff[i] = kOob;
         if (eok && sl >= 0 && sl < slot_end) {
-          const int arow = PHASE == 1 ? (SH && sl >= g.slots ? sl - g.slots : sl / g.k) : rb * BM + row;
-          l_aoff[i] = (uint32_t)(arow * K + c_log * 8) * ASZ;
+          if constexpr (PHASE == 1) {
+            const int arow = SH && sl >= g.slots ? sl - g.slots : sl / g.k;
+            l_aoff[i] = (uint32_t)(arow * K + c_log * 8) * ASZ;
+          } else {
+            l_aoff[i] = (uint32_t)(row * 64 + c_log * 16);
+          }
         }
       }
     };
@@ -1246,8 +1269,8 @@ struct Tile {
     auto issue_begin = [&]() __attribute__((always_inline)) {
       if (l_new) enter_load_tile(l_j);
       l_new = false;
-      l_soff = l_s * BK * ASZ;
-      l_bsoff = pk ? l_s * (int)kPkBlock : l_soff;
+      l_soff = PHASE == 1 ? l_s * BK * ASZ : l_s * 256 * 64;  // x rows; blocks of h
+      l_bsoff = pk ? l_s * (int)kPkBlock : l_s * BK * WSZ;
       // this wave's LDS offset, opaque to the compiler at every step: each load's
       // destination is then one scalar add (hoisted, the 32 destinations of the
       // four buffers were kept in scalar registers, which spilled)
