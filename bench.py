@@ -250,6 +250,14 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
                counts=[int(c) for c in w["counts"]], t_hat=[round(x, 4) for x in t_hat])
     res["binding"] = "hbm" if w["layer_bytes"] / HBM_PEAK >= w["mfma_s"] else "mfma"
     res["roof_frac"] = round(res["roof_us"] / res["us"], 4)
+    if force is None and L.choose_plan(b.p, "auto") == "fused":
+        # the fused small-batch plan on the same load (the chooser's labels below
+        # stay on the grouped plan)
+        L.use_plan(b, "fused")
+        g_fused = T.graph(lambda: L.forward(b))
+        res["fused_us"] = round(stats(T.time_graph(g_fused, reps, warmup))["median"], 3)
+        L.use_plan(b, "grouped")
+        del g_fused
     if exhaustive:
         g_forced = T.graph(lambda: L.forward(b, forced_variant=True))
         per_v = []

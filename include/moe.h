@@ -379,6 +379,56 @@ moe_status moe_combine_shared(const moe_problem* p, const void* y_slots, const i
 moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t* slot_pos,
                        const float* topk_w, void* y, void* stream);
 
+/* The fused plan for small batches (RaMP appendix A.8, "Fusion": each tile runs
+ * the up-projection, the gated activation and the down-projection in turn, and
+ * adds its down-projection result into the layer's output).  It replaces steps 4
+ * and 5 (moe_grouped_ffn, moe_combine) with one FFN launch and one combine launch;
+ * steps 1-3 are unchanged.  A tile is one row-block of the alignment (BLOCK_M of
+ * *variant) times one slice of 32 columns of I:
+ *   h_j[r]       = bf16(silu(x[t] W1_e[slice j]^T) * (x[t] W3_e[slice j]^T))
+ *   part[j][s]   = h_j[r] W2_e[:, slice j]^T              (fp32)
+ * for every row r that holds slot s = sorted_slots[r] (t = s / k, e =
+ * block_expert[r / b]); the combine then writes
+ *   y[t] = sum over i = 0..k-1 with slot_pos[t*k+i] >= 0 of
+ *          topk_w[t][i] * (sum over j of part[j][t*k+i])
+ * in fp32, the slices added in a fixed order (slice lanes l = 0..15 each add
+ * slices l, l + 16, ... in ascending order, then the lanes in order), rounded to
+ * bf16 once.  No atomics, so the result is deterministic.  Compared with the
+ * grouped plan, the slot's sum over I is added per 32-column slice and is not
+ * rounded to bf16 before the combine (there is no y_slots).
+ * Where it pays: each tile streams its slice of W1, W3 and W2 once, and the
+ * partial rows add 4 * B * k * H * I / 32 bytes, written once and read once; at
+ * a few token rows per expert that is a small share of the weight bytes, and the
+ * FFN is one launch instead of four.  The caller chooses the plan by batch size.
+ * Supported problems: bf16 activations with bf16 or fp8 weights, act_quant = 0,
+ * no shared experts (else MOE_ERR_UNSUPPORTED).  With packed_weights set (bf16
+ * problems, moe_pack_wide) the FFN reads the weights from the packed copy, whose
+ * blocks give each fragment load 1 KiB of consecutive bytes (W1, W3 and W2 must
+ * still be passed); the result is bit-identical to reading W1, W3, W2.
+ * moe_fused_workspace_bytes: *bytes = 256 + 4 * (I / 32) * B * k * H, the size
+ *   of fused_ws: a 256-byte header whose int32 at MOE_DEVICE_STATUS_OFFSET is the
+ *   device status word (as for moe_grouped_ffn; written by every fused FFN
+ *   launch), then part [I/32][B*k][H] fp32.  Only the rows of local slots are
+ *   written; nothing needs to start at zero.
+ * moe_grouped_ffn_fused: x [B][H] bf16, weights and scales as moe_grouped_ffn,
+ *   sorted_slots / block_expert / num_blocks / variant from steps 1-3 (device);
+ *   fused_ws device, 256-byte aligned, >= fused_ws_bytes bytes (else
+ *   MOE_ERR_WORKSPACE).  One persistent launch of 256-thread workgroups.
+ * moe_combine_fused: reads fused_ws after moe_grouped_ffn_fused on the same
+ *   stream; y [B][H] bf16.  Tokens with no local slot get zeros, and so does
+ *   every token when the status word is not MOE_DEV_OK.
+ * Errors: MOE_ERR_INVALID_ARG (NULL pointers, misalignment), MOE_ERR_UNSUPPORTED,
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP; all calls are asynchronous on stream. */
+moe_status moe_fused_workspace_bytes(const moe_problem* p, int64_t* bytes);
+moe_status moe_grouped_ffn_fused(const moe_problem* p, const void* x, const void* w1,
+                                 const void* w3, const void* w2, const float* s1, const float* s3,
+                                 const float* s2, const int32_t* sorted_slots,
+                                 const int32_t* block_expert, const int32_t* num_blocks,
+                                 const int32_t* variant, void* fused_ws, size_t fused_ws_bytes,
+                                 void* stream);
+moe_status moe_combine_fused(const moe_problem* p, const void* fused_ws, const int32_t* slot_pos,
+                             const float* topk_w, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,6 +81,10 @@ _SIGS = {
     "moe_noalloc_workspace_limit": ([], ctypes.c_int64),
     "moe_pack_wide_bytes": ([ctypes.POINTER(moe_problem), P], ctypes.c_int),
     "moe_pack_wide": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
+    "moe_fused_workspace_bytes": ([ctypes.POINTER(moe_problem), P], ctypes.c_int),
+    "moe_grouped_ffn_fused": ([ctypes.POINTER(moe_problem), P, P, P, P, P, P, P, P, P, P, P, P,
+                               ctypes.c_size_t, P], ctypes.c_int),
+    "moe_combine_fused": ([ctypes.POINTER(moe_problem), P, P, P, P, P], ctypes.c_int),
 }
 
 
@@ -247,6 +251,26 @@ def moe_combine_shared(p, y_slots, slot_pos, topk_w, num_blocks, variant, y, str
 def moe_combine(p, y_slots, slot_pos, topk_w, y, stream=None):
     _check("moe_combine", lib().moe_combine(_pp(p), _ptr(y_slots), _ptr(slot_pos),
                                             _ptr(topk_w), _ptr(y), _stream(stream)))
+
+
+# ------------------------------------------------- the fused small-batch plan --
+def moe_fused_workspace_bytes(p: moe_problem) -> int:
+    out = ctypes.c_int64(0)
+    _check("moe_fused_workspace_bytes", lib().moe_fused_workspace_bytes(_pp(p), ctypes.byref(out)))
+    return int(out.value)
+
+
+def moe_grouped_ffn_fused(p, x, w1, w3, w2, s1, s3, s2, sorted_slots, block_expert, num_blocks,
+                          variant, fused_ws, fused_ws_bytes=None, stream=None):
+    _check("moe_grouped_ffn_fused", lib().moe_grouped_ffn_fused(
+        _pp(p), _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2),
+        _ptr(sorted_slots), _ptr(block_expert), _ptr(num_blocks), _ptr(variant), _ptr(fused_ws),
+        _ws_bytes(fused_ws, fused_ws_bytes), _stream(stream)))
+
+
+def moe_combine_fused(p, fused_ws, slot_pos, topk_w, y, stream=None):
+    _check("moe_combine_fused", lib().moe_combine_fused(_pp(p), _ptr(fused_ws), _ptr(slot_pos),
+                                                        _ptr(topk_w), _ptr(y), _stream(stream)))
 
 
 __all__ = [n for n in dir() if n.startswith("moe_") or n.startswith("MOE_")] + [

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["selection.hip", "grouped_ffn.hip",
+SOURCES = ["selection.hip", "grouped_ffn.hip", "fused_ffn.hip",
            "combine.hip", "quant.hip", "moe_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

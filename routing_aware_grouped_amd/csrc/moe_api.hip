@@ -189,7 +189,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 7; }
+int32_t moe_abi_version(void) { return 8; }
 
 moe_status moe_query_sizes(const moe_problem* p, moe_sizes* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
@@ -490,6 +490,67 @@ moe_status moe_combine_shared(const moe_problem* p, const void* y_slots, const i
   sizes_of(p, &sz);
   return hip_status(launch_combine(*p, y_slots, slot_pos, topk_w, num_blocks, variant, y,
                                    sz.rows_max, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// The fused plan for small batches (include/moe.h, moe_grouped_ffn_fused)
+// ---------------------------------------------------------------------------
+
+// bf16 activations with bf16 or fp8 weights, no FP8 activation path and no shared
+// experts
+static moe_status fused_supported(const moe_problem* p) {
+  if (p->act_dtype != MOE_BF16 || (p->weight_dtype != MOE_BF16 && p->weight_dtype != MOE_FP8_E4M3))
+    return MOE_ERR_UNSUPPORTED;
+  if (p->act_quant || p->shared_experts) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_fused_workspace_bytes(const moe_problem* p, int64_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  st = fused_supported(p);
+  if (st != MOE_OK) return st;
+  *bytes = fused_ws_bytes(*p);
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_fused(const moe_problem* p, const void* x, const void* w1,
+                                 const void* w3, const void* w2, const float* s1, const float* s3,
+                                 const float* s2, const int32_t* sorted_slots,
+                                 const int32_t* block_expert, const int32_t* num_blocks,
+                                 const int32_t* variant, void* fused_ws, size_t fused_ws_bytes_,
+                                 void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  st = fused_supported(p);
+  if (st != MOE_OK) return st;
+  const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
+  if (!x || !w1 || !w3 || !w2 || !sorted_slots || !block_expert || !num_blocks || !variant ||
+      !fused_ws || (fp8 && (!s1 || !s3 || !s2)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) ||
+      !aligned(fused_ws, 256) || (fp8 && (!aligned(s1, 4) || !aligned(s3, 4) || !aligned(s2, 4))))
+    return MOE_ERR_INVALID_ARG;
+  if ((int64_t)fused_ws_bytes_ < fused_ws_bytes(*p)) return MOE_ERR_WORKSPACE;
+  hipError_t err;
+  const int cus = num_cus_current(&err);
+  if (err != hipSuccess || cus <= 0) return MOE_ERR_HIP;
+  return hip_status(launch_fused_ffn(*p, x, w1, w3, w2, fp8 ? s1 : nullptr, fp8 ? s3 : nullptr,
+                                     fp8 ? s2 : nullptr, sorted_slots, block_expert, num_blocks,
+                                     variant, fused_ws, cus, rows_max_of(p), (hipStream_t)stream));
+}
+
+moe_status moe_combine_fused(const moe_problem* p, const void* fused_ws, const int32_t* slot_pos,
+                             const float* topk_w, void* y, void* stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  st = fused_supported(p);
+  if (st != MOE_OK) return st;
+  if (!fused_ws || !slot_pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(fused_ws, 256) || !aligned(y, 16) || !aligned(topk_w, 4) || !aligned(slot_pos, 4))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine_fused(*p, fused_ws, slot_pos, topk_w, y, (hipStream_t)stream));
 }
 
 }  // extern "C"

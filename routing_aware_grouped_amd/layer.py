@@ -3,8 +3,10 @@
 Holds no arithmetic of its own: torch allocates device memory, and `forward`
 enqueues moe_route_select_align (routing, configuration choice and alignment
 fused) -> moe_grouped_ffn -> moe_combine on one stream, with no host
-synchronisation, so a caller may capture it in a HIP graph.  The separate step
-calls (route, select, align) remain for tests and per-step timing.
+synchronisation, so a caller may capture it in a HIP graph.  With the fused
+plan (small batches) the last two are moe_grouped_ffn_fused -> moe_combine_fused.
+The separate step calls (route, select, align) remain for tests and per-step
+timing.
 """
 from __future__ import annotations
 
@@ -12,9 +14,10 @@ import dataclasses
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_combine_shared,
-               moe_grouped_down,
-               moe_grouped_ffn, moe_grouped_gate_up, moe_num_variants, moe_pack_wide,
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, moe_align_sort, moe_combine, moe_combine_fused,
+               moe_combine_shared, moe_fused_workspace_bytes, moe_grouped_down,
+               moe_grouped_ffn, moe_grouped_ffn_fused, moe_grouped_gate_up, moe_num_variants,
+               moe_pack_wide,
                moe_pack_wide_bytes, moe_problem,
                moe_query_sizes, moe_route_select_align, moe_route_topk, moe_select_config)
 
@@ -46,6 +49,36 @@ class Buffers:
     workspace: torch.Tensor
     y: torch.Tensor
     packed: torch.Tensor | None = None  # the wide configuration's packed weights
+    fused_ws: torch.Tensor | None = None  # the fused plan's workspace (plan "fused")
+    plan: str = "grouped"
+
+
+# Plan "auto" takes the fused plan for bf16 problems that have the packed weight
+# copy when the expert weights the batch can reach, min(E_loc, B k) experts of
+# 3 H I bf16 values, are at most this many bytes: there the layer's launches cost
+# more than the fused plan's slower weight stream (measured on MI355X: Qwen3-shaped
+# layers at B = 1 and 4 are 10-17% faster fused, B = 16 ties; a Mixtral-shaped
+# layer at B = 1 is 10% slower, and so are the fp8-weight shares).
+FUSED_MAX_WEIGHT_BYTES = 512 << 20
+
+
+def fused_supported(p: moe_problem) -> bool:
+    """The problems the fused plan covers: bf16 activations with bf16 or fp8
+    weights, no FP8 activation path, no shared experts."""
+    return (p.act_dtype == MOE_BF16 and p.weight_dtype in (MOE_BF16, MOE_FP8_E4M3)
+            and not p.act_quant and not p.shared_experts)
+
+
+def choose_plan(p: moe_problem, plan: str = "auto") -> str:
+    """"grouped", "fused", or "auto" (the rule of FUSED_MAX_WEIGHT_BYTES)."""
+    if plan == "auto":
+        if not (fused_supported(p) and p.weight_dtype == MOE_BF16 and p.packed_weights):
+            return "grouped"
+        reach = min(p.local_experts, p.tokens * p.top_k) * 3 * p.hidden * p.inter * 2
+        return "fused" if reach <= FUSED_MAX_WEIGHT_BYTES else "grouped"
+    if plan not in ("grouped", "fused"):
+        raise ValueError(f"unknown plan {plan!r}")
+    return plan
 
 
 def packed_weights(p: moe_problem, w1, w3, w2, stream=None) -> torch.Tensor:
@@ -67,10 +100,11 @@ def packed_weights(p: moe_problem, w1, w3, w2, stream=None) -> torch.Tensor:
 
 
 def allocate(p: moe_problem, logits, x, w1, w3, w2, s1=None, s3=None, s2=None, theta=None,
-             device="cuda", pack=None) -> Buffers:
+             device="cuda", pack=None, plan="grouped") -> Buffers:
     """Output/intermediate buffers sized by moe_query_sizes; inputs are moved to
     the device as given (already dtype-encoded).  pack (default: bf16 problems)
-    gives the wide configuration its packed weight copy (packed_weights)."""
+    gives the wide configuration its packed weight copy (packed_weights).  plan:
+    see choose_plan; the fused plan also gets its workspace."""
     p = moe_problem.from_buffer_copy(p)
     if pack is None:
         pack = p.act_dtype == MOE_BF16 and p.weight_dtype == MOE_BF16
@@ -85,12 +119,16 @@ def allocate(p: moe_problem, logits, x, w1, w3, w2, s1=None, s3=None, s2=None, t
 
     if theta is None:
         theta = torch.zeros(V, 4, dtype=torch.float32)
+    if tuple(theta.shape) != (V, 4):
+        # the selection kernels read four coefficients per compiled configuration
+        raise ValueError(f"theta must be [{V}][4], got {tuple(theta.shape)}")
     w1, w3, w2 = d(w1), d(w3), d(w2)
     packed = None
     if pack:
         p.packed_weights = None
         packed = packed_weights(p, w1, w3, w2)
         p.packed_weights = packed.data_ptr()
+    plan = choose_plan(p, plan)
     return Buffers(
         p=p, logits=d(logits), x=d(x), w1=w1, w3=w3, w2=w2, s1=d(s1), s3=d(s3), s2=d(s2),
         theta=d(theta),
@@ -107,7 +145,19 @@ def allocate(p: moe_problem, logits, x, w1, w3, w2, s1=None, s3=None, s2=None, t
         workspace=torch.empty(sz.workspace_bytes, dtype=torch.uint8, device=dev),
         y=torch.empty(B, p.hidden, dtype=act, device=dev),
         packed=packed,
+        fused_ws=(torch.empty(moe_fused_workspace_bytes(p), dtype=torch.uint8, device=dev)
+                  if plan == "fused" else None),
+        plan=plan,
     )
+
+
+def use_plan(b: Buffers, plan: str) -> None:
+    """Switch existing buffers to another plan (choose_plan), allocating the fused
+    plan's workspace on first use."""
+    b.plan = choose_plan(b.p, plan)
+    if b.plan == "fused" and b.fused_ws is None:
+        b.fused_ws = torch.empty(moe_fused_workspace_bytes(b.p), dtype=torch.uint8,
+                                 device=b.y.device)
 
 
 def route(b: Buffers, stream=None):
@@ -135,6 +185,15 @@ def ffn(b: Buffers, stream=None):
                     b.num_blocks, b.variant, b.y_slots, b.workspace, None, stream)
 
 
+def ffn_fused(b: Buffers, stream=None):
+    moe_grouped_ffn_fused(b.p, b.x, b.w1, b.w3, b.w2, b.s1, b.s3, b.s2, b.sorted_slots,
+                          b.block_expert, b.num_blocks, b.variant, b.fused_ws, None, stream)
+
+
+def combine_fused(b: Buffers, stream=None):
+    moe_combine_fused(b.p, b.fused_ws, b.slot_pos, b.topk_w, b.y, stream)
+
+
 def gate_up(b: Buffers, stream=None):
     moe_grouped_gate_up(b.p, b.x, b.w1, b.w3, b.s1, b.s3, b.sorted_slots, b.block_expert,
                         b.num_blocks, b.variant, b.workspace, None, stream)
@@ -157,6 +216,10 @@ def forward(b: Buffers, stream=None, forced_variant: bool = False):
     """The whole layer.  With forced_variant the select step is skipped and the
     value already in b.variant is used (exhaustive timing of every configuration)."""
     route_select_align(b, stream, forced_variant)
+    if b.plan == "fused":
+        ffn_fused(b, stream)
+        combine_fused(b, stream)
+        return
     ffn(b, stream)
     combine(b, stream)
 
@@ -203,7 +266,7 @@ def problem_of(layer, renormalize: int = 1) -> moe_problem:
 
 
 def from_layer(layer, theta=None, device="cuda", weights=None, renormalize: int = 1,
-               pack=None) -> Buffers:
+               pack=None, plan="grouped") -> Buffers:
     """Buffers for a synthetic layer (see synth.Layer); `weights` reuses device
     weight tensors (w1, w3, w2, s1, s3, s2) across loads (and their packed copy)."""
     p = problem_of(layer, renormalize)
@@ -211,4 +274,4 @@ def from_layer(layer, theta=None, device="cuda", weights=None, renormalize: int 
         weights = weight_tensors(layer)
     w1, w3, w2, s1, s3, s2 = weights
     return allocate(p, torch.from_numpy(layer.logits), act_tensor(layer, layer.x), w1, w3, w2, s1,
-                    s3, s2, theta=theta, device=device, pack=pack)
+                    s3, s2, theta=theta, device=device, pack=pack, plan=plan)

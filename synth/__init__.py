@@ -83,13 +83,15 @@ SHAPES = {
     # bf16 with the shortest reductions the API admits: H = 128 (a gate/up
     # reduction of four 32-deep stages) and I = 384
     "tiny_bf16": Shape("tiny_bf16", 128, 384, 8, 8, 2, BF16, BF16, BF16, "dirichlet"),
+    # a small fp8-weight layer with bf16 activations (no activation quantization)
+    "small_fp8": Shape("small_fp8", 384, 256, 8, 8, 2, BF16, FP8, BF16, "dirichlet"),
 }
 
 CFG_INDEX = {"tiny": 1, "mixtral": 2, "qwen3": 3, "dsv3_share": 4, "kimi_share": 5,
              "dsv3_share_fp8a": 4, "kimi_share_fp8a": 5, "small_fp8a": 6,
              "dsv3_share_fp8ah": 4, "kimi_share_fp8ah": 5, "small_fp8ah": 6,
              "dsv3_share_sh": 4, "kimi_share_sh": 5, "small_sh": 6, "tiny_sh": 1,
-             "small_sh_fp8ah": 6, "tiny_bf16": 7}
+             "small_sh_fp8ah": 6, "tiny_bf16": 7, "small_fp8": 6}
 
 
 def seed_seq(shape: str, tokens: int, alpha: float | None, rep: int) -> np.random.SeedSequence:

@@ -122,6 +122,26 @@ int main(void) {
   EXPECT(moe_combine_shared(&ok, D, D, D, D, D, D, NULL), MOE_ERR_INVALID_ARG);
   EXPECT(moe_cost_constants(&ok, NULL, NULL, NULL, NULL, NULL), MOE_ERR_INVALID_ARG);
 
+  /* the fused small-batch plan */
+  moe_problem fb = prob(3, 384, 256, 8, 2, MOE_BF16, MOE_BF16);
+  int64_t fws = 0;
+  EXPECT(moe_fused_workspace_bytes(&fb, &fws), MOE_OK);
+  if (fws != 256 + 4ll * (256 / 32) * 3 * 2 * 384) {
+    fprintf(stderr, "moe_fused_workspace_bytes: %lld\n", (long long)fws);
+    ++failures;
+  }
+  EXPECT(moe_fused_workspace_bytes(&ok, &fws), MOE_ERR_UNSUPPORTED); /* fp32 */
+  EXPECT(moe_fused_workspace_bytes(&fb, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_grouped_ffn_fused(&fb, D, D, D, D, NULL, NULL, NULL, D, D, D, D, D, (size_t)fws - 1,
+                               NULL),
+         MOE_ERR_WORKSPACE);
+  EXPECT(moe_grouped_ffn_fused(&fb, Dm, D, D, D, NULL, NULL, NULL, D, D, D, D, D, 1ull << 40, NULL),
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_grouped_ffn_fused(&f8, D, D, D, D, NULL, NULL, NULL, D, D, D, D, D, 1ull << 40, NULL),
+         MOE_ERR_INVALID_ARG); /* fp8 weights need their scales */
+  EXPECT(moe_combine_fused(&fb, D, D, D, NULL, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_combine_fused(&ok, D, D, D, D, NULL), MOE_ERR_UNSUPPORTED);
+
   if (failures) {
     fprintf(stderr, "%d checks failed\n", failures);
     return 1;

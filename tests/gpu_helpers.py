@@ -59,12 +59,14 @@ def device_weights(layer, wdev=None):
 
 
 def run(layer, variant: int | None = None, theta=None, wdev=None, renormalize: int = 1,
-        pack=None):
+        pack=None, plan="grouped"):
     """Whole layer on the GPU.  variant=None: the select step chooses with theta;
     else configuration `variant` is forced.  pack: see layer.allocate (default:
-    bf16 layers give the wide configuration its packed weight copy)."""
+    bf16 layers give the wide configuration its packed weight copy).  plan: the
+    grouped or the fused plan (layer.choose_plan)."""
     b = L.from_layer(layer, theta=theta if theta is not None else theta_forcing(0),
-                     weights=device_weights(layer, wdev), renormalize=renormalize, pack=pack)
+                     weights=device_weights(layer, wdev), renormalize=renormalize, pack=pack,
+                     plan=plan)
     if variant is not None:
         b.variant.fill_(variant)
     torch.cuda.synchronize()

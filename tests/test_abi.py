@@ -34,7 +34,7 @@ def test_binding_mirrors_names():
 
 
 def test_variant_menu_matches_spec():
-    assert moe.moe_abi_version() == 7
+    assert moe.moe_abi_version() == 8
     assert moe.moe_num_variants() == len(spec.MENU)
     for v, m in enumerate(spec.MENU):
         assert tuple(moe.moe_variant_info(v)) == m
@@ -265,3 +265,38 @@ def test_pack_layout_restatement_small():
         assert pk[base + blk * 256 * 32 + r * 32 + k % 32] == w2[e, r, k]
     # rows 64..255 of each down block are zeros (H = 64)
     assert not pk[base:].reshape(-1, 256, 32)[:, 64:].any()
+
+
+def test_fused_plan_sizes_and_validation():
+    """The fused small-batch plan: its workspace is a 256-byte header plus fp32
+    partial rows [I / 32][B k][H] (the header's formula); problems outside it and
+    bad arguments are rejected on the host, before anything runs."""
+    pb = _p(tokens=3, hidden=384, inter=256, act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16)
+    assert moe.moe_fused_workspace_bytes(pb) == 256 + 4 * (256 // 32) * 3 * 2 * 384
+    for kw in (dict(),  # fp32
+               dict(act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_FP8_E4M3, act_quant=1),
+               dict(act_dtype=moe.MOE_BF16, weight_dtype=moe.MOE_BF16, shared_experts=1)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_fused_workspace_bytes(_p(**kw))
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED, kw
+    a = 0x10000
+    need = moe.moe_fused_workspace_bytes(pb)
+    with pytest.raises(moe.MoeError) as ei:  # workspace one byte short
+        moe.moe_grouped_ffn_fused(pb, a, a, a, a, None, None, None, a, a, a, a, a, need - 1, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as ei:  # workspace not 256-byte aligned
+        moe.moe_grouped_ffn_fused(pb, a, a, a, a, None, None, None, a, a, a, a, a + 128, need,
+                                  stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    pf = _p(tokens=3, hidden=384, inter=256, act_dtype=moe.MOE_BF16,
+            weight_dtype=moe.MOE_FP8_E4M3)
+    with pytest.raises(moe.MoeError) as ei:  # fp8 weights need their scales
+        moe.moe_grouped_ffn_fused(pf, a, a, a, a, None, None, None, a, a, a, a, a, 1 << 30,
+                                  stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # no y
+        moe.moe_combine_fused(pb, a, a, a, None, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:  # the grouped plan's problems only
+        moe.moe_combine_fused(_p(), a, a, a, a, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED

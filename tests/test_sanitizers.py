@@ -44,7 +44,7 @@ def test_oracle_under_asan_ubsan():
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANG)), reason="no ROCm toolchain")
 def test_abi_under_asan_ubsan():
-    objs = [os.path.join(ROOT, "_build", f"{n}.o") for n in ("selection", "grouped_ffn", "combine",
+    objs = [os.path.join(ROOT, "_build", f"{n}.o") for n in ("selection", "grouped_ffn", "fused_ffn", "combine",
                                                               "quant")]
     if not all(os.path.exists(o) for o in objs):
         pytest.skip("the library's objects are not built (run routing_aware_grouped_amd.build)")
