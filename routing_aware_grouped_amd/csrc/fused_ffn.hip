@@ -40,7 +40,7 @@
 //     first batch is issued before h is formed.
 //   - at most 128 registers per lane, so that two workgroups share a CU.
 //   - a row-block with more than 32 rows takes several passes over its slice.
-#include "moe_common.h"
+#include "fused_ffn.h"
 
 namespace moe {
 namespace {
@@ -402,8 +402,6 @@ __global__ void __launch_bounds__(256) combine_fused_kernel(const float* __restr
 }
 
 }  // namespace
-
-int fused_slice() { return kSlice; }
 
 int64_t fused_ws_bytes(const moe_problem& p) {
   return 256 + (int64_t)(p.inter / kSlice) * p.tokens * p.top_k * p.hidden * 4;

@@ -8,6 +8,7 @@
 #include <mutex>
 #include <utility>
 
+#include "fused_ffn.h"
 #include "moe_common.h"
 
 namespace moe {

@@ -169,19 +169,6 @@ hipError_t launch_grouped_ffn(const moe_problem& p, int phases, const void* x, c
 int64_t pack_wide_bytes(const moe_problem& p);
 hipError_t launch_pack_wide(const moe_problem& p, const void* w1, const void* w3, const void* w2,
                             void* packed, hipStream_t s);
-// The fused plan for small batches (fused_ffn.hip): the slice width of I per tile,
-// the size of its workspace (a 256-byte header holding the device status word,
-// then the fp32 slice partials [I / slice][B k][H]), the one FFN launch, and the
-// combine that adds the slices.
-int fused_slice();
-int64_t fused_ws_bytes(const moe_problem& p);
-hipError_t launch_fused_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
-                            const void* w2, const float* s1, const float* s3, const float* s2,
-                            const int32_t* sorted_slots, const int32_t* block_expert,
-                            const int32_t* num_blocks, const int32_t* variant, void* ws,
-                            int num_cus, int64_t rows_max, hipStream_t s);
-hipError_t launch_combine_fused(const moe_problem& p, const void* ws, const int32_t* slot_pos,
-                                const float* w, void* y, hipStream_t s);
 // num_blocks / variant: device values of the sort, needed with shared experts only
 hipError_t launch_combine(const moe_problem& p, const void* y_slots, const int32_t* slot_pos,
                           const float* w, const int32_t* num_blocks, const int32_t* variant,
