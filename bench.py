@@ -108,12 +108,15 @@ def work(layer, ids_np):
     mfma_s = 4 * S * H * I / gu_peak + 2 * S * H * I / dn_peak
     return dict(S=S, A=A, U=U, flops=6 * S * H * I, layer_bytes=layer_bytes,
                 gate_up_bytes=gate_up_bytes, gate_up_flops=4 * S * H * I, gate_up_peak=gu_peak,
+                # the fused plan's one FFN launch: every weight byte and the gathered x rows
+                ffn_bytes=wbytes + U * H * ab,
                 mfma_s=mfma_s, eff_exp=synth.eff_exp(cnt),
                 # the chooser's view: a shared expert is a local expert with B tokens
                 counts=np.concatenate([cnt, np.full(nsh, B, dtype=cnt.dtype)]))
 
 
 PACK = None  # layer.allocate's pack argument (--pack)
+PLAN = "grouped"  # the headline point's plan (--plan)
 
 
 def roof_us(w):
@@ -224,9 +227,9 @@ def device_weights(wdev):
 
 
 def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, V, reps, warmup,
-              exhaustive=True, rep=0, force=None):
+              exhaustive=True, rep=0, force=None, plan="grouped"):
     layer = synth.make_layer(shape, tokens, alpha, rep, weights=whost)
-    b = L.from_layer(layer, theta=theta, weights=device_weights(wdev), pack=PACK)
+    b = L.from_layer(layer, theta=theta, weights=device_weights(wdev), pack=PACK, plan=plan)
     L.forward(b)
     torch.cuda.synchronize()
     ids = b.topk_ids.cpu().numpy()
@@ -250,7 +253,7 @@ def run_point(torch, np, synth, L, T, shape, tokens, alpha, wdev, whost, theta, 
                counts=[int(c) for c in w["counts"]], t_hat=[round(x, 4) for x in t_hat])
     res["binding"] = "hbm" if w["layer_bytes"] / HBM_PEAK >= w["mfma_s"] else "mfma"
     res["roof_frac"] = round(res["roof_us"] / res["us"], 4)
-    if force is None and L.choose_plan(b.p, "auto") == "fused":
+    if force is None and plan == "grouped" and L.choose_plan(b.p, "auto") == "fused":
         # the fused small-batch plan on the same load (the chooser's labels below
         # stay on the grouped plan)
         L.use_plan(b, "fused")
@@ -282,6 +285,9 @@ def kernel_segments(torch, L, b, T, reps, forced=False):
     names = ["route_select_align", "grouped_gate_up", "grouped_down", "combine"]
     fns = [lambda b_, stream: L.route_select_align(b_, stream, forced_variant=forced), L.gate_up,
            L.down, L.combine]
+    if b.plan == "fused":
+        names = ["route_select_align", "grouped_ffn_fused", "combine_fused"]
+        fns = [fns[0], L.ffn_fused, L.combine_fused]
     acc = {n: [] for n in names}
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -496,12 +502,16 @@ def main():
     ap.add_argument("--pack", type=int, default=1,
                     help="1: bf16 layers give the wide configuration its packed weight copy "
                          "(moe_pack_wide, written once per weight set before timing); 0: row-major")
+    ap.add_argument("--plan", default="grouped", choices=["grouped", "fused"],
+                    help="the headline point's plan: the grouped FFN, or the fused small-batch "
+                         "plan (one FFN launch; its roofline line is that launch's)")
     ap.add_argument("--calibrate-gemm", type=int, default=0, metavar="N",
                     help="only time a dense bf16 N x N x N torch.mm (the vendor GEMM library on the "
                          "same GPU: a practical reference for the MFMA-bound rate) and exit")
     args = ap.parse_args()
-    global PACK
+    global PACK, PLAN
     PACK = None if args.pack else False
+    PLAN = args.plan
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the layer runs on one GPU "
@@ -565,7 +575,8 @@ def main():
     log(f"[bench] headline {args.shape} B={args.tokens} alpha={args.alpha}")
     head, layer, b, w = run_point(torch, np, synth, L, T, args.shape, args.tokens, args.alpha, wdev,
                                   whost, theta, V, max(10, args.steps // 2), 3,
-                                  exhaustive=bool(args.exhaustive), force=args.force_variant)
+                                  exhaustive=bool(args.exhaustive), force=args.force_variant,
+                                  plan=PLAN)
     g = T.graph(lambda: L.forward(b, forced_variant=args.force_variant is not None))
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
@@ -578,6 +589,10 @@ def main():
         ", ".join(f"{k} {v:.1f}" for k, v in seg.items()))
 
     # dominant kernel: the grouped gate/up launch (2/3 of the weight bytes and FLOPs)
+    if PLAN == "fused":  # the fused plan's one FFN launch
+        seg["grouped_gate_up"] = seg["grouped_ffn_fused"]
+        w = dict(w, gate_up_bytes=w["ffn_bytes"], gate_up_flops=w["flops"],
+                 gate_up_peak=MFMA_BF16_PEAK)
     t_gu = seg["grouped_gate_up"] * 1e-6
     gu_peak = w["gate_up_peak"]  # the gate/up GEMM's own dtype: bf16, or fp8 x fp8
     bound = "hbm" if w["gate_up_bytes"] / HBM_PEAK >= w["gate_up_flops"] / gu_peak else "mfma"
@@ -588,9 +603,12 @@ def main():
     wl_key = f"{args.shape}:B{args.tokens}:a{args.alpha:g}:v{head['variant']}"
     # the chosen configuration's class: one workgroup per CU runs in the wide kernel
     gu_kernel = "ffn_wide_kernel" if moe.moe_variant_info(head["variant"])[9] == 1 else "ffn_kernel"
+    kname = (f"{gu_kernel}<1,*> (moe_grouped_gate_up)" if PLAN == "grouped"
+             else "fused_ffn_kernel (moe_grouped_ffn_fused)")
     roofline = dict(bound=bound, achieved=round(achieved, 2), peak=round(peak, 1), unit=unit,
-                    frac=round(achieved / peak, 4), traffic=measured_traffic(wl_key),
-                    kernel=f"{gu_kernel}<1,*> (moe_grouped_gate_up)",
+                    frac=round(achieved / peak, 4),
+                    traffic=measured_traffic(wl_key) if PLAN == "grouped" else None,
+                    kernel=kname,
                     alg_bytes=int(w["gate_up_bytes"]), alg_flops=int(w["gate_up_flops"]),
                     avg_launch_us=round(seg["grouped_gate_up"], 3))
 
@@ -644,6 +662,7 @@ def main():
                    "tokens": args.tokens, "alpha": args.alpha, "hidden": sh.hidden,
                    "inter": sh.inter, "experts": sh.num_experts, "top_k": sh.top_k,
                    "weights": synth.DTYPE_NAMES[sh.weight_dtype], "parallelism": "single GPU",
+                   "plan": PLAN,
                    "timing": "HIP graph replay, cold L2/Infinity Cache, hipEvent per step, median"},
         "roofline": roofline,
         "cpu_baseline": cpu,

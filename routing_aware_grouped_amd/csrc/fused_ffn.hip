@@ -26,19 +26,20 @@
 //     columns (w >> 1): one 16-column MFMA fragment, over the whole reduction,
 //     on two 16-row groups of the pass's 32 token rows (v_mfma_f32_16x16x32_bf16).
 //     Fragments go from memory straight into registers (buffer loads, 16 bytes
-//     per lane), four 32-deep steps per batch, the next batch in flight while the
-//     current one is multiplied.  A batch past the reduction's end loads with an
-//     out-of-range offset, which returns zeros and reads no memory, so the loop
+//     per lane), eight 32-deep steps per batch, the next batch in flight while
+//     the current one is multiplied.  A step past the reduction's end loads with
+//     an out-of-range offset, which returns zeros and reads no memory, so the loop
 //     has no branch around its loads.
 //   - fp8 weights are decoded in registers, w = q * s rounded to bf16, as the
-//     grouped plan decodes them in staging; a wave's fragments of one batch lie
-//     in one 128 x 128 scale block, so each batch needs one scale.
+//     grouped plan decodes them in staging (one scale per step: a 32-deep step of
+//     16 rows lies in one 128 x 128 scale block).
 //   - g and u meet in LDS as fp32, where h is formed in bf16.
 //   - down: wave w takes every fourth 16-column group of H; a group is one
 //     product over the 32-deep slice, with h's fragments read from LDS once per
 //     pass and W2's loaded eight groups per batch, two batches in flight; the
 //     first batch is issued before h is formed.
-//   - at most 128 registers per lane, so that two workgroups share a CU.
+//   - two to four workgroups share a CU (the grid holds up to four per CU, so
+//     every tile of a small batch is in flight at once).
 //   - a row-block with more than 32 rows takes several passes over its slice.
 #include "fused_ffn.h"
 
@@ -48,7 +49,7 @@ namespace {
 constexpr int kSlice = 32;          // columns of I per tile
 constexpr int kFusedThreads = 256;  // four waves
 constexpr int kPassRows = 32;       // token rows per pass: two 16-row MFMA groups
-constexpr int kStepBatch = 4;       // 32-deep gate/up steps per load batch (128 deep)
+constexpr int kStepBatch = 8;       // 32-deep gate/up steps per load batch (256 deep)
 constexpr int kGroupBatch = 8;      // down-phase 16-column groups per load batch
 constexpr uint32_t kNoOperand = 0x80000000u;  // past every operand buffer's range
 constexpr int kStreamLoad = 2;      // cache policy of a buffer load: non-temporal
@@ -129,12 +130,12 @@ __device__ __forceinline__ float silu_times(float g, float u) {
 }
 
 // one gate/up load batch of a wave: kStepBatch 32-deep steps, two token-row
-// groups (A) and one weight fragment (B) per step, and the batch's scale
+// groups (A), one weight fragment (B) and its block scale (fp8) per step
 template <bool FP8>
 struct UpBatch {
   u32x4 a[kStepBatch][2];
   WFrag<FP8> b[kStepBatch];
-  float s;
+  float s[kStepBatch];
 };
 
 // one down-phase load batch of a wave: kGroupBatch column groups, one 32-deep W2
@@ -171,12 +172,16 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_ffn_kernel(FusedArgs g
   if (st == MOE_DEV_BAD_VARIANT) return;
 
   constexpr int WSZ = FP8 ? 1 : 2;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index through readfirstlane: values derived from it (the weight
+  // matrix, the descriptors) are then known to be wave-uniform and live in scalar
+  // registers; otherwise each buffer load becomes a loop over distinct descriptors
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int mt = wv & 1, half = wv >> 1;
   const int H = g.H, I = g.I;
   const int nsl = I / kSlice;
-  const int nbt = H / 128;                 // gate/up load batches (H is a multiple of 128)
+  const int nst = H / 32;                  // 32-deep gate/up steps
+  const int nbt = (nst + kStepBatch - 1) / kStepBatch;  // gate/up load batches
   const int ncg = H / 64;                  // down-phase column groups per wave
   const int nbd = (ncg + kGroupBatch - 1) / kGroupBatch;  // down-phase load batches
   const __amdgpu_buffer_rsrc_t xr = buffer_of(g.x, (uint32_t)((int64_t)g.slots / g.k * H * 2));
@@ -238,23 +243,24 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_ffn_kernel(FusedArgs g
       }
 
       auto load_up = [&](UpBatch<FP8>& U, int bt) __attribute__((always_inline)) {
-        const bool in = bt < nbt;
 #pragma unroll
         for (int q = 0; q < kStepBatch; ++q) {
-          const int k0 = (bt * kStepBatch + q) * 32;
+          const int st = bt * kStepBatch + q;
+          const bool in = st < nst;
+          const int k0 = st * 32;
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi)
             U.a[q][gi] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, in ? aoff[gi] : kNoOperand, k0 * 2, 0));
-          U.b[q] = load_w<FP8>(wr, in ? boff : kNoOperand, (bt * kStepBatch + q) * sstep);
+          U.b[q] = load_w<FP8>(wr, in ? boff : kNoOperand, st * sstep);
+          if constexpr (FP8) U.s[q] = sm[su0 + (in ? st / 4 : 0)];
         }
-        if constexpr (FP8) U.s = sm[su0 + (in ? bt : 0)];
       };
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       auto mul_up = [&](const UpBatch<FP8>& U) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < kStepBatch; ++q) {
-          const bf16x8 b = decode<FP8>(U.b[q], FP8 ? U.s : 1.0f);
+          const bf16x8 b = decode<FP8>(U.b[q], FP8 ? U.s[q] : 1.0f);
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) acc[gi] = mfma(__builtin_bit_cast(bf16x8, U.a[q][gi]), b, acc[gi]);
         }
@@ -262,7 +268,7 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_ffn_kernel(FusedArgs g
       {
         UpBatch<FP8> U0, U1;
         load_up(U0, 0);
-        // batches past nbt read zeros (an odd nbt runs one batch of zeros)
+        // steps past nst read zeros (an odd nbt runs one batch of zeros)
         for (int bt = 0; bt < nbt; bt += 2) {
           load_up(U1, bt + 1);
           mul_up(U0);
@@ -345,13 +351,15 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_ffn_kernel(FusedArgs g
 }
 
 // The combine of the fused plan.  A workgroup takes one token and 64 columns: 16
-// column vectors of 4 floats x 16 slice lanes.  For each of the token's local
-// slots (in ascending i), lane l adds slices l, l + 16, ... in ascending order,
-// the 16 lane sums are added in lane order through LDS, and the slot's sum is
-// added with its router weight; y is rounded to bf16 once.  With a nonzero
+// column vectors of 4 floats x 16 pair lanes.  The token's (slot i, slice j)
+// pairs, numbered p = i * nsl + j, are dealt to the lanes (lane l: p = l, l + 16,
+// ... in ascending order); a lane adds topk_w[t][i] * part[j][t k + i] over its
+// pairs, loading eight pairs before it adds them, and skips the slots of other
+// GPUs' experts.  The 16 lane sums are then added in lane order through LDS and
+// rounded to bf16 once: a fixed order, so y is deterministic.  With a nonzero
 // device status the FFN may have skipped rows, and y is written as zeros.
 constexpr int kCombLanes = 16;
-constexpr int kCombBatch = 8;  // slices loaded before they are added
+constexpr int kCombBatch = 8;  // pairs loaded before they are added
 
 __global__ void __launch_bounds__(256) combine_fused_kernel(const float* __restrict__ part,
                                                             const int32_t* __restrict__ status,
@@ -360,42 +368,43 @@ __global__ void __launch_bounds__(256) combine_fused_kernel(const float* __restr
                                                             uint16_t* __restrict__ y, int B, int H,
                                                             int k, int nsl, int slots) {
   __shared__ f32x4 red[kCombLanes][16];
+  __shared__ float s_w[32];  // the token's router weights; 0 for other GPUs' experts
   const int cv = threadIdx.x & 15, sl = threadIdx.x >> 4;
   const bool ok = *status == MOE_DEV_OK;
   const int chunks = H / 64;
+  const int pairs = k * nsl;
   for (int64_t item = blockIdx.x; item < (int64_t)B * chunks; item += gridDim.x) {
     const int t = (int)(item / chunks);
     const int col = (int)(item - (int64_t)t * chunks) * 64 + cv * 4;
+    __syncthreads();  // the previous item's readers of s_w and red are done
+    if (threadIdx.x < k) s_w[threadIdx.x] = slot_pos[t * k + threadIdx.x] >= 0 ? w[t * k + threadIdx.x] : 0.f;
+    __syncthreads();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < k; ++i) {
-      const int slot = t * k + i;
-      if (!ok || slot_pos[slot] < 0) continue;  // the same in every thread
-      const float* src = part + (int64_t)slot * H + col;
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      for (int j0 = sl; j0 < nsl; j0 += kCombLanes * kCombBatch) {
+    if (ok) {
+      for (int p0 = sl; p0 < pairs; p0 += kCombLanes * kCombBatch) {
         f32x4 v[kCombBatch];
+        float g[kCombBatch];
 #pragma unroll
         for (int q = 0; q < kCombBatch; ++q) {
-          const int jj = j0 + q * kCombLanes;
-          v[q] = jj < nsl ? *(const f32x4*)(src + (int64_t)jj * slots * H) : f32x4{0.f, 0.f, 0.f, 0.f};
+          const int pq = p0 + q * kCombLanes;
+          const int i = pq / nsl, j = pq - (pq / nsl) * nsl;
+          g[q] = pq < pairs ? s_w[i] : 0.f;
+          v[q] = g[q] != 0.f ? *(const f32x4*)(part + ((int64_t)j * slots + t * k + i) * H + col)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int q = 0; q < kCombBatch; ++q) s += v[q];
-      }
-      __syncthreads();  // the previous slot's readers of red are done
-      red[sl][cv] = s;
-      __syncthreads();
-      if (sl == 0) {
-        f32x4 tot = red[0][cv];
+        for (int q = 0; q < kCombBatch; ++q)
 #pragma unroll
-        for (int q = 1; q < kCombLanes; ++q) tot += red[q][cv];
-        const float g = w[slot];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(g, tot[c], acc[c]);
+          for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(g[q], v[q][c], acc[c]);
       }
     }
+    red[sl][cv] = acc;
+    __syncthreads();
     if (sl == 0) {
-      u32x2 o = {bf16_pair(acc[0], acc[1]), bf16_pair(acc[2], acc[3])};
+      f32x4 tot = red[0][cv];
+#pragma unroll
+      for (int q = 1; q < kCombLanes; ++q) tot += red[q][cv];
+      u32x2 o = {bf16_pair(tot[0], tot[1]), bf16_pair(tot[2], tot[3])};
       *(u32x2*)(y + (int64_t)t * H + col) = o;
     }
   }
@@ -437,7 +446,8 @@ hipError_t launch_fused_ffn(const moe_problem& p, const void* x, const void* w1,
   const int64_t slots = g.slots;
   const int64_t nb_max = (slots + kMinBlockM - 1) / kMinBlockM + (p.local_experts < slots ? p.local_experts : slots);
   const int64_t tiles = nb_max * (p.inter / kSlice);
-  const int64_t cap = 2 * (int64_t)num_cus;
+  // up to four workgroups per CU at once: every tile of a small batch in flight
+  const int64_t cap = 4 * (int64_t)num_cus;
   const int grid = (int)(tiles < cap ? tiles : cap);
   if (p.weight_dtype == MOE_FP8_E4M3)
     fused_ffn_kernel<true><<<grid, kFusedThreads, 0, s>>>(g);
