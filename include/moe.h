@@ -389,12 +389,12 @@ moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t*
  *   part[j][s]   = h_j[r] W2_e[:, slice j]^T              (fp32)
  * for every row r that holds slot s = sorted_slots[r] (t = s / k, e =
  * block_expert[r / b]); the combine then writes
- *   y[t] = sum over i = 0..k-1 with slot_pos[t*k+i] >= 0 of
- *          topk_w[t][i] * (sum over j of part[j][t*k+i])
- * in fp32, the slices added in a fixed order (slice lanes l = 0..15 each add
- * slices l, l + 16, ... in ascending order, then the lanes in order), rounded to
- * bf16 once.  No atomics, so the result is deterministic.  Compared with the
- * grouped plan, the slot's sum over I is added per 32-column slice and is not
+ *   y[t] = sum over i = 0..k-1 with slot_pos[t*k+i] >= 0, and over j, of
+ *          topk_w[t][i] * part[j][t*k+i]
+ * in fp32 in a fixed order (pair p = i * (I/32) + j goes to lane p mod 16; each
+ * of the 16 lanes adds its pairs in ascending p, then the lanes are added in
+ * order), rounded to bf16 once.  No atomics, so the result is deterministic.  Compared with the
+ * grouped plan, the sum over I is added per 32-column slice and nothing is
  * rounded to bf16 before the combine (there is no y_slots).
  * Where it pays: each tile streams its slice of W1, W3 and W2 once, and the
  * partial rows add 4 * B * k * H * I / 32 bytes, written once and read once; at
