@@ -57,8 +57,9 @@ class Buffers:
 # copy when the expert weights the batch can reach, min(E_loc, B k) experts of
 # 3 H I bf16 values, are at most this many bytes: there the layer's launches cost
 # more than the fused plan's slower weight stream (measured on MI355X: Qwen3-shaped
-# layers at B = 1 and 4 are 10-17% faster fused, B = 16 ties; a Mixtral-shaped
-# layer at B = 1 is 10% slower, and so are the fp8-weight shares).
+# layers at B = 1 and 4 are 21-24% and 12-14% faster fused, B = 16 ties or is 10%
+# slower; a Mixtral-shaped layer at B = 1 is 11% slower, the fp8-weight shares
+# 45-60% slower).
 FUSED_MAX_WEIGHT_BYTES = 512 << 20
 
 
