@@ -41,6 +41,8 @@
 //   - two to four workgroups share a CU (the grid holds up to four per CU, so
 //     every tile of a small batch is in flight at once).
 //   - a row-block with more than 32 rows takes several passes over its slice.
+#include <type_traits>
+
 #include "fused_ffn.h"
 
 namespace moe {
@@ -131,9 +133,9 @@ __device__ __forceinline__ float silu_times(float g, float u) {
 
 // one gate/up load batch of a wave: kStepBatch 32-deep steps, two token-row
 // groups (A), one weight fragment (B) and its block scale (fp8) per step
-template <bool FP8>
+template <bool FP8, int NG>
 struct UpBatch {
-  u32x4 a[kStepBatch][2];
+  u32x4 a[kStepBatch][NG];
   WFrag<FP8> b[kStepBatch];
   float s[kStepBatch];
 };
@@ -234,118 +236,131 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_ffn_kernel(FusedArgs g
       // the rows of a row-block that hold a slot come first
       if (s_slot[0] < 0) break;
 
-      // ---- gate/up over H ----
-      uint32_t aoff[2];
+      // one instance per row-group count: a pass whose rows 16..31 hold no slot
+      // (the usual case at small batches) loads and multiplies one 16-row group
+      auto pass = [&](auto ngc) __attribute__((always_inline)) {
+        constexpr int NG = decltype(ngc)::value;
+        // ---- gate/up over H ----
+        uint32_t aoff[NG];
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        const int s = s_slot[gi * 16 + lr];
-        aoff[gi] = s >= 0 ? (uint32_t)(((int64_t)(s / g.k) * H + 8 * lg) * 2) : kNoOperand;
-      }
+        for (int gi = 0; gi < NG; ++gi) {
+          const int s = s_slot[gi * 16 + lr];
+          aoff[gi] = s >= 0 ? (uint32_t)(((int64_t)(s / g.k) * H + 8 * lg) * 2) : kNoOperand;
+        }
 
-      auto load_up = [&](UpBatch<FP8>& U, int bt) __attribute__((always_inline)) {
+        auto load_up = [&](UpBatch<FP8, NG>& U, int bt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < kStepBatch; ++q) {
-          const int st = bt * kStepBatch + q;
-          const bool in = st < nst;
-          const int k0 = st * 32;
+          for (int q = 0; q < kStepBatch; ++q) {
+            const int st = bt * kStepBatch + q;
+            const bool in = st < nst;
+            const int k0 = st * 32;
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi)
-            U.a[q][gi] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, in ? aoff[gi] : kNoOperand, k0 * 2, 0));
-          U.b[q] = load_w<FP8>(wr, in ? boff : kNoOperand, st * sstep);
-          if constexpr (FP8) U.s[q] = sm[su0 + (in ? st / 4 : 0)];
+            for (int gi = 0; gi < NG; ++gi)
+              U.a[q][gi] = __builtin_bit_cast(
+                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, in ? aoff[gi] : kNoOperand, k0 * 2, 0));
+            U.b[q] = load_w<FP8>(wr, in ? boff : kNoOperand, st * sstep);
+            if constexpr (FP8) U.s[q] = sm[su0 + (in ? st / 4 : 0)];
+          }
+        };
+        f32x4 acc[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) acc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto mul_up = [&](const UpBatch<FP8, NG>& U) __attribute__((always_inline)) {
+#pragma unroll
+          for (int q = 0; q < kStepBatch; ++q) {
+            const bf16x8 b = decode<FP8>(U.b[q], FP8 ? U.s[q] : 1.0f);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) acc[gi] = mfma(__builtin_bit_cast(bf16x8, U.a[q][gi]), b, acc[gi]);
+          }
+        };
+        {
+          UpBatch<FP8, NG> U0, U1;
+          load_up(U0, 0);
+          // steps past nst read zeros (an odd nbt runs one batch of zeros)
+          for (int bt = 0; bt < nbt; bt += 2) {
+            load_up(U1, bt + 1);
+            mul_up(U0);
+            load_up(U0, bt + 2);
+            mul_up(U1);
+          }
         }
-      };
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      auto mul_up = [&](const UpBatch<FP8>& U) __attribute__((always_inline)) {
+        // the first W2 batch does not depend on h: its loads fly while h is formed
+        const uint32_t doff0 = (uint32_t)((lr * (int64_t)I + j * kSlice + 8 * lg) * WSZ);
+        auto load_down = [&](DownBatch<FP8>& D, int bd) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < kStepBatch; ++q) {
-          const bf16x8 b = decode<FP8>(U.b[q], FP8 ? U.s[q] : 1.0f);
+          for (int q = 0; q < kGroupBatch; ++q) {
+            // group i of this wave is column group cg = wv + 4 i (columns 16 cg ..)
+            const int i = bd * kGroupBatch + q;
+            const bool in = i < ncg;
+            const int cg = wv + 4 * (in ? i : 0);
+            const uint32_t off =
+                pk ? (uint32_t)(((cg / 16) * nst2 + j) * kPkBlock + ((cg % 16) * 16 + lr) * 64 + 16 * lg)
+                   : doff0 + (uint32_t)((int64_t)cg * 16 * I * WSZ);
+            D.b[q] = load_w<FP8>(w2r, in ? off : kNoOperand, 0);
+            if constexpr (FP8) D.s[q] = g.s2[sd0 + (int64_t)(cg * 16 / 128) * (I / 128)];
+          }
+        };
+        DownBatch<FP8> D0, D1;
+        load_down(D0, 0);
+        // g (wave matrix 0) and u (1) of rows 4 lg + c of each group, column
+        // 16 half + lr of the slice
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi) acc[gi] = mfma(__builtin_bit_cast(bf16x8, U.a[q][gi]), b, acc[gi]);
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) s_gu[mt][gi * 16 + 4 * lg + c][half * 16 + lr] = acc[gi][c];
+        __syncthreads();
+        {
+          // 32 rows x 32 columns: 4 consecutive columns per thread
+          const int row = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+          if (row < 16 * NG) {
+            u32x2 o;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              o[q] = bf16_pair(silu_times(s_gu[0][row][c0 + 2 * q], s_gu[1][row][c0 + 2 * q]),
+                               silu_times(s_gu[0][row][c0 + 2 * q + 1], s_gu[1][row][c0 + 2 * q + 1]));
+            *(u32x2*)&s_h[row][c0] = o;
+          }
         }
-      };
-      {
-        UpBatch<FP8> U0, U1;
-        load_up(U0, 0);
-        // steps past nst read zeros (an odd nbt runs one batch of zeros)
-        for (int bt = 0; bt < nbt; bt += 2) {
-          load_up(U1, bt + 1);
-          mul_up(U0);
-          load_up(U0, bt + 2);
-          mul_up(U1);
-        }
-      }
-      // the first W2 batch does not depend on h: its loads fly while h is formed
-      const uint32_t doff0 = (uint32_t)((lr * (int64_t)I + j * kSlice + 8 * lg) * WSZ);
-      auto load_down = [&](DownBatch<FP8>& D, int bd) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < kGroupBatch; ++q) {
-          // group i of this wave is column group cg = wv + 4 i (columns 16 cg ..)
-          const int i = bd * kGroupBatch + q;
-          const bool in = i < ncg;
-          const int cg = wv + 4 * (in ? i : 0);
-          const uint32_t off =
-              pk ? (uint32_t)(((cg / 16) * nst2 + j) * kPkBlock + ((cg % 16) * 16 + lr) * 64 + 16 * lg)
-                 : doff0 + (uint32_t)((int64_t)cg * 16 * I * WSZ);
-          D.b[q] = load_w<FP8>(w2r, in ? off : kNoOperand, 0);
-          if constexpr (FP8) D.s[q] = g.s2[sd0 + (int64_t)(cg * 16 / 128) * (I / 128)];
-        }
-      };
-      DownBatch<FP8> D0, D1;
-      load_down(D0, 0);
-      // g (wave matrix 0) and u (1) of rows 4 lg + c of each group, column
-      // 16 half + lr of the slice
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) s_gu[mt][gi * 16 + 4 * lg + c][half * 16 + lr] = acc[gi][c];
-      __syncthreads();
-      {
-        // 32 rows x 32 columns: 4 consecutive columns per thread
-        const int row = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
-        u32x2 o;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          o[q] = bf16_pair(silu_times(s_gu[0][row][c0 + 2 * q], s_gu[1][row][c0 + 2 * q]),
-                           silu_times(s_gu[0][row][c0 + 2 * q + 1], s_gu[1][row][c0 + 2 * q + 1]));
-        *(u32x2*)&s_h[row][c0] = o;
-      }
-      __syncthreads();
+        __syncthreads();
 
-      // ---- down over the slice: y_j[rows][H] ----
-      bf16x8 ha[2];  // [row group]: the 32-deep slice
+        // ---- down over the slice: y_j[rows][H] ----
+        bf16x8 ha[NG];  // [row group]: the 32-deep slice
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) ha[gi] = *(const bf16x8*)&s_h[gi * 16 + lr][8 * lg];
-      int slot_of[2][4];
+        for (int gi = 0; gi < NG; ++gi) ha[gi] = *(const bf16x8*)&s_h[gi * 16 + lr][8 * lg];
+        int slot_of[NG][4];
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
+        for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) slot_of[gi][c] = s_slot[gi * 16 + 4 * lg + c];
-      float* prow = g.part + (int64_t)j * g.slots * H;
-      auto mul_down = [&](const DownBatch<FP8>& D, int bd) __attribute__((always_inline)) {
+          for (int c = 0; c < 4; ++c) slot_of[gi][c] = s_slot[gi * 16 + 4 * lg + c];
+        float* prow = g.part + (int64_t)j * g.slots * H;
+        auto mul_down = [&](const DownBatch<FP8>& D, int bd) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < kGroupBatch; ++q) {
-          const int i = bd * kGroupBatch + q;
-          const bf16x8 b = decode<FP8>(D.b[q], FP8 ? D.s[q] : 1.0f);
-          f32x4 y[2];
+          for (int q = 0; q < kGroupBatch; ++q) {
+            const int i = bd * kGroupBatch + q;
+            const bf16x8 b = decode<FP8>(D.b[q], FP8 ? D.s[q] : 1.0f);
+            f32x4 y[NG];
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi) y[gi] = mfma(ha[gi], b, f32x4{0.f, 0.f, 0.f, 0.f});
-          if (i >= ncg) continue;
-          const int col = (wv + 4 * i) * 16 + lr;
+            for (int gi = 0; gi < NG; ++gi) y[gi] = mfma(ha[gi], b, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (i >= ncg) continue;
+            const int col = (wv + 4 * i) * 16 + lr;
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi)
+            for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (slot_of[gi][c] >= 0) prow[(int64_t)slot_of[gi][c] * H + col] = y[gi][c];
+              for (int c = 0; c < 4; ++c)
+                if (slot_of[gi][c] >= 0) prow[(int64_t)slot_of[gi][c] * H + col] = y[gi][c];
+          }
+        };
+        for (int bd = 0; bd < nbd; bd += 2) {
+          load_down(D1, bd + 1);
+          mul_down(D0, bd);
+          load_down(D0, bd + 2);
+          mul_down(D1, bd + 1);
         }
       };
-      for (int bd = 0; bd < nbd; bd += 2) {
-        load_down(D1, bd + 1);
-        mul_down(D0, bd);
-        load_down(D0, bd + 2);
-        mul_down(D1, bd + 1);
-      }
+      if (s_slot[16] < 0)
+        pass(std::integral_constant<int, 1>{});
+      else
+        pass(std::integral_constant<int, 2>{});
     }
   }
 }
