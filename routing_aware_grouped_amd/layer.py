@@ -57,9 +57,9 @@ class Buffers:
 # copy when the expert weights the batch can reach, min(E_loc, B k) experts of
 # 3 H I bf16 values, are at most this many bytes: there the layer's launches cost
 # more than the fused plan's slower weight stream (measured on MI355X: Qwen3-shaped
-# layers at B = 1 and 4 are 21-24% and 12-14% faster fused, B = 16 ties or is 10%
-# slower; a Mixtral-shaped layer at B = 1 is 11% slower, the fp8-weight shares
-# 45-60% slower).
+# layers at B = 1 and 4 are 27-28% and 16-17% faster fused, B = 16 within 5%
+# either way; a Mixtral-shaped layer at B = 1 is 9-10% slower, the fp8-weight
+# shares 42-52% slower).
 FUSED_MAX_WEIGHT_BYTES = 512 << 20
 
 
