@@ -391,8 +391,8 @@ moe_status moe_combine(const moe_problem* p, const void* y_slots, const int32_t*
  * block_expert[r / b]); the combine then writes
  *   y[t] = sum over i = 0..k-1 with slot_pos[t*k+i] >= 0, and over j, of
  *          topk_w[t][i] * part[j][t*k+i]
- * in fp32 in a fixed order (pair p = i * (I/32) + j goes to lane p mod 16; each
- * of the 16 lanes adds its pairs in ascending p, then the lanes are added in
+ * in fp32 in a fixed order (pair p = i * (I/32) + j goes to lane p mod 32; each
+ * of the 32 lanes adds its pairs in ascending p, then the lanes are added in
  * order), rounded to bf16 once.  No atomics, so the result is deterministic.  Compared with the
  * grouped plan, the sum over I is added per 32-column slice and nothing is
  * rounded to bf16 before the combine (there is no y_slots).

@@ -365,15 +365,16 @@ __global__ void __launch_bounds__(kFusedThreads, 2) fused_ffn_kernel(FusedArgs g
   }
 }
 
-// The combine of the fused plan.  A workgroup takes one token and 64 columns: 16
-// column vectors of 4 floats x 16 pair lanes.  The token's (slot i, slice j)
-// pairs, numbered p = i * nsl + j, are dealt to the lanes (lane l: p = l, l + 16,
+// The combine of the fused plan.  A workgroup takes one token and 32 columns: 8
+// column vectors of 4 floats x 32 pair lanes.  The token's (slot i, slice j)
+// pairs, numbered p = i * nsl + j, are dealt to the lanes (lane l: p = l, l + 32,
 // ... in ascending order); a lane adds topk_w[t][i] * part[j][t k + i] over its
 // pairs, loading eight pairs before it adds them, and skips the slots of other
-// GPUs' experts.  The 16 lane sums are then added in lane order through LDS and
+// GPUs' experts.  The 32 lane sums are then added in lane order through LDS and
 // rounded to bf16 once: a fixed order, so y is deterministic.  With a nonzero
 // device status the FFN may have skipped rows, and y is written as zeros.
-constexpr int kCombLanes = 16;
+constexpr int kCombLanes = 32;
+constexpr int kCombVecs = 256 / kCombLanes;  // column vectors of 4 floats per workgroup
 constexpr int kCombBatch = 8;  // pairs loaded before they are added
 
 __global__ void __launch_bounds__(256) combine_fused_kernel(const float* __restrict__ part,
@@ -382,15 +383,15 @@ __global__ void __launch_bounds__(256) combine_fused_kernel(const float* __restr
                                                             const float* __restrict__ w,
                                                             uint16_t* __restrict__ y, int B, int H,
                                                             int k, int nsl, int slots) {
-  __shared__ f32x4 red[kCombLanes][16];
+  __shared__ f32x4 red[kCombLanes][kCombVecs];
   __shared__ float s_w[32];  // the token's router weights; 0 for other GPUs' experts
-  const int cv = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const int cv = threadIdx.x % kCombVecs, sl = threadIdx.x / kCombVecs;
   const bool ok = *status == MOE_DEV_OK;
-  const int chunks = H / 64;
+  const int chunks = H / (4 * kCombVecs);
   const int pairs = k * nsl;
   for (int64_t item = blockIdx.x; item < (int64_t)B * chunks; item += gridDim.x) {
     const int t = (int)(item / chunks);
-    const int col = (int)(item - (int64_t)t * chunks) * 64 + cv * 4;
+    const int col = (int)(item - (int64_t)t * chunks) * (4 * kCombVecs) + cv * 4;
     __syncthreads();  // the previous item's readers of s_w and red are done
     if (threadIdx.x < k) s_w[threadIdx.x] = slot_pos[t * k + threadIdx.x] >= 0 ? w[t * k + threadIdx.x] : 0.f;
     __syncthreads();
@@ -473,7 +474,7 @@ hipError_t launch_fused_ffn(const moe_problem& p, const void* x, const void* w1,
 
 hipError_t launch_combine_fused(const moe_problem& p, const void* ws, const int32_t* slot_pos,
                                 const float* w, void* y, hipStream_t s) {
-  const int64_t items = (int64_t)p.tokens * (p.hidden / 64);
+  const int64_t items = (int64_t)p.tokens * (p.hidden / (4 * kCombVecs));
   const int grid = (int)(items < 8192 ? items : 8192);
   combine_fused_kernel<<<grid, 256, 0, s>>>((const float*)((const char*)ws + 256), (const int32_t*)ws,
                                             slot_pos, w, (uint16_t*)y, p.tokens, p.hidden,
