@@ -57,9 +57,9 @@ class Buffers:
 # copy when the expert weights the batch can reach, min(E_loc, B k) experts of
 # 3 H I bf16 values, are at most this many bytes: there the layer's launches cost
 # more than the fused plan's slower weight stream (measured on MI355X: Qwen3-shaped
-# layers at B = 1 and 4 are 27-28% and 16-17% faster fused, B = 16 within 5%
-# either way; a Mixtral-shaped layer at B = 1 is 9-10% slower, the fp8-weight
-# shares 42-52% slower).
+# layers at B = 1 and 4 are 30% and 17-19% faster fused, B = 16 within 4% either
+# way; a Mixtral-shaped layer at B = 1 is 6-9% slower, the fp8-weight shares
+# 40-52% slower).
 FUSED_MAX_WEIGHT_BYTES = 512 << 20
 
 
